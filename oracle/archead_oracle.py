@@ -1,0 +1,315 @@
+"""CPU oracle for the packed ARCHead LM-head forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package's smoke check and the benchmark's CPU-baseline
+leg may import or call this module.  The product path never does: it runs on
+the HIP kernels and fails loudly when they are missing.
+
+Source of the definitions: "ARCHead: Activation-Metric Residual Correction for
+Large Language Model Output Heads" (arXiv:2608.02703), Sec. 3 and Algorithm 1.
+
+* The head is a quantised low-rank core plus an SC4 residual,
+  W_d = Q(A_c) Q(B_c) + SC4(R)  (Sec. 3, quantized-core equation and the
+  sentence after it: SC4 is a packed signed-INT4 residual with quantised group
+  scales; A_c B_c has rank r_c).
+* The correction factors are stored with row-wise INT8 (A_w) and group-wise
+  INT8 (B_w) quantisation (Sec. 3, packed-variant paragraph; Algorithm 1).
+* Inference evaluates Y = H W_d^T + (H B_w^T) A_w^T (Algorithm 1, last step).
+  There is no approximation at inference time, so the oracle writes out the
+  plain definition: decode every stored code exactly, rebuild
+  W_hat = R_hat + A_c_hat B_c_hat + A_w_hat B_w_hat in fp64, and return
+  H W_hat^T in fp64.
+* The serialized module holds only the residual codes and scales, the core
+  factors, the correction factors and shape metadata; its persistent size is
+  the sum of numel x element size over those tensors (Sec. 3, persistent-size
+  equation).  ``layout``/``pack``/``unpack`` below implement the byte format of
+  that module independently of the library.
+
+Readings taken where the page leaves the format open (the bit width of Q_b,
+SC4 internals, nibble order, the tile order of the stored residual) are the
+byte format described in ``FORMAT`` below.  Every floating-point step is fp64;
+all dequantised values are exact in fp64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+FORMAT = """
+Packed head, format version 1 (all integers little-endian).
+  V16 = ceil(V/16)*16 rows (rows >= V are zero), nb = V16/16 row blocks,
+  nkt = D/128 k-tiles, ng = D/g groups, r = r_c + r_r, nA = [r_c>0] + [r_r>0].
+  Sections in order, each starting on a 256-byte boundary:
+   header     64 B: u32 magic 0x48435241, u32 version 1, u64 V, u64 D,
+                    u32 r_c, u32 r_r, u32 g, u32 flags 0, 24 zero bytes
+   r_codes    nb*nkt tiles of 1024 B.  In tile (b, kt), byte 16*l + 4*s + c
+              (l in [0,64), s in [0,4), c in [0,4)) holds the two INT4 codes
+              (two's complement) of row v = 16*b + (l mod 16) at
+              k = 128*kt + 32*s + 8*(l div 16) + 2*c   (low nibble)
+              and k + 1                                (high nibble).
+   r_gcodes   nb*ng*16 B: byte (b*ng + t)*16 + i = uint8 group code of row
+              16*b + i, group t (columns t*g .. t*g+g-1).
+   r_rowscale V16 fp16: per-row residual scale s_R.
+   a_codes    V16*r int8, row-major; row v = [A_c[v, :r_c] | A_w[v, :r_r]].
+   a_scales   V16*nA fp16; row v = [s_Ac[v] if r_c>0, s_Aw[v] if r_r>0].
+   b_codes    r*D int8, row-major; rows [B_c; B_w].
+   b_scales   r*ng fp16, row-major; rows [s_Bc; s_Bw].
+  Dequantisation:
+   R_hat[v,k] = q4[v,k] * c8[v, k//g] * s_R[v]
+   A_hat[v,j] = a_codes[v,j] * (s_Ac[v] if j < r_c else s_Aw[v])
+   B_hat[j,k] = b_codes[j,k] * b_scales[j, k//g]
+"""
+
+MAGIC = 0x48435241
+FORMAT_VERSION = 1
+ALIGN = 256
+HEADER_BYTES = 64
+
+_SECTIONS = ("r_codes", "r_gcodes", "r_rowscale", "a_codes", "a_scales",
+             "b_codes", "b_scales")
+
+
+def _up(x, a):
+    return (x + a - 1) // a * a
+
+
+def layout(V, D, r_c, r_r, g):
+    """Offsets and sizes of every section of the packed buffer (see FORMAT)."""
+    if V < 1 or D < 128 or D % 128 or g < 2 or g % 2 or D % g or r_c < 0 or r_r < 0:
+        raise ValueError("unsupported dims")
+    V16 = _up(V, 16)
+    r = r_c + r_r
+    ng = D // g
+    nA = int(r_c > 0) + int(r_r > 0)
+    sizes = dict(
+        r_codes=V16 * D // 2,
+        r_gcodes=V16 * ng,
+        r_rowscale=2 * V16,
+        a_codes=V16 * r,
+        a_scales=2 * V16 * nA,
+        b_codes=r * D,
+        b_scales=2 * r * ng,
+    )
+    out = dict(header=(0, HEADER_BYTES))
+    off = _up(HEADER_BYTES, ALIGN)
+    for name in _SECTIONS:
+        out[name] = (off, sizes[name])
+        off = _up(off + sizes[name], ALIGN)
+    out["total_bytes"] = off
+    out["payload_bytes"] = sum(sizes.values())
+    out["V16"] = V16
+    return out
+
+
+def persistent_bytes(V, D, r_c, r_r, g):
+    """Sum of numel x element size over the stored tensors, for V a multiple
+    of 16 (Sec. 3, persistent-size equation): residual codes at 4 bits, group
+    codes at 8 bits, fp16 row scale, INT8 factor codes, fp16 factor scales."""
+    r = r_c + r_r
+    nA = int(r_c > 0) + int(r_r > 0)
+    elems = [
+        (V * D, 0.5),           # SC4 codes, two per byte
+        (V * (D // g), 1),      # uint8 group codes
+        (V, 2),                 # fp16 row scale
+        (V * r, 1),             # INT8 A_c | A_w
+        (V * nA, 2),            # fp16 A row scales
+        (r * D, 1),             # INT8 B_c ; B_w
+        (r * (D // g), 2),      # fp16 B group scales
+    ]
+    return int(sum(n * b for n, b in elems))
+
+
+# ---------------------------------------------------------------- packing ---
+
+def _nibbles_to_tiles(nib):
+    """[V16, D] nibbles -> r_codes bytes.  Writing k = 128*kt + 32*s + 8*q + 2*c + h
+    and v = 16*b + i, the tile byte order is (b, kt, q, i, s, c) and h selects
+    the low (h=0) or high (h=1) nibble; lane l = 16*q + i."""
+    V16, D = nib.shape
+    t = nib.reshape(V16 // 16, 16, D // 128, 4, 4, 4, 2)        # b i kt s q c h
+    t = t.transpose(0, 2, 4, 1, 3, 5, 6)                        # b kt q i s c h
+    return (t[..., 0] | (t[..., 1] << 4)).astype(np.uint8).reshape(-1)
+
+
+def _tiles_to_nibbles(raw, V16, D):
+    """Inverse of ``_nibbles_to_tiles``."""
+    t = raw.reshape(V16 // 16, D // 128, 4, 16, 4, 4)            # b kt q i s c
+    both = np.stack([t & 0xF, t >> 4], axis=-1)                  # b kt q i s c h
+    return both.transpose(0, 3, 1, 4, 2, 5, 6).reshape(V16, D)   # b i kt s q c h
+
+
+def pack(head) -> np.ndarray:
+    """Serialise a ``synth.Head`` into the packed byte format (FORMAT)."""
+    V, D, r_c, r_r, g = head.V, head.D, head.r_c, head.r_r, head.g
+    L = layout(V, D, r_c, r_r, g)
+    V16 = L["V16"]
+    buf = np.zeros(L["total_bytes"], np.uint8)
+
+    hdr = np.zeros(HEADER_BYTES, np.uint8)
+    hdr[0:4] = np.frombuffer(np.uint32(MAGIC).tobytes(), np.uint8)
+    hdr[4:8] = np.frombuffer(np.uint32(FORMAT_VERSION).tobytes(), np.uint8)
+    hdr[8:16] = np.frombuffer(np.uint64(V).tobytes(), np.uint8)
+    hdr[16:24] = np.frombuffer(np.uint64(D).tobytes(), np.uint8)
+    hdr[24:28] = np.frombuffer(np.uint32(r_c).tobytes(), np.uint8)
+    hdr[28:32] = np.frombuffer(np.uint32(r_r).tobytes(), np.uint8)
+    hdr[32:36] = np.frombuffer(np.uint32(g).tobytes(), np.uint8)
+    buf[0:HEADER_BYTES] = hdr
+
+    def put(name, arr):
+        off, size = L[name]
+        raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+        assert raw.size == size, (name, raw.size, size)
+        buf[off:off + size] = raw
+
+    q = np.zeros((V16, D), np.int8)
+    q[:V] = head.q4
+    if q.min() < -8 or q.max() > 7:
+        raise ValueError("INT4 code out of range")
+    nib = (q.view(np.uint8) & 0xF)                               # two's complement nibble
+    put("r_codes", _nibbles_to_tiles(nib))
+
+    ng = D // g
+    c8 = np.zeros((V16, ng), np.uint8)
+    c8[:V] = head.c8
+    put("r_gcodes", c8.reshape(V16 // 16, 16, ng).transpose(0, 2, 1))
+
+    sR = np.zeros(V16, np.float16)
+    sR[:V] = head.s_R
+    put("r_rowscale", sR)
+
+    A = np.zeros((V16, r_c + r_r), np.int8)
+    A[:V, :r_c] = head.A_c
+    A[:V, r_c:] = head.A_w
+    put("a_codes", A)
+
+    cols = []
+    if r_c > 0:
+        cols.append(head.s_Ac)
+    if r_r > 0:
+        cols.append(head.s_Aw)
+    sA = np.zeros((V16, len(cols)), np.float16)
+    for i, col in enumerate(cols):
+        sA[:V, i] = col
+    put("a_scales", sA)
+
+    put("b_codes", np.concatenate([head.B_c.reshape(r_c, D), head.B_w.reshape(r_r, D)], 0))
+    put("b_scales", np.concatenate([head.s_Bc.reshape(r_c, ng), head.s_Bw.reshape(r_r, ng)], 0))
+    return buf
+
+
+def unpack(buf: np.ndarray, V, D, r_c, r_r, g) -> dict:
+    """Read every component back out of a packed buffer (inverse of ``pack``)."""
+    L = layout(V, D, r_c, r_r, g)
+    V16 = L["V16"]
+    ng = D // g
+    buf = np.asarray(buf, np.uint8)
+    hdr = buf[:HEADER_BYTES]
+
+    def get(name, dtype):
+        off, size = L[name]
+        return buf[off:off + size].view(dtype)
+
+    nib = _tiles_to_nibbles(get("r_codes", np.uint8), V16, D)
+    q4 = nib.astype(np.int8)
+    q4[q4 >= 8] -= 16
+    c8 = get("r_gcodes", np.uint8).reshape(V16 // 16, ng, 16).transpose(0, 2, 1).reshape(V16, ng)
+    s_R = get("r_rowscale", np.float16)
+    A = get("a_codes", np.int8).reshape(V16, r_c + r_r)
+    nA = int(r_c > 0) + int(r_r > 0)
+    sA = get("a_scales", np.float16).reshape(V16, nA)
+    B = get("b_codes", np.int8).reshape(r_c + r_r, D)
+    sB = get("b_scales", np.float16).reshape(r_c + r_r, ng)
+    return dict(
+        magic=int(hdr[0:4].view(np.uint32)[0]), version=int(hdr[4:8].view(np.uint32)[0]),
+        V=int(hdr[8:16].view(np.uint64)[0]), D=int(hdr[16:24].view(np.uint64)[0]),
+        r_c=int(hdr[24:28].view(np.uint32)[0]), r_r=int(hdr[28:32].view(np.uint32)[0]),
+        g=int(hdr[32:36].view(np.uint32)[0]),
+        q4=q4[:V], c8=c8[:V], s_R=s_R[:V],
+        A_c=A[:V, :r_c], A_w=A[:V, r_c:],
+        s_Ac=sA[:V, 0] if r_c > 0 else np.zeros(V, np.float16),
+        s_Aw=sA[:V, nA - 1] if r_r > 0 else np.zeros(V, np.float16),
+        B_c=B[:r_c], B_w=B[r_c:], s_Bc=sB[:r_c], s_Bw=sB[r_c:],
+        pad_rows_zero=bool(np.all(q4[V:] == 0) and np.all(c8[V:] == 0) and np.all(A[V:] == 0)),
+    )
+
+
+# ------------------------------------------------------------ number decode ---
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 is the upper half of an IEEE binary32; widen and convert exactly."""
+    u = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(x: np.ndarray) -> np.ndarray:
+    """IEEE binary16 to fp64, exact (subnormals and zero included)."""
+    return np.asarray(x, np.float16).astype(np.float64)
+
+
+# ------------------------------------------------------------ dequantise ---
+
+def dequant_R(q4, c8, s_R, g):
+    """SC4 residual: R_hat[v,k] = q4[v,k] * c8[v, k//g] * s_R[v] (exact in fp64)."""
+    grp = np.repeat(c8.astype(np.float64), g, axis=1)              # [V, D]
+    return q4.astype(np.float64) * grp * f16_to_f64(s_R)[:, None]
+
+
+def dequant_rows(codes, row_scale):
+    """Row-wise INT8: A_hat[v,j] = code[v,j] * s[v]."""
+    return codes.astype(np.float64) * f16_to_f64(row_scale)[:, None]
+
+
+def dequant_groups(codes, group_scale, g):
+    """Group-wise INT8 along D: B_hat[j,k] = code[j,k] * s[j, k//g]."""
+    return codes.astype(np.float64) * np.repeat(f16_to_f64(group_scale), g, axis=1)
+
+
+def w_hat(head, v0=0, v1=None):
+    """Rows v0..v1 of W_hat = R_hat + A_c_hat B_c_hat + A_w_hat B_w_hat (fp64)."""
+    v1 = head.V if v1 is None else v1
+    g = head.g
+    W = dequant_R(head.q4[v0:v1], head.c8[v0:v1], head.s_R[v0:v1], g)
+    if head.r_c:
+        W += dequant_rows(head.A_c[v0:v1], head.s_Ac[v0:v1]) @ dequant_groups(head.B_c, head.s_Bc, g)
+    if head.r_r:
+        W += dequant_rows(head.A_w[v0:v1], head.s_Aw[v0:v1]) @ dequant_groups(head.B_w, head.s_Bw, g)
+    return W
+
+
+def logits(H_bits, head, rows=None, cols=None, v_chunk=8192):
+    """Y_ref = H W_hat^T in fp64 (Algorithm 1, inference step).
+
+    ``rows`` selects token rows of H, ``cols`` selects vocabulary rows of the
+    head (both optional index arrays); W_hat is rebuilt in chunks of
+    ``v_chunk`` vocabulary rows so the V x D fp64 matrix is never whole.
+    """
+    H = bf16_bits_to_f64(H_bits if rows is None else H_bits[rows])
+    if cols is not None:
+        cols = np.asarray(cols)
+        return H @ _w_hat_rows(head, cols).T
+    Y = np.empty((H.shape[0], head.V), np.float64)
+    for v0 in range(0, head.V, v_chunk):
+        v1 = min(head.V, v0 + v_chunk)
+        Y[:, v0:v1] = H @ w_hat(head, v0, v1).T
+    return Y
+
+
+def _w_hat_rows(head, cols):
+    g = head.g
+    W = dequant_R(head.q4[cols], head.c8[cols], head.s_R[cols], g)
+    if head.r_c:
+        W += dequant_rows(head.A_c[cols], head.s_Ac[cols]) @ dequant_groups(head.B_c, head.s_Bc, g)
+    if head.r_r:
+        W += dequant_rows(head.A_w[cols], head.s_Aw[cols]) @ dequant_groups(head.B_w, head.s_Bw, g)
+    return W
+
+
+# -------------------------------------------------------------- statistics ---
+
+def row_argmax(Y):
+    """Per-row argmax; exact ties go to the lowest vocabulary index."""
+    return np.argmax(Y, axis=1)
+
+
+def top2_gap(Y):
+    """Per-row gap between the largest and second-largest logit."""
+    part = np.partition(Y, Y.shape[1] - 2, axis=1)
+    return part[:, -1] - part[:, -2]

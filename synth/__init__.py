@@ -1,0 +1,171 @@
+"""Seeded synthetic inputs for the packed LM-head forward.
+
+This module only draws random numbers and stores them in the storage types the
+packed head uses (bf16 bit patterns, fp16, int8/uint8 codes).  It holds none of
+the method's arithmetic: no dequantisation, no packing, no products.  Both the
+CPU oracle and the GPU path are fed from here, and nothing else is shared
+between them.
+
+Workloads (the five shapes used throughout, "ARCHead: Activation-Metric Residual
+Correction for Large Language Model Output Heads", Sec. 3 and Alg. 1 define the
+components; the shapes stand in for the Qwen3-8B-Base head of its Tables 4-8
+and a 70B-class head):
+
+  tiny      V=1024   D=256  N=4    r_c=16 r_r=8  g=64   4 outlier ch. x20, fp32 Y
+  decode    V=151936 D=4096 N=1    r_c=32 r_r=32 g=128 16 outlier ch. x20, fp32 Y
+  batched   V=151936 D=4096 N=64   r_c=32 r_r=32 g=128 16 outlier ch. x20, fp32 Y
+  prefill   V=151936 D=4096 N=4096 r_c=64 r_r=64 g=128 16 outlier ch. x20, bf16 Y
+  head70b   V=128256 D=8192 N=256  r_c=64 r_r=64 g=128 32 outlier ch. x25, fp32 Y
+
+Value distributions (same for every workload):
+  H      bf16, N(0,1) drawn in fp32, outlier channels multiplied by the factor
+         in fp32, then rounded once to bf16 (round to nearest even).
+  q4     signed INT4 residual codes, uniform on [-8, 7].
+  c8     uint8 group-scale codes, uniform on [1, 255].
+  s_R    per-row fp16 residual scale, |N(0, 1e-3)| drawn in fp64, rounded to fp16.
+  A_c/A_w  INT8 codes uniform on [-127, 127]; fp16 row scales |N(0, 1e-2)|.
+  B_c/B_w  INT8 codes uniform on [-127, 127]; fp16 group scales |N(0, 1e-2)|.
+
+Draw order from one numpy PCG64 stream (``numpy.random.default_rng(seed)``):
+H, outlier channel indices, q4, c8, s_R, A_c, A_w, s_Ac, s_Aw, B_c, B_w, s_Bc,
+s_Bw.  The default seed of a workload is its index in ``CONFIGS``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+CONFIGS = [
+    dict(name="tiny", V=1024, D=256, N=4, r_c=16, r_r=8, g=64,
+         n_outlier=4, outlier_scale=20.0, y_dtype="f32"),
+    dict(name="decode", V=151936, D=4096, N=1, r_c=32, r_r=32, g=128,
+         n_outlier=16, outlier_scale=20.0, y_dtype="f32"),
+    dict(name="batched", V=151936, D=4096, N=64, r_c=32, r_r=32, g=128,
+         n_outlier=16, outlier_scale=20.0, y_dtype="f32"),
+    dict(name="prefill", V=151936, D=4096, N=4096, r_c=64, r_r=64, g=128,
+         n_outlier=16, outlier_scale=20.0, y_dtype="bf16"),
+    dict(name="head70b", V=128256, D=8192, N=256, r_c=64, r_r=64, g=128,
+         n_outlier=32, outlier_scale=25.0, y_dtype="f32"),
+]
+
+
+def config(name_or_index) -> dict:
+    if isinstance(name_or_index, int):
+        return dict(CONFIGS[name_or_index])
+    for c in CONFIGS:
+        if c["name"] == name_or_index:
+            return dict(c)
+    raise KeyError(name_or_index)
+
+
+@dataclass
+class Head:
+    """Quantised components of one packed head, unpacked (one code per element).
+
+    Shapes: q4 [V, D] int8 in [-8, 7]; c8 [V, D/g] uint8; s_R [V] float16;
+    A_c [V, r_c] int8; A_w [V, r_r] int8; s_Ac, s_Aw [V] float16;
+    B_c [r_c, D] int8; B_w [r_r, D] int8; s_Bc [r_c, D/g], s_Bw [r_r, D/g] float16.
+    """
+    V: int
+    D: int
+    r_c: int
+    r_r: int
+    g: int
+    q4: np.ndarray
+    c8: np.ndarray
+    s_R: np.ndarray
+    A_c: np.ndarray
+    A_w: np.ndarray
+    s_Ac: np.ndarray
+    s_Aw: np.ndarray
+    B_c: np.ndarray
+    B_w: np.ndarray
+    s_Bc: np.ndarray
+    s_Bw: np.ndarray
+
+    @property
+    def dims(self):
+        return dict(V=self.V, D=self.D, r_c=self.r_c, r_r=self.r_r, g=self.g)
+
+
+@dataclass
+class Inputs:
+    H_bits: np.ndarray          # [N, D] uint16, bf16 bit patterns
+    head: Head
+    outlier_channels: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    seed: Optional[int] = None
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite fp32 values to bf16 (nearest, ties to even); return uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def _abs_normal_f16(rng, sigma, size):
+    return np.abs(rng.normal(0.0, sigma, size=size)).astype(np.float16)
+
+
+def draw_hidden(rng, N, D, n_outlier, outlier_scale):
+    h = rng.standard_normal((N, D), dtype=np.float32)
+    n_outlier = min(n_outlier, D)
+    idx = np.sort(rng.choice(D, size=n_outlier, replace=False)) if n_outlier else np.zeros(0, np.int64)
+    if n_outlier:
+        h[:, idx] *= np.float32(outlier_scale)
+    return f32_to_bf16_bits(h), idx
+
+
+def draw_head(rng, V, D, r_c, r_r, g) -> Head:
+    ng = D // g
+    q4 = rng.integers(-8, 8, size=(V, D), dtype=np.int8)
+    c8 = rng.integers(1, 256, size=(V, ng), dtype=np.uint8)
+    s_R = _abs_normal_f16(rng, 1e-3, V)
+    A_c = rng.integers(-127, 128, size=(V, r_c), dtype=np.int8)
+    A_w = rng.integers(-127, 128, size=(V, r_r), dtype=np.int8)
+    s_Ac = _abs_normal_f16(rng, 1e-2, V)
+    s_Aw = _abs_normal_f16(rng, 1e-2, V)
+    B_c = rng.integers(-127, 128, size=(r_c, D), dtype=np.int8)
+    B_w = rng.integers(-127, 128, size=(r_r, D), dtype=np.int8)
+    s_Bc = _abs_normal_f16(rng, 1e-2, (r_c, ng))
+    s_Bw = _abs_normal_f16(rng, 1e-2, (r_r, ng))
+    return Head(V, D, r_c, r_r, g, q4, c8, s_R, A_c, A_w, s_Ac, s_Aw, B_c, B_w, s_Bc, s_Bw)
+
+
+def make(cfg, seed: Optional[int] = None, N: Optional[int] = None, **overrides) -> Inputs:
+    """Draw one workload.  ``cfg`` is a CONFIGS entry, its name or its index.
+
+    ``N`` and keyword overrides (V, D, r_c, r_r, g, n_outlier, outlier_scale)
+    change the shape while keeping the distributions and the draw order.
+    """
+    if not isinstance(cfg, dict):
+        if seed is None and isinstance(cfg, int):
+            seed = cfg
+        cfg = config(cfg)
+    c = dict(cfg)
+    c.update(overrides)
+    if N is not None:
+        c["N"] = N
+    if seed is None:
+        seed = next((i for i, k in enumerate(CONFIGS) if k["name"] == c["name"]), 0)
+    rng = np.random.default_rng(seed)
+    H_bits, idx = draw_hidden(rng, c["N"], c["D"], c["n_outlier"], c["outlier_scale"])
+    head = draw_head(rng, c["V"], c["D"], c["r_c"], c["r_r"], c["g"])
+    return Inputs(H_bits=H_bits, head=head, outlier_channels=idx, seed=seed)
+
+
+def zero_head(V, D, r_c, r_r, g) -> Head:
+    """All-zero codes with unit scales; tests overwrite parts of it."""
+    ng = D // g
+    one = np.float16(1.0)
+    return Head(V, D, r_c, r_r, g,
+                np.zeros((V, D), np.int8), np.ones((V, ng), np.uint8),
+                np.full(V, one, np.float16),
+                np.zeros((V, r_c), np.int8), np.zeros((V, r_r), np.int8),
+                np.full(V, one, np.float16), np.full(V, one, np.float16),
+                np.zeros((r_c, D), np.int8), np.zeros((r_r, D), np.int8),
+                np.full((r_c, ng), one, np.float16), np.full((r_r, ng), one, np.float16))

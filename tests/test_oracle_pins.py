@@ -1,0 +1,453 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: the hand-derived golden files,
+exact integer arithmetic, a textbook reduction (group-INT4 dequantisation), a
+brute-force loop, or an algebraic invariant.  A wrong sign, index, dropped term
+or transposed operand anywhere in the oracle fails at least one of them.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+# ----------------------------------------------------------------- helpers ---
+
+
+def _f16_exact(bits: int) -> Fraction:
+    """IEEE binary16 decoded from its bits with integer arithmetic only."""
+    sign = -1 if bits & 0x8000 else 1
+    e = (bits >> 10) & 0x1F
+    m = bits & 0x3FF
+    assert e != 31
+    if e == 0:
+        return sign * Fraction(m, 1 << 24)
+    return sign * Fraction(1024 + m, 1 << 10) * (Fraction(2) ** (e - 15))
+
+
+def _bf16_exact(bits: int) -> Fraction:
+    """bfloat16 (8 exponent bits, 7 fraction bits) decoded with integers only."""
+    sign = -1 if bits & 0x8000 else 1
+    e = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    assert e != 255
+    if e == 0:
+        return sign * Fraction(m, 1 << 7) * Fraction(2) ** (-126)
+    return sign * Fraction(128 + m, 1 << 7) * Fraction(2) ** (e - 127)
+
+
+def _head_close(a, b):
+    """Bitwise equality of every stored component (a rank-0 part stores no scale)."""
+    keys = ["q4", "c8", "s_R", "A_c", "A_w", "B_c", "B_w", "s_Bc", "s_Bw"]
+    keys += ["s_Ac"] if a.r_c else []
+    keys += ["s_Aw"] if a.r_r else []
+    for k in keys:
+        x = np.ascontiguousarray(getattr(a, k) if not isinstance(a, dict) else a[k])
+        y = np.ascontiguousarray(b[k] if isinstance(b, dict) else getattr(b, k))
+        assert x.shape == y.shape, k
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), k
+
+
+# ------------------------------------------------------------ number decode ---
+
+def test_f16_decode_all_finite_patterns():
+    bits = np.arange(65536, dtype=np.uint32)
+    finite = ((bits >> 10) & 0x1F) != 31
+    bits = bits[finite].astype(np.uint16)
+    got = oracle.f16_to_f64(bits.view(np.float16))
+    want = np.array([float(_f16_exact(int(b))) for b in bits])
+    assert np.array_equal(got, want)
+
+
+def test_bf16_decode_all_finite_patterns():
+    bits = np.arange(65536, dtype=np.uint32)
+    finite = ((bits >> 7) & 0xFF) != 255
+    bits = bits[finite].astype(np.uint16)
+    got = oracle.bf16_bits_to_f64(bits)
+    want = np.array([float(_bf16_exact(int(b))) for b in bits])
+    assert np.array_equal(got, want)
+
+
+# -------------------------------------------------------------- the format ---
+
+def test_nibble_code_table():
+    """Signed INT4 in two's complement: the 16 nibble patterns and their values."""
+    table = [0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1]
+    h = synth.zero_head(16, 128, 0, 0, 32)
+    # put every nibble value at every low/high position of row 0 and row 9
+    for k in range(128):
+        h.q4[0, k] = table[k % 16]
+        h.q4[9, k] = table[(k * 7 + 3) % 16]
+    buf = oracle.pack(h)
+    u = oracle.unpack(buf, **h.dims)
+    assert np.array_equal(u["q4"], h.q4)
+    off = oracle.layout(**h.dims)["r_codes"][0]
+    # row 0, k = 0,1 -> tile 0 byte 0: low nibble code 0 (0x0), high nibble code 1 (0x1)
+    assert buf[off] == 0x10
+    # row 0, k = 14, 15 -> codes -2, -1 -> nibbles 0xE, 0xF; kk=14: s=0 q=1 c=3 -> l=16 -> byte 16*16+3
+    assert buf[off + 16 * 16 + 3] == 0xFE
+
+
+def test_golden_format_positions(golden_dir):
+    G = json.load(open(os.path.join(golden_dir, "format_v1_cases.json")))
+    d = G["dims"]
+    L = oracle.layout(**d)
+    for name, (off, size) in G["sections"].items():
+        assert tuple(L[name]) == (off, size), name
+    assert L["total_bytes"] == G["total_bytes"]
+    assert L["payload_bytes"] == G["payload_bytes"]
+
+    h = synth.zero_head(d["V"], d["D"], d["r_c"], d["r_r"], d["g"])
+    h.c8[:] = 0
+    h.s_R[:] = 0
+    h.s_Ac[:] = 0
+    h.s_Aw[:] = 0
+    h.s_Bc[:] = 0
+    h.s_Bw[:] = 0
+    for c in G["nibbles"]:
+        h.q4[c["v"], c["k"]] = c["code"]
+    for c in G["group_codes"]:
+        h.c8[c["v"], c["t"]] = c["code"]
+    for c in G["row_scale"]:
+        h.s_R.view(np.uint16)[c["v"]] = c["f16_bits"]
+    for c in G["a_codes"]:
+        (h.A_c if c["part"] == "c" else h.A_w)[c["v"], c["j"]] = c["code"]
+    for c in G["a_scales"]:
+        (h.s_Ac if c["part"] == "c" else h.s_Aw).view(np.uint16)[c["v"]] = c["f16_bits"]
+    for c in G["b_codes"]:
+        (h.B_c if c["part"] == "c" else h.B_w)[c["j"], c["k"]] = c["code"]
+    for c in G["b_scales"]:
+        (h.s_Bc if c["part"] == "c" else h.s_Bw).view(np.uint16)[c["j"], c["t"]] = c["f16_bits"]
+    buf = oracle.pack(h)
+    assert buf.size == G["total_bytes"]
+
+    expect = {}
+    for c in G["nibbles"]:
+        nib = c["code"] & 0xF
+        expect[c["byte"]] = expect.get(c["byte"], 0) | (nib if c["half"] == "lo" else nib << 4)
+    for c in G["group_codes"]:
+        expect[c["byte"]] = c["code"]
+    for c in G["row_scale"] + G["a_scales"] + G["b_scales"]:
+        expect[c["byte"]] = c["f16_bits"] & 0xFF
+        expect[c["byte"] + 1] = c["f16_bits"] >> 8
+    for c in G["a_codes"] + G["b_codes"]:
+        expect[c["byte"]] = c["code"] & 0xFF
+    # header
+    hdr = np.frombuffer(np.array([0x48435241, 1], np.uint32).tobytes() +
+                        np.array([d["V"], d["D"]], np.uint64).tobytes() +
+                        np.array([d["r_c"], d["r_r"], d["g"], 0], np.uint32).tobytes(), np.uint8)
+    for i, b in enumerate(hdr):
+        expect[i] = int(b)
+    nz = {int(i): int(buf[i]) for i in np.flatnonzero(buf)}
+    want = {k: v for k, v in expect.items() if v}
+    assert nz == want
+    for c in G["row_scale"] + G["a_scales"] + G["b_scales"]:
+        assert float(_f16_exact(c["f16_bits"])) == c["value"]
+
+
+def _tile_pack_loop(q4_padded):
+    """Element-by-element reading of the residual tile order (tiny shapes only)."""
+    V16, D = q4_padded.shape
+    out = np.zeros(V16 * D // 2, np.uint8)
+    nkt = D // 128
+    for v in range(V16):
+        for k in range(0, D, 2):
+            b, i = divmod(v, 16)
+            kt, kk = divmod(k, 128)
+            s, rem = divmod(kk, 32)
+            q, rem8 = divmod(rem, 8)
+            c = rem8 // 2
+            lane = 16 * q + i
+            pos = (b * nkt + kt) * 1024 + 16 * lane + 4 * s + c
+            lo = int(q4_padded[v, k]) & 0xF
+            hi = int(q4_padded[v, k + 1]) & 0xF
+            out[pos] = lo | (hi << 4)
+    return out
+
+
+@pytest.mark.parametrize("V,D", [(16, 128), (33, 256), (5, 384)])
+def test_tile_order_matches_loop(V, D):
+    rng = np.random.default_rng(V * D)
+    h = synth.draw_head(rng, V, D, 8, 0, 32)
+    buf = oracle.pack(h)
+    L = oracle.layout(**h.dims)
+    off, size = L["r_codes"]
+    q = np.zeros((L["V16"], D), np.int8)
+    q[:V] = h.q4
+    assert np.array_equal(buf[off:off + size], _tile_pack_loop(q))
+
+
+@pytest.mark.parametrize("V,D,r_c,r_r,g", [
+    (1024, 256, 16, 8, 64), (37, 128, 0, 0, 128), (50, 512, 0, 24, 32),
+    (16, 256, 40, 0, 256), (129, 384, 8, 8, 64), (1, 128, 6, 6, 128)])
+def test_pack_unpack_roundtrip(V, D, r_c, r_r, g):
+    rng = np.random.default_rng(V + D + r_c)
+    h = synth.draw_head(rng, V, D, r_c, r_r, g)
+    buf = oracle.pack(h)
+    u = oracle.unpack(buf, V, D, r_c, r_r, g)
+    assert (u["magic"], u["version"]) == (oracle.MAGIC, oracle.FORMAT_VERSION)
+    assert (u["V"], u["D"], u["r_c"], u["r_r"], u["g"]) == (V, D, r_c, r_r, g)
+    assert u["pad_rows_zero"]
+    _head_close(h, u)
+
+
+def test_layout_sections_aligned_disjoint_and_no_dense_matrix():
+    for c in synth.CONFIGS:
+        d = dict(V=c["V"], D=c["D"], r_c=c["r_c"], r_r=c["r_r"], g=c["g"])
+        L = oracle.layout(**d)
+        spans = sorted(L[n] for n in ["header", "r_codes", "r_gcodes", "r_rowscale",
+                                      "a_codes", "a_scales", "b_codes", "b_scales"])
+        end = 0
+        for off, size in spans:
+            assert off % 256 == 0 and off >= end
+            end = off + size
+        assert L["total_bytes"] >= end and L["total_bytes"] % 256 == 0
+        # a dense V x D matrix at 8 bits or more would need V*D bytes; no section is that big
+        biggest = max(size for _, size in spans)
+        assert biggest == L["r_codes"][1] == c["V"] * c["D"] // 2 < c["V"] * c["D"]
+
+
+def test_persistent_size_equals_sum_of_stored_tensors():
+    """Sec. 3 persistent-size equation: the payload is the sum over the stored
+    tensors of numel x element size.  Values for the five workloads were worked
+    out from that closed form independently."""
+    expect = {"tiny": 172224, "decode": 326928640, "batched": 326928640,
+              "prefill": 336918784, "head70b": 551796224}
+    for c in synth.CONFIGS:
+        d = dict(V=c["V"], D=c["D"], r_c=c["r_c"], r_r=c["r_r"], g=c["g"])
+        assert oracle.layout(**d)["payload_bytes"] == oracle.persistent_bytes(**d) == expect[c["name"]]
+    # no factors: a plain group-INT4 head with a uint8 group code and an fp16 row scale
+    assert oracle.persistent_bytes(1024, 4096, 0, 0, 128) == 1024 * 2048 + 1024 * 32 + 2048
+
+
+def test_storage_ratio_matches_pages():
+    """The pages quote 25.61% of the BF16 head for the packed Qwen3-8B head
+    (Sec. 5, comparison with GPTQ) and a rank-6 correction (Table 9 ablation);
+    read with r_c = r_r = 6 and g = 128 the format gives the same 25.61%, i.e. a
+    3.90x reduction (the abstract's 3.7-3.9x range)."""
+    V, D = 151936, 4096
+    ratio = oracle.persistent_bytes(V, D, 6, 6, 128) / (2 * V * D)
+    assert round(100 * ratio, 2) == 25.61
+    assert 3.7 <= 1 / ratio <= 3.91
+    # the GPTQ-style INT4 head quoted beside it: 4 bits + one fp16 per 128 weights
+    assert round(100 * (4 + 16 / 128) / 16, 2) == 25.78
+
+
+# ------------------------------------------------------------ dequantisation ---
+
+def test_golden_dequant_cases(golden_dir):
+    G = json.load(open(os.path.join(golden_dir, "dequant_cases.json")))
+    for c in G["cases"]:
+        q4 = np.array([[c["q4"]] * 2], np.int8)
+        c8 = np.array([[c["c8"]]], np.uint8)
+        sR = np.array([c["s_R_bits"]], np.uint16).view(np.float16)
+        R = oracle.dequant_R(q4, c8, sR, 2)
+        assert R[0, 0] == c["expect"] and R[0, 1] == c["expect"], c
+
+
+def test_dequant_group_boundaries():
+    """Column k uses group k // g: move one group code and only that group changes."""
+    V, D, g = 3, 256, 64
+    q4 = np.ones((V, D), np.int8)
+    c8 = np.array([[1, 2, 3, 4]] * V, np.uint8)
+    sR = np.array([1.0, 0.5, 2.0], np.float16)
+    R = oracle.dequant_R(q4, c8, sR, g)
+    for k in range(D):
+        assert np.array_equal(R[:, k], (k // g + 1) * np.array([1.0, 0.5, 2.0]))
+    B = oracle.dequant_groups(np.full((2, D), -2, np.int8),
+                              np.array([[1, 2, 4, 8], [0.25, 0.5, 1, 2]], np.float16), g)
+    assert B[0, 63] == -2 and B[0, 64] == -4 and B[1, 255] == -4 and B[1, 0] == -0.5
+    A = oracle.dequant_rows(np.array([[1, -127], [127, 0]], np.int8), np.array([0.5, 4.0], np.float16))
+    assert A.tolist() == [[0.5, -63.5], [508.0, 0.0]]
+
+
+# ------------------------------------------------------------- the forward ---
+
+def _exact_logits(H_bits, h):
+    """Y computed exactly with Python integers.  Every stored value is an
+    integer times a power of two: bf16 H values are multiples of 2^-133 and fp16
+    scales are multiples of 2^-24, so scaling by those powers gives integers."""
+    N, D = H_bits.shape
+    SH = 133
+    Hi = np.array([[int(_bf16_exact(int(b)) * (1 << SH)) for b in row] for row in H_bits], dtype=object)
+    f16i = lambda a: np.array([int(_f16_exact(int(b)) * (1 << 24)) for b in np.asarray(a).view(np.uint16).reshape(-1)],
+                              dtype=object).reshape(np.asarray(a).shape)
+    g = h.g
+    # residual: integer weight q4 * c8 * (s_R * 2^24), column by column of the D axis
+    sR = f16i(h.s_R)
+    Wq = np.empty((h.V, D), dtype=object)
+    for v in range(h.V):
+        for k in range(D):
+            Wq[v, k] = int(h.q4[v, k]) * int(h.c8[v, k // g]) * sR[v]
+    Yint = (Hi.dot(Wq.T)) * (1 << 48)                       # units 2^-(SH+24) -> 2^-(SH+72)
+    for A, sA, B, sB in ((h.A_c, h.s_Ac, h.B_c, h.s_Bc), (h.A_w, h.s_Aw, h.B_w, h.s_Bw)):
+        r = A.shape[1]
+        if r == 0:
+            continue
+        sAi, sBi = f16i(sA), f16i(sB)
+        Bq = np.empty((r, D), dtype=object)
+        for j in range(r):
+            for k in range(D):
+                Bq[j, k] = int(B[j, k]) * sBi[j, k // g]
+        Aq = np.empty((h.V, r), dtype=object)
+        for v in range(h.V):
+            for j in range(r):
+                Aq[v, j] = int(A[v, j]) * sAi[v]
+        # Hi*Bq is in units of 2^-(SH+24), times Aq 2^-(SH+48); bring to 2^-(SH+72)
+        Yint = Yint + (Hi.dot(Bq.T)).dot(Aq.T) * (1 << 24)
+    return Yint, SH + 72
+
+
+def test_exact_rational_tiny_workload():
+    """The fp64 oracle against exact integer evaluation on the tiny workload."""
+    inp = synth.make("tiny")
+    h = inp.head
+    SH = 133
+    Yint, _ = _exact_logits_scaled(inp.H_bits, h, SH)
+    Y = oracle.logits(inp.H_bits, h)
+    exact = np.array([[float(Fraction(int(x), 1 << (SH + 72))) for x in row] for row in Yint])
+    scale = np.abs(exact).max()
+    assert scale > 0
+    assert np.abs(Y - exact).max() <= 1e-12 * scale
+
+
+def _exact_logits_scaled(H_bits, h, SH):
+    """Integer Y in units of 2^-(SH+72): residual term (units 2^-(SH+24)) times
+    2^48 plus each low-rank term (units 2^-(SH+48)) times 2^24."""
+    N, D = H_bits.shape
+    Hi = np.array([[int(_bf16_exact(int(b)) * (1 << SH)) for b in row] for row in H_bits], dtype=object)
+
+    def f16i(a):
+        a = np.asarray(a)
+        flat = [int(_f16_exact(int(b)) * (1 << 24)) for b in a.view(np.uint16).reshape(-1)]
+        return np.array(flat, dtype=object).reshape(a.shape)
+
+    g = h.g
+    sR = f16i(h.s_R)
+    c8 = h.c8.astype(object)
+    Wq = h.q4.astype(object) * np.repeat(c8, g, axis=1) * sR[:, None]
+    Y = Hi.dot(Wq.T) * (1 << 48)
+    for A, sA, B, sB in ((h.A_c, h.s_Ac, h.B_c, h.s_Bc), (h.A_w, h.s_Aw, h.B_w, h.s_Bw)):
+        if A.shape[1] == 0:
+            continue
+        Bq = B.astype(object) * np.repeat(f16i(sB), g, axis=1)
+        Aq = A.astype(object) * f16i(sA)[:, None]
+        Y = Y + Hi.dot(Bq.T).dot(Aq.T) * (1 << 24)
+    return Y, SH + 72
+
+
+def test_exact_rational_loop_form_small():
+    """Same exactness pin, written as scalar loops, on a shape small enough for them."""
+    inp = synth.make("tiny", V=40, D=128, N=3, r_c=8, r_r=16, g=32, n_outlier=2)
+    h = inp.head
+    Yint, _ = _exact_logits(inp.H_bits, h)
+    exact = np.array([[float(Fraction(int(x), 1 << (133 + 72))) for x in row] for row in Yint])
+    Y = oracle.logits(inp.H_bits, h)
+    assert np.abs(Y - exact).max() <= 1e-12 * np.abs(exact).max()
+
+
+def test_no_factors_reduces_to_group_int4():
+    """r_c = r_r = 0: the forward is the textbook group-INT4 matvec,
+    Y[n,v] = s_R[v] * sum_t c8[v,t] * sum_{k in group t} q4[v,k] h[n,k],
+    computed here in the integer-group-sum association order."""
+    inp = synth.make("tiny", r_c=0, r_r=0, V=300, N=5)
+    h = inp.head
+    Y = oracle.logits(inp.H_bits, h)
+    H = oracle.bf16_bits_to_f64(inp.H_bits)
+    g, ng = h.g, h.D // h.g
+    part = np.einsum("vtk,ntk->nvt", h.q4.reshape(h.V, ng, g).astype(np.float64),
+                     H.reshape(H.shape[0], ng, g))
+    Y2 = np.einsum("nvt,vt->nv", part, h.c8.astype(np.float64)) * h.s_R.astype(np.float64)[None, :]
+    assert np.allclose(Y, Y2, rtol=0, atol=1e-12 * np.abs(Y).max())
+
+
+def test_low_rank_term_brute_force():
+    """q4 = 0: Y = H (A_c_hat B_c_hat + A_w_hat B_w_hat)^T, checked with a
+    triple loop and with the (H B_hat^T) A_hat^T order of the inference step."""
+    inp = synth.make("tiny", V=24, D=128, N=3, r_c=8, r_r=8, g=32, n_outlier=1)
+    h = inp.head
+    h.q4[:] = 0
+    Y = oracle.logits(inp.H_bits, h)
+    H = oracle.bf16_bits_to_f64(inp.H_bits)
+    sBc = h.s_Bc.astype(np.float64)
+    sBw = h.s_Bw.astype(np.float64)
+    brute = np.zeros_like(Y)
+    for n in range(3):
+        for v in range(h.V):
+            acc = 0.0
+            for k in range(h.D):
+                w = 0.0
+                for j in range(h.r_c):
+                    w += float(h.A_c[v, j]) * float(h.s_Ac[v]) * float(h.B_c[j, k]) * sBc[j, k // h.g]
+                for j in range(h.r_r):
+                    w += float(h.A_w[v, j]) * float(h.s_Aw[v]) * float(h.B_w[j, k]) * sBw[j, k // h.g]
+                acc += H[n, k] * w
+            brute[n, v] = acc
+    assert np.allclose(Y, brute, rtol=0, atol=1e-12 * np.abs(Y).max())
+    Bc = h.B_c * np.repeat(sBc, h.g, axis=1)
+    Bw = h.B_w * np.repeat(sBw, h.g, axis=1)
+    Zc, Zw = H @ Bc.T, H @ Bw.T
+    Y3 = (Zc @ (h.A_c * h.s_Ac.astype(np.float64)[:, None]).T +
+          Zw @ (h.A_w * h.s_Aw.astype(np.float64)[:, None]).T)
+    assert np.allclose(Y, Y3, rtol=0, atol=1e-12 * np.abs(Y).max())
+
+
+def test_one_hot_rows_give_the_dequantised_weights():
+    inp = synth.make("tiny", V=64, D=256, r_c=0, r_r=0)
+    h = inp.head
+    eye = synth.f32_to_bf16_bits(np.eye(h.D, dtype=np.float32))
+    Y = oracle.logits(eye, h)
+    R = oracle.dequant_R(h.q4, h.c8, h.s_R, h.g)
+    assert np.array_equal(Y, R.T)
+
+
+def test_invariants():
+    inp = synth.make("tiny")
+    h = inp.head
+    Y = oracle.logits(inp.H_bits, h)
+    # scaling H by 2 (an exponent bump in bf16) scales Y by 2 exactly
+    H2 = (inp.H_bits.astype(np.uint32) + (1 << 7)).astype(np.uint16)
+    assert np.array_equal(oracle.logits(H2, h), 2 * Y)
+    # permuting vocabulary rows permutes the columns of Y
+    perm = np.random.default_rng(0).permutation(h.V)
+    hp = synth.Head(h.V, h.D, h.r_c, h.r_r, h.g, h.q4[perm], h.c8[perm], h.s_R[perm],
+                    h.A_c[perm], h.A_w[perm], h.s_Ac[perm], h.s_Aw[perm],
+                    h.B_c, h.B_w, h.s_Bc, h.s_Bw)
+    assert np.array_equal(oracle.logits(inp.H_bits, hp), Y[:, perm])
+    # all-zero codes give Y = 0
+    z = synth.zero_head(h.V, h.D, h.r_c, h.r_r, h.g)
+    assert not np.any(oracle.logits(inp.H_bits, z))
+    # linearity in H over exactly representable sums (disjoint supports)
+    Ha = inp.H_bits.copy()
+    Hb = inp.H_bits.copy()
+    Ha[:, 1::2] = 0
+    Hb[:, 0::2] = 0
+    assert np.allclose(oracle.logits(Ha, h) + oracle.logits(Hb, h), Y, rtol=0, atol=1e-12 * np.abs(Y).max())
+    # doubling one row scale doubles that column's residual part exactly
+    hz = synth.make("tiny", r_c=0, r_r=0).head
+    Yz = oracle.logits(inp.H_bits, hz)
+    hz.s_R[7] = hz.s_R[7] * np.float16(2)
+    Y7 = oracle.logits(inp.H_bits, hz)
+    assert np.array_equal(Y7[:, 7], 2 * Yz[:, 7])
+    assert np.array_equal(np.delete(Y7, 7, 1), np.delete(Yz, 7, 1))
+
+
+def test_row_selection_and_chunking_agree():
+    inp = synth.make("tiny")
+    h = inp.head
+    Y = oracle.logits(inp.H_bits, h)
+    # BLAS may block differently per chunk: agreement to fp64 rounding
+    assert np.allclose(oracle.logits(inp.H_bits, h, v_chunk=100), Y, rtol=0, atol=1e-12 * np.abs(Y).max())
+    cols = np.array([5, 900, 3, 1023])
+    assert np.allclose(oracle.logits(inp.H_bits, h, rows=[2, 0], cols=cols), Y[[2, 0]][:, cols],
+                       rtol=0, atol=1e-12 * np.abs(Y).max())
+
+
+def test_argmax_ties_and_gap():
+    Y = np.array([[1.0, 3.0, 3.0, -1.0], [0.0, 0.0, 0.0, 0.0], [-5.0, -4.0, -4.5, -9.0]])
+    assert oracle.row_argmax(Y).tolist() == [1, 0, 1]
+    assert oracle.top2_gap(Y).tolist() == [0.0, 0.0, 0.5]
