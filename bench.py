@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed ARCHead LM-head forward on one MI355X.
+
+Prints ONE JSON line.  ``value`` is the decode throughput (GB/s of packed head
+bytes per forward, whole call: pre-projection + decode kernel) on the
+Qwen3-8B-shaped decode workload (V=151936, D=4096, N=1, r_c=r_r=32, g=128);
+``secondary`` carries the other half of the metric, prefill TFLOP/s on
+V=151936, D=4096, N=4096, r_c=r_r=64, g=128 with bf16 logits.
+
+Inputs are seeded synthetic tensors already resident in HBM.  Two device
+copies of the packed head alternate between steps so the 256 MB last-level
+cache cannot serve a head that was just read.  ``roofline`` times the dominant
+kernel with HIP events that the library records on the launch stream.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed-head logits: decode HBM GB/s and prefill TFLOP/s (% of roofline), V=151936"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+KERNEL_SOURCES = ["prep.hip", "decode.hip", "tile.hip", "device_common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg, L, N):
+    """Algorithmic bytes and flops of one forward, split as the kernels split it.
+
+    Per vocabulary row the decode kernel must read D/2 + D/g + 2 + r + 2*nA
+    bytes of the packed head and write N logits; per call it reads the
+    converted hidden states (2*N*D) and the pre-projection (4*N*(rc32+rr32)).
+    The main contraction does 2*(D + r) flops per logit; the pre-projection
+    2*N*D*r.
+    """
+    V, D, g, r_c, r_r = cfg["V"], cfg["D"], cfg["g"], cfg["r_c"], cfg["r_r"]
+    r = r_c + r_r
+    nA = (r_c > 0) + (r_r > 0)
+    ysz = 2 if cfg["y_dtype"] == "bf16" else 4
+    rc32, rr32 = -(-r_c // 32) * 32, -(-r_r // 32) * 32
+    per_row = D // 2 + D // g + 2 + r + 2 * nA
+    main_bytes = V * per_row + N * V * ysz + 2 * N * D + 4 * N * (rc32 + rr32)
+    main_flops = 2 * N * V * (D + r)
+    total_flops = main_flops + 2 * N * D * r
+    return dict(per_row_bytes=per_row, main_bytes=main_bytes, main_flops=main_flops,
+                total_flops=total_flops, payload=L["payload_bytes"],
+                step_bytes=L["payload_bytes"] + 2 * N * D + N * V * ysz)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "compressed_output_head_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload, per_launch_units):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def run_workload(name, steps, warmup, path=0):
+    import torch
+    import synth
+    import compressed_output_head_amd as ah
+
+    cfg = synth.config(name)
+    t0 = time.time()
+    inp = synth.make(name)
+    packed = ah.archead_pack(inp.head)
+    L = ah.archead_pack_layout(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"])
+    heads = [ah.PackedHead(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], packed)]
+    heads.append(ah.PackedHead(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], heads[0].buffer.clone()))
+    N = cfg["N"]
+    H = torch.from_numpy(inp.H_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    ydt = torch.bfloat16 if cfg["y_dtype"] == "bf16" else torch.float32
+    Y = torch.empty((N, cfg["V"]), dtype=ydt, device="cuda")
+    for h in heads:
+        h.ensure_workspace(N)
+    del inp
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s "
+        f"(packed head {L['payload_bytes'] / 1e6:.1f} MB payload, x2 copies)")
+
+    stream = torch.cuda.current_stream()
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    eve = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in evb + eve:
+        e.record(stream)  # creates the underlying hipEvent
+    for i in range(warmup):
+        ah.archead_logits_path(H, heads[i % 2], Y, path)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        ah.archead_logits_events(H, heads[i % 2], Y, path, evb[i], eve[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kms = [evb[i].elapsed_time(eve[i]) for i in range(steps)]
+    A = algorithmic(cfg, L, N)
+    return dict(cfg=cfg, L=L, A=A, ms=ms, kernel_ms=float(np.mean(kms)),
+                kernel_ms_min=float(np.min(kms)), kernel_ms_max=float(np.max(kms)))
+
+
+def cpu_baseline(name, sample_rows):
+    """The oracle as it stands, timed on a bounded vocabulary sample."""
+    import synth
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    cfg = synth.config(name)
+    inp = synth.make(name)
+    cols = np.arange(min(sample_rows, cfg["V"]))
+    t0 = time.time()
+    oracle.logits(inp.H_bits, inp.head, cols=cols)
+    dt = time.time() - t0
+    L = oracle.layout(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"])
+    sample_bytes = L["payload_bytes"] * cols.size / cfg["V"]
+    return dict(value=round(sample_bytes / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"fp64 oracle (unpack, rebuild W_hat, H W_hat^T) on vocabulary rows 0..{cols.size - 1} "
+                       f"of the {name} workload, {dt:.1f}s; GB/s of packed bytes of those rows")
+
+
+def roofline_decode(r):
+    A = r["A"]
+    achieved = A["main_bytes"] / (r["kernel_ms"] / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(r["cfg"]["name"], 1),
+            "kernel": "decode_kernel", "kernel_ms": round(r["kernel_ms"], 5),
+            "algorithmic_bytes_per_launch": A["main_bytes"]}
+
+
+def roofline_tile(r):
+    A = r["A"]
+    achieved = A["main_flops"] / (r["kernel_ms"] / 1e3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic_for(r["cfg"]["name"], 1),
+            "kernel": "tile_kernel", "kernel_ms": round(r["kernel_ms"], 4),
+            "algorithmic_flops_per_launch": A["main_flops"]}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode", help="headline workload (decode or batched)")
+    ap.add_argument("--secondary", default="prefill", help="second workload ('' to skip)")
+    ap.add_argument("--cpu-sample-rows", type=int, default=24576)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+
+    r = run_workload(args.config, args.steps, args.warmup)
+    cfg, A = r["cfg"], r["A"]
+    value = A["payload"] / (r["ms"] / 1e3) / 1e9
+    log(f"[bench] {args.config}: {r['ms'] * 1e3:.1f} us/step, decode kernel {r['kernel_ms'] * 1e3:.1f} us")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "V": cfg["V"], "D": cfg["D"], "N": cfg["N"], "r_c": cfg["r_c"],
+                   "r_r": cfg["r_r"], "g": cfg["g"], "logits": cfg["y_dtype"],
+                   "packed_payload_bytes": A["payload"], "head_copies_rotated": 2},
+        "roofline": roofline_decode(r),
+    }
+    if args.secondary:
+        s = run_workload(args.secondary, max(5, args.steps // 5), max(2, args.warmup // 5))
+        tf = s["A"]["total_flops"] / (s["ms"] / 1e3) / 1e12
+        log(f"[bench] {args.secondary}: {s['ms']:.3f} ms/step, tile kernel {s['kernel_ms']:.3f} ms")
+        out["secondary"] = {
+            "workload": s["cfg"]["name"], "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(s["ms"], 4), "steps": max(5, args.steps // 5),
+            "config": {k: s["cfg"][k] for k in ("V", "D", "N", "r_c", "r_r", "g")} | {"logits": s["cfg"]["y_dtype"]},
+            "roofline": roofline_tile(s),
+        }
+    out["kernel_sources"] = kernel_hash()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

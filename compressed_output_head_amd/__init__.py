@@ -1,0 +1,254 @@
+"""Python binding of libarchead: the packed ARCHead LM-head forward on MI355X.
+
+The functions below carry the names of the C entry points in
+``include/archead.h`` and only marshal arguments: every step of the forward
+runs in the library's HIP kernels.  Torch is used for device memory and the
+current stream.  Importing the package fails loudly when ``libarchead.so`` has
+not been built (``python compressed_output_head_amd/build.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libarchead.so")
+
+ARCHEAD_OK = 0
+ARCHEAD_BF16, ARCHEAD_F32 = 1, 2
+ARCHEAD_PATH_AUTO, ARCHEAD_PATH_DECODE, ARCHEAD_PATH_TILE = 0, 1, 2
+STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5: "E_SHAPE",
+          6: "E_ALIGN", 7: "E_WORKSPACE", 8: "E_HIP", 9: "E_VALUE", 10: "E_SIZE"}
+EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_pack", "archead_logits",
+           "archead_logits_path", "archead_logits_events", "archead_status_string",
+           "archead_format_version")
+
+
+class ArcheadError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {archead_status_string(status)}")
+
+
+class ArcheadDims(ctypes.Structure):
+    _fields_ = [("V", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("r_c", ctypes.c_int32), ("r_r", ctypes.c_int32), ("g", ctypes.c_int32)]
+
+
+class ArcheadSpan(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_uint64), ("bytes", ctypes.c_uint64)]
+
+
+_SECTIONS = ("header", "r_codes", "r_gcodes", "r_rowscale", "a_codes", "a_scales", "b_codes", "b_scales")
+
+
+class ArcheadLayout(ctypes.Structure):
+    _fields_ = ([("format_version", ctypes.c_uint32), ("alignment", ctypes.c_uint32),
+                 ("total_bytes", ctypes.c_uint64), ("payload_bytes", ctypes.c_uint64),
+                 ("header_bytes", ctypes.c_uint64)]
+                + [(n, ArcheadSpan) for n in _SECTIONS]
+                + [("padded_rows", ctypes.c_int64)])
+
+
+class ArcheadHostComponents(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q4", "c8", "s_R", "A_c", "A_w", "s_Ac", "s_Aw", "B_c", "B_w", "s_Bc", "s_Bw")]
+
+
+class ArcheadTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+
+class ArcheadPackedHead(ctypes.Structure):
+    _fields_ = [("dims", ArcheadDims), ("buffer", ctypes.c_void_p), ("buffer_bytes", ctypes.c_uint64),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python compressed_output_head_amd/build.py`")
+    # torch ships its own libamdhip64 (same soname).  Loading torch first makes
+    # the dynamic linker bind libarchead to that one HIP runtime, so torch's
+    # streams, events and allocations are valid handles for the library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.archead_pack_layout.argtypes = [P(ArcheadDims), P(ArcheadLayout)]
+    lib.archead_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int64, P(ctypes.c_uint64)]
+    lib.archead_pack.argtypes = [P(ArcheadDims), P(ArcheadHostComponents), ctypes.c_void_p, ctypes.c_uint64]
+    lib.archead_logits.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor), ctypes.c_void_p]
+    lib.archead_logits_path.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor),
+                                        ctypes.c_int, ctypes.c_void_p]
+    lib.archead_logits_events.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor),
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.archead_status_string.argtypes = [ctypes.c_int]
+    lib.archead_status_string.restype = ctypes.c_char_p
+    lib.archead_format_version.argtypes = []
+    for name in EXPORTS:
+        if name not in ("archead_status_string",):
+            getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _dims(V, D, r_c, r_r, g) -> ArcheadDims:
+    return ArcheadDims(int(V), int(D), int(r_c), int(r_r), int(g))
+
+
+def _check(status: int, where: str):
+    if status != ARCHEAD_OK:
+        raise ArcheadError(status, where)
+
+
+# ------------------------------------------------------------- host calls ---
+
+def archead_status_string(status: int) -> str:
+    return lib.archead_status_string(int(status)).decode()
+
+
+def archead_format_version() -> int:
+    return lib.archead_format_version()
+
+
+def archead_pack_layout(V, D, r_c, r_r, g) -> dict:
+    """Section offsets/sizes of the packed buffer (see include/archead.h)."""
+    L = ArcheadLayout()
+    _check(lib.archead_pack_layout(ctypes.byref(_dims(V, D, r_c, r_r, g)), ctypes.byref(L)),
+           "archead_pack_layout")
+    out = {n: (getattr(L, n).offset, getattr(L, n).bytes) for n in _SECTIONS}
+    out.update(total_bytes=L.total_bytes, payload_bytes=L.payload_bytes, header_bytes=L.header_bytes,
+               format_version=L.format_version, alignment=L.alignment, V16=L.padded_rows)
+    return out
+
+
+def archead_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
+    b = ctypes.c_uint64()
+    _check(lib.archead_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
+                                       ctypes.byref(b)), "archead_workspace_bytes")
+    return b.value
+
+
+def _ptr(a: Optional[np.ndarray], dtype):
+    if a is None or a.size == 0:
+        return None, None
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+def archead_pack(head) -> np.ndarray:
+    """Serialise host components (an object with attributes V, D, r_c, r_r, g,
+    q4, c8, s_R, A_c, A_w, s_Ac, s_Aw, B_c, B_w, s_Bc, s_Bw) into a uint8 array."""
+    d = _dims(head.V, head.D, head.r_c, head.r_r, head.g)
+    L = archead_pack_layout(head.V, head.D, head.r_c, head.r_r, head.g)
+    out = np.empty(L["total_bytes"], np.uint8)
+    keep = []
+    comp = ArcheadHostComponents()
+    spec = [("q4", np.int8), ("c8", np.uint8), ("s_R", np.float16), ("A_c", np.int8), ("A_w", np.int8),
+            ("s_Ac", np.float16), ("s_Aw", np.float16), ("B_c", np.int8), ("B_w", np.int8),
+            ("s_Bc", np.float16), ("s_Bw", np.float16)]
+    for name, dt in spec:
+        arr, p = _ptr(getattr(head, name), dt)
+        keep.append(arr)
+        setattr(comp, name, p)
+    _check(lib.archead_pack(ctypes.byref(d), ctypes.byref(comp), out.ctypes.data, out.nbytes), "archead_pack")
+    return out
+
+
+# ----------------------------------------------------------- device calls ---
+
+def _torch():
+    import torch
+    return torch
+
+
+class PackedHead:
+    """A packed head resident in device memory plus a reusable workspace."""
+
+    def __init__(self, V, D, r_c, r_r, g, buffer, device=None):
+        torch = _torch()
+        self.V, self.D, self.r_c, self.r_r, self.g = int(V), int(D), int(r_c), int(r_r), int(g)
+        self.layout = archead_pack_layout(V, D, r_c, r_r, g)
+        if isinstance(buffer, np.ndarray):
+            buffer = torch.from_numpy(buffer).to(device or "cuda")
+        if buffer.dtype != torch.uint8 or buffer.numel() < self.layout["total_bytes"]:
+            raise ValueError("packed buffer must be uint8 with at least layout total_bytes elements")
+        self.buffer = buffer
+        self.workspace = None
+
+    @classmethod
+    def from_components(cls, head, device="cuda") -> "PackedHead":
+        return cls(head.V, head.D, head.r_c, head.r_r, head.g, archead_pack(head), device=device)
+
+    @property
+    def dims(self):
+        return dict(V=self.V, D=self.D, r_c=self.r_c, r_r=self.r_r, g=self.g)
+
+    def ensure_workspace(self, n_tokens: int):
+        torch = _torch()
+        need = archead_workspace_bytes(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens)
+        if self.workspace is None or self.workspace.numel() < need:
+            self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.buffer.device)
+        return self.workspace
+
+    def struct(self) -> ArcheadPackedHead:
+        ws = self.workspace
+        return ArcheadPackedHead(_dims(self.V, self.D, self.r_c, self.r_r, self.g),
+                                 self.buffer.data_ptr(), self.buffer.numel(),
+                                 ws.data_ptr() if ws is not None else None,
+                                 ws.numel() if ws is not None else 0)
+
+
+def _tensor(t) -> ArcheadTensor:
+    torch = _torch()
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    code = {torch.bfloat16: ARCHEAD_BF16, torch.float32: ARCHEAD_F32}.get(t.dtype, 0)
+    return ArcheadTensor(t.data_ptr(), t.shape[0], t.shape[1], t.stride(0), code)
+
+
+def archead_logits_path(H, head: PackedHead, Y, path: int = ARCHEAD_PATH_AUTO, stream=None):
+    """Y = H W_hat^T on the GPU.  H: bf16 [N, D]; Y: fp32 or bf16 [N, V] (written)."""
+    torch = _torch()
+    head.ensure_workspace(H.shape[0])
+    if stream is None:
+        stream = torch.cuda.current_stream(H.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    h, y, p = _tensor(H), _tensor(Y), head.struct()
+    _check(lib.archead_logits_path(ctypes.byref(h), ctypes.byref(p), ctypes.byref(y), int(path),
+                                   ctypes.c_void_p(stream)), "archead_logits")
+    return Y
+
+
+def archead_logits_events(H, head: PackedHead, Y, path: int, ev_begin, ev_end, stream=None):
+    """archead_logits_path that also records two torch.cuda.Event objects
+    around the main kernel (each must have been recorded once, so it exists)."""
+    torch = _torch()
+    head.ensure_workspace(H.shape[0])
+    if stream is None:
+        stream = torch.cuda.current_stream(H.device).cuda_stream
+    h, y, p = _tensor(H), _tensor(Y), head.struct()
+    _check(lib.archead_logits_events(ctypes.byref(h), ctypes.byref(p), ctypes.byref(y), int(path),
+                                     ctypes.c_void_p(stream), ctypes.c_void_p(ev_begin.cuda_event),
+                                     ctypes.c_void_p(ev_end.cuda_event)), "archead_logits_events")
+    return Y
+
+
+def archead_logits(H, head: PackedHead, Y, stream=None):
+    return archead_logits_path(H, head, Y, ARCHEAD_PATH_AUTO, stream)
+
+
+def logits(H, head: PackedHead, out_dtype=None, path: int = ARCHEAD_PATH_AUTO):
+    """Allocate Y and run the forward; returns Y (fp32 unless out_dtype says bf16)."""
+    torch = _torch()
+    Y = torch.empty((H.shape[0], head.V), dtype=out_dtype or torch.float32, device=H.device)
+    return archead_logits_path(H, head, Y, path)

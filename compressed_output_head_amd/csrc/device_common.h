@@ -1,0 +1,104 @@
+// Device helpers shared by the gfx950 kernels: operand types, exact integer
+// unpacking into fp16 MFMA operands, and number conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace archead {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// Kernel k-order inside one 8-column run of an MFMA operand.  Operand slot j
+// (0..7) of a lane carries column kOrderH[j] of the run for H and the residual
+// codes, and column kOrderZ[j] for the pre-projection and the A codes.  Both
+// operands of every MFMA use the same order, so the dot product is unchanged.
+//   residual dword bytes (k0k1)(k2k3)(k4k5)(k6k7) unpack to slots k0 k4 k1 k5 k2 k6 k3 k7
+//   A-code dwords (j0 j1 j2 j3)(j4 j5 j6 j7) unpack to slots j0 j2 j1 j3 j4 j6 j5 j7
+__host__ __device__ constexpr int k_order_h(int j) { return (j >> 1) + 4 * (j & 1); }
+__host__ __device__ constexpr int k_order_z(int j) {
+  return 4 * (j >> 2) + ((j & 3) >> 1) + 2 * (j & 1);
+}
+
+__device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ h2 bits_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+
+// 0x6400 is fp16 1024.0, whose ulp is 1: OR-ing an unsigned value u < 1024
+// into the low mantissa bits gives exactly 1024 + u.
+constexpr uint32_t kF16Magic2 = 0x64006400u;
+
+// Eight signed INT4 codes (one dword, low nibble first) -> eight exact fp16
+// values in k_order_h.  The XOR moves two's complement [-8,7] to offset-binary
+// u = q + 8, so 1024 + u - 1032 = q exactly.
+__device__ __forceinline__ h8 unpack_q4(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const uint32_t r0 = h2_bits(bits_h2((x & 0x000F000Fu) | kF16Magic2) - bias);
+  const uint32_t r1 = h2_bits(bits_h2(((x >> 4) & 0x000F000Fu) | kF16Magic2) - bias);
+  const uint32_t r2 = h2_bits(bits_h2(((x >> 8) & 0x000F000Fu) | kF16Magic2) - bias);
+  const uint32_t r3 = h2_bits(bits_h2(((x >> 12) & 0x000F000Fu) | kF16Magic2) - bias);
+  const u4 v = {r0, r1, r2, r3};
+  return __builtin_bit_cast(h8, v);
+}
+
+// Same, each code multiplied by the group code c (exact: |q*c| <= 2040 < 2048).
+__device__ __forceinline__ h8 unpack_q4_scaled(uint32_t w, _Float16 c) {
+  const uint32_t x = w ^ 0x88888888u;
+  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2 cc = {c, c};
+  const uint32_t r0 = h2_bits((bits_h2((x & 0x000F000Fu) | kF16Magic2) - bias) * cc);
+  const uint32_t r1 = h2_bits((bits_h2(((x >> 4) & 0x000F000Fu) | kF16Magic2) - bias) * cc);
+  const uint32_t r2 = h2_bits((bits_h2(((x >> 8) & 0x000F000Fu) | kF16Magic2) - bias) * cc);
+  const uint32_t r3 = h2_bits((bits_h2(((x >> 12) & 0x000F000Fu) | kF16Magic2) - bias) * cc);
+  const u4 v = {r0, r1, r2, r3};
+  return __builtin_bit_cast(h8, v);
+}
+
+// Eight INT8 codes (two dwords) -> eight exact fp16 values in k_order_z.
+// The XOR gives u = q + 128 in [0, 255]; 1024 + u - 1152 = q.
+__device__ __forceinline__ h8 unpack_i8x8(uint32_t lo, uint32_t hi) {
+  const uint32_t x0 = lo ^ 0x80808080u, x1 = hi ^ 0x80808080u;
+  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t r0 = h2_bits(bits_h2((x0 & 0x00FF00FFu) | kF16Magic2) - bias);
+  const uint32_t r1 = h2_bits(bits_h2(((x0 >> 8) & 0x00FF00FFu) | kF16Magic2) - bias);
+  const uint32_t r2 = h2_bits(bits_h2((x1 & 0x00FF00FFu) | kF16Magic2) - bias);
+  const uint32_t r3 = h2_bits(bits_h2(((x1 >> 8) & 0x00FF00FFu) | kF16Magic2) - bias);
+  const u4 v = {r0, r1, r2, r3};
+  return __builtin_bit_cast(h8, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Power-of-two exponent S that brings the largest magnitude m of a row into
+// [2^14, 2^15) (fp16 keeps every bf16 value of the row above 2^-17 * 2^(-S)
+// exact).  Rows that are all zero or not finite get S = 0.
+__device__ __forceinline__ int row_exponent(float maxabs) {
+  if (!(maxabs > 0.0f) || !(maxabs < __builtin_huge_valf())) return 0;
+  int e;
+  (void)frexpf(maxabs, &e);  // maxabs = m * 2^e, m in [0.5, 1)
+  return 15 - e;
+}
+
+__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace archead

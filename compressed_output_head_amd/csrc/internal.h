@@ -1,0 +1,64 @@
+// Internal declarations shared by the host library and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "archead.h"
+
+namespace archead {
+
+constexpr int kKTile = 128;        // columns per residual tile
+constexpr int kTileBytes = 1024;   // 16 rows x 128 columns of INT4
+constexpr int kMaxRank = 1024;     // per part (r_c, r_r)
+constexpr int kDecodeMaxTokens = 64;
+
+inline uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// Checks shared by every entry point.  Returns ARCHEAD_OK or an error.
+int check_dims(const archead_dims* d);
+// Additional limits of the kernels (rank a multiple of 8, g in {32,64,128,256}).
+int check_kernel_dims(const archead_dims* d);
+void compute_layout(const archead_dims* d, archead_layout* L);
+
+// Device workspace of one call (all offsets 256-byte aligned).
+struct WorkspaceLayout {
+  int64_t n16;          // tokens rounded up to 16
+  int rc32, rr32;       // ranks rounded up to 32
+  int zsteps;           // (rc32 + rr32) / 32
+  uint64_t hf, hscale, z32, zf, zscale, total;
+};
+WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens);
+
+// Everything a kernel needs, resolved to raw device pointers.
+struct FwdArgs {
+  // dims
+  int64_t V, D, N, n16, nb;   // nb = V16/16 row blocks
+  int r_c, r_r, g, ng, nkt, nks, rc32, rr32, zsteps, nA;
+  // input / output
+  const uint16_t* H;          // bf16 [N][H_stride]
+  int64_t H_stride;
+  void* Y;                    // fp32 or bf16 [N][Y_stride]
+  int64_t Y_stride;
+  int y_bf16;
+  // packed head sections
+  const uint8_t* r_codes;
+  const uint8_t* r_gcodes;
+  const uint16_t* r_rowscale;
+  const int8_t* a_codes;
+  const uint16_t* a_scales;
+  const int8_t* b_codes;
+  const uint16_t* b_scales;
+  // workspace
+  _Float16* hf;               // [n16/16][D/32][64][8] converted, scaled H
+  float* hscale;              // [n16]
+  float* z32;                 // [n16][r]
+  _Float16* zf;               // [n16/16][2*zsteps][64][8] hi/lo pre-projection
+  float* zscale;              // [n16]
+};
+
+hipError_t launch_prep(const FwdArgs& a, hipStream_t s);
+hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
+hipError_t launch_tile(const FwdArgs& a, hipStream_t s);
+
+}  // namespace archead

@@ -1,0 +1,165 @@
+// Pre-projection kernels.
+//
+// Algorithm 1 (inference step) evaluates the correction as (H B_w^T) A_w^T;
+// the quantised core A_c B_c is evaluated the same way.  These kernels form
+// Z = H [B_c_hat ; B_w_hat]^T once per call (r dot products of length D per
+// token, fp32), and convert H into the fp16 MFMA operand the forward kernels
+// stream:
+//   hf  : H * 2^S_n in fp16, S_n chosen per token so the row maximum lands in
+//         [2^14, 2^15); every bf16 value at most 2^31 below the row maximum is
+//         then exact in fp16.  hscale[n] = 2^-S_n undoes it in the epilogue.
+//   zf  : Z * 2^F_n split into fp16 hi + lo (22 significant bits), per-token
+//         exponent F_n chosen the same way; zscale[n] = 2^-F_n.
+// Both are stored in MFMA operand order (see device_common.h) so the forward
+// kernels read each 16x32 operand fragment as one contiguous 1 KB block.
+#include "device_common.h"
+#include "internal.h"
+
+namespace archead {
+
+namespace {
+
+constexpr int kPrepThreads = 256;
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// grid (n16, nJ): block (n, jc) converts token n (jc == 0) and computes
+// z32[n][4*jc + wave].
+__global__ __launch_bounds__(kPrepThreads) void prep_hz_kernel(const FwdArgs a) {
+  const int64_t n = blockIdx.x;
+  const int jc = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool real = n < a.N;
+  const uint16_t* hrow = a.H + (real ? n : 0) * a.H_stride;
+  const int nchunk = (int)(a.D / 8);
+
+  if (jc == 0) {
+    __shared__ float red[kPrepThreads / 64];
+    float m = 0.0f;
+    if (real) {
+      for (int c = tid; c < nchunk; c += kPrepThreads) {
+        const u4 raw = *reinterpret_cast<const u4*>(hrow + 8 * c);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] & 0xffffu))));
+          m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] >> 16))));
+        }
+      }
+    }
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int S = row_exponent(m);
+    if (tid == 0) a.hscale[n] = real ? ldexpf(1.0f, -S) : 0.0f;
+    const int64_t tile = n >> 4;
+    const int i = (int)(n & 15);
+    for (int c = tid; c < nchunk; c += kPrepThreads) {
+      const int64_t k0 = 8 * (int64_t)c;
+      const int64_t ks = k0 >> 5;
+      const int q = (int)((k0 >> 3) & 3);
+      float v[8];
+      if (real) {
+        const u4 raw = *reinterpret_cast<const u4*>(hrow + k0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          v[2 * w] = bf16_to_f32((uint16_t)(raw[w] & 0xffffu));
+          v[2 * w + 1] = bf16_to_f32((uint16_t)(raw[w] >> 16));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+      }
+      h8 out;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[j] = (_Float16)ldexpf(v[k_order_h(j)], S);
+      *reinterpret_cast<h8*>(a.hf + (((tile * a.nks + ks) * 64) + 16 * q + i) * 8) = out;
+    }
+  }
+
+  const int r = a.r_c + a.r_r;
+  const int j = 4 * jc + wave;
+  if (j >= r) return;
+  float acc = 0.0f;
+  if (real) {
+    const int8_t* brow = a.b_codes + (int64_t)j * a.D;
+    const uint16_t* srow = a.b_scales + (int64_t)j * a.ng;
+    for (int c = lane; c < nchunk; c += 64) {
+      const int64_t k0 = 8 * (int64_t)c;
+      const u4 hraw = *reinterpret_cast<const u4*>(hrow + k0);
+      const u2 braw = *reinterpret_cast<const u2*>(brow + k0);
+      float part = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t bw = braw[w >> 1] >> (16 * (w & 1));
+        const float b0 = (float)(int8_t)(bw & 0xff);
+        const float b1 = (float)(int8_t)((bw >> 8) & 0xff);
+        part = fmaf(bf16_to_f32((uint16_t)(hraw[w] & 0xffffu)), b0, part);
+        part = fmaf(bf16_to_f32((uint16_t)(hraw[w] >> 16)), b1, part);
+      }
+      acc = fmaf(f16_to_f32(srow[k0 / a.g]), part, acc);
+    }
+    acc = wave_sum(acc);
+  }
+  if (lane == 0) a.z32[n * r + j] = acc;
+}
+
+// grid (n16), one wave per token: per-token exponent of Z and its fp16 hi/lo
+// operand fragments (zero where the rank is padded to 32).
+__global__ __launch_bounds__(64) void prep_zf_kernel(const FwdArgs a) {
+  const int64_t n = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int r = a.r_c + a.r_r;
+  const bool real = n < a.N;
+  const float* zrow = a.z32 + n * r;
+  float m = 0.0f;
+  if (real)
+    for (int j = lane; j < r; j += 64) m = fmaxf(m, fabsf(zrow[j]));
+  m = wave_max(m);
+  const int F = row_exponent(m);
+  if (lane == 0) a.zscale[n] = real ? ldexpf(1.0f, -F) : 0.0f;
+  const int64_t tile = n >> 4;
+  const int i = (int)(n & 15);
+  const int csteps = a.rc32 / 32;
+  for (int e = lane; e < a.zsteps * 4; e += 64) {
+    const int s = e >> 2, q = e & 3;
+    const bool part_c = s < csteps;
+    const int sl = part_c ? s : s - csteps;
+    const int rank = part_c ? a.r_c : a.r_r;
+    const int base = part_c ? 0 : a.r_c;
+    h8 hi, lo;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int col = 32 * sl + 8 * q + k_order_z(jj);
+      float z = 0.0f;
+      if (real && col < rank) z = ldexpf(zrow[base + col], F);
+      const _Float16 zh = (_Float16)z;
+      hi[jj] = zh;
+      lo[jj] = (_Float16)(z - (float)zh);
+    }
+    _Float16* dst = a.zf + ((tile * (2 * a.zsteps) + 2 * s) * 64 + 16 * q + i) * 8;
+    *reinterpret_cast<h8*>(dst) = hi;
+    *reinterpret_cast<h8*>(dst + 64 * 8) = lo;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const FwdArgs& a, hipStream_t s) {
+  const int r = a.r_c + a.r_r;
+  const int nJ = r > 0 ? (r + 3) / 4 : 1;
+  hipLaunchKernelGGL(prep_hz_kernel, dim3((unsigned)a.n16, (unsigned)nJ), dim3(kPrepThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || r == 0) return e;
+  hipLaunchKernelGGL(prep_zf_kernel, dim3((unsigned)a.n16), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace archead

@@ -1,0 +1,192 @@
+/*
+ * archead.h -- C ABI of the packed ARCHead LM-head forward for AMD MI355X (gfx950).
+ *
+ * Method: "ARCHead: Activation-Metric Residual Correction for Large Language
+ * Model Output Heads" (arXiv:2608.02703).  The packed head stores
+ *   - an SC4 residual: signed INT4 codes with quantised group scales
+ *     (Sec. 3, quantized-core equation and the sentence after it),
+ *   - a low-rank core A_c B_c held as quantised factors (same equation),
+ *   - the activation-metric correction A_w (row-wise INT8) and B_w
+ *     (group-wise INT8) (Sec. 3, packed-variant paragraph; Algorithm 1),
+ * and inference evaluates  Y = H W_d^T + (H B_w^T) A_w^T  (Algorithm 1, last
+ * step), with W_d = Q(A_c) Q(B_c) + SC4(R).  This library computes exactly that
+ * forward from the packed bytes; it never forms the V x D matrix.
+ *
+ * Conventions for every entry point:
+ *   - All functions return an archead_status (0 = ARCHEAD_OK).  They never
+ *     abort, throw or print.  Arguments are checked on the host before any
+ *     HIP call; on a non-zero status nothing has been enqueued.
+ *   - The caller owns all memory.  The library allocates nothing on the
+ *     device and keeps no pointer after a call returns.
+ *   - Device pointers must stay valid until the stream has passed the work
+ *     enqueued by the call.  Calls on different streams need different
+ *     workspaces; the library holds no global state and is re-entrant.
+ */
+#ifndef ARCHEAD_H
+#define ARCHEAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ARCHEAD_API __attribute__((visibility("default")))
+#else
+#define ARCHEAD_API
+#endif
+
+#define ARCHEAD_FORMAT_VERSION 1
+#define ARCHEAD_ALIGNMENT 256
+
+typedef enum {
+  ARCHEAD_OK = 0,
+  ARCHEAD_E_NULL = 1,        /* a required pointer is NULL                        */
+  ARCHEAD_E_DIMS = 2,        /* dims are invalid (V<1, D not a multiple of 128, D % g != 0, rank < 0) */
+  ARCHEAD_E_UNSUPPORTED = 3, /* valid but not implemented (g not in {32,64,128,256}, rank not a multiple of 8,
+                                rank above 1024, forced decode path with more than 64 tokens) */
+  ARCHEAD_E_DTYPE = 4,       /* H is not bf16, or Y is neither fp32 nor bf16       */
+  ARCHEAD_E_SHAPE = 5,       /* H.cols != D, Y.cols != V, Y.rows != H.rows, bad strides */
+  ARCHEAD_E_ALIGN = 6,       /* buffer/workspace not 256-byte aligned, H rows not 16-byte aligned,
+                                Y not aligned to its element size                 */
+  ARCHEAD_E_WORKSPACE = 7,   /* workspace smaller than archead_workspace_bytes()   */
+  ARCHEAD_E_HIP = 8,         /* a kernel launch reported an error                  */
+  ARCHEAD_E_VALUE = 9,       /* archead_pack: an INT4 code outside [-8, 7]          */
+  ARCHEAD_E_SIZE = 10        /* packed buffer smaller than archead_layout.total_bytes */
+} archead_status;
+
+typedef enum { ARCHEAD_BF16 = 1, ARCHEAD_F32 = 2 } archead_dtype;
+
+typedef enum {
+  ARCHEAD_PATH_AUTO = 0,   /* N <= 64: decode path; N > 64: tile path            */
+  ARCHEAD_PATH_DECODE = 1, /* skinny path (streams the head once for all N <= 64 tokens) */
+  ARCHEAD_PATH_TILE = 2    /* LDS-tiled MFMA path (any N)                          */
+} archead_path;
+
+/* Shape of a packed head (Algorithm 1 inputs: vocabulary V, hidden size D,
+ * core rank r_c, correction rank r_r, group size g along D). */
+typedef struct {
+  int64_t V, D;
+  int32_t r_c, r_r, g;
+} archead_dims;
+
+typedef struct {
+  uint64_t offset, bytes;
+} archead_span;
+
+/* Where every stored tensor lives inside the one contiguous packed buffer
+ * (format version 1; each section starts on a 256-byte boundary):
+ *   header      64 B: u32 magic 0x48435241, u32 version, u64 V, u64 D,
+ *                     u32 r_c, u32 r_r, u32 g, u32 flags (0), 24 zero bytes
+ *   r_codes     SC4 codes in tiles of 16 rows x 128 columns (1024 B).  With
+ *               V16 = V rounded up to 16, tile (b, kt) of the (V16/16) x (D/128)
+ *               grid sits at (b*(D/128) + kt)*1024; its byte 16*l + 4*s + c
+ *               (l < 64, s < 4, c < 4) holds row 16*b + l%16 at columns
+ *               k = 128*kt + 32*s + 8*(l/16) + 2*c (low nibble) and k+1 (high
+ *               nibble), two's complement.  Rows >= V are zero.
+ *   r_gcodes    uint8 group codes: byte (b*(D/g) + t)*16 + i is row 16*b+i, group t.
+ *   r_rowscale  fp16 per-row residual scale s_R [V16].
+ *   a_codes     int8 [V16][r_c + r_r], row v = A_c[v,:] then A_w[v,:].
+ *   a_scales    fp16 [V16][n_A], n_A = (r_c>0) + (r_r>0): s_Ac[v] then s_Aw[v].
+ *   b_codes     int8 [r_c + r_r][D], rows B_c then B_w.
+ *   b_scales    fp16 [r_c + r_r][D/g], group scales of B_c then B_w.
+ * Dequantisation: R[v,k] = q4 * c8[v,k/g] * s_R[v];  A[v,j] = code * s_A(part)[v];
+ * B[j,k] = code * s_B[j,k/g].  W_hat = R + A_c B_c + A_w B_w.
+ * payload_bytes is the sum of numel x element size over the seven stored
+ * tensors (the persistent size of Sec. 3); total_bytes adds the header and
+ * alignment padding. */
+typedef struct {
+  uint32_t format_version, alignment;
+  uint64_t total_bytes, payload_bytes, header_bytes;
+  archead_span header, r_codes, r_gcodes, r_rowscale, a_codes, a_scales, b_codes, b_scales;
+  int64_t padded_rows; /* V16 */
+} archead_layout;
+
+/* Host-side components of one head, one code per element, row-major.  fp16
+ * values are passed as their uint16 bit patterns.  Pointers for a part of rank
+ * 0 may be NULL.
+ *   q4   [V][D]   int8 in [-8, 7]      c8   [V][D/g] uint8     s_R  [V] fp16
+ *   A_c  [V][r_c] int8   A_w [V][r_r] int8   s_Ac [V] fp16   s_Aw [V] fp16
+ *   B_c  [r_c][D] int8   B_w [r_r][D] int8   s_Bc [r_c][D/g] fp16   s_Bw [r_r][D/g] fp16 */
+typedef struct {
+  const int8_t* q4;
+  const uint8_t* c8;
+  const uint16_t* s_R;
+  const int8_t* A_c;
+  const int8_t* A_w;
+  const uint16_t* s_Ac;
+  const uint16_t* s_Aw;
+  const int8_t* B_c;
+  const int8_t* B_w;
+  const uint16_t* s_Bc;
+  const uint16_t* s_Bw;
+} archead_host_components;
+
+/* A 2-D device tensor: element (i, j) at data + (i*row_stride + j)*elem_size. */
+typedef struct {
+  void* data;
+  int64_t rows, cols, row_stride; /* row_stride in elements, >= cols */
+  int32_t dtype;                  /* archead_dtype */
+} archead_tensor;
+
+/* A packed head resident in device memory, plus the caller's device workspace. */
+typedef struct {
+  archead_dims dims;
+  const void* buffer;       /* device, 256-byte aligned, laid out per archead_pack_layout */
+  uint64_t buffer_bytes;    /* >= layout.total_bytes */
+  void* workspace;          /* device, 256-byte aligned scratch for one call */
+  uint64_t workspace_bytes; /* >= archead_workspace_bytes(dims, N) */
+} archead_packed_head;
+
+/* Layout of the packed buffer for `d`.  Pure host arithmetic: no allocation,
+ * no HIP call.  E_NULL, E_DIMS. */
+ARCHEAD_API int archead_pack_layout(const archead_dims* d, archead_layout* out);
+
+/* Device workspace one archead_logits call with n_tokens rows of H needs
+ * (converted hidden states, the low-rank pre-projection and per-token scales).
+ * Pure host arithmetic.  E_NULL, E_DIMS. */
+ARCHEAD_API int archead_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes);
+
+/* Serialise host components into `dst` (host memory, dst_bytes >=
+ * layout.total_bytes), writing every byte of the layout including padding.
+ * Host only; multithreaded.  E_NULL, E_DIMS, E_SIZE, E_VALUE. */
+ARCHEAD_API int archead_pack(const archead_dims* d, const archead_host_components* src, void* dst,
+                 uint64_t dst_bytes);
+
+/* Y = H W_hat^T  (Algorithm 1, inference step).
+ *   H: bf16 [N][D] device tensor; rows 16-byte aligned.
+ *   Y: fp32 or bf16 [N][V] device tensor, written completely (every element
+ *      once); bf16 output is rounded to nearest even from the fp32 result.
+ *   stream: a hipStream_t (NULL = the default stream).
+ * Enqueues the pre-projection kernels and then the decode path (N <= 64) or
+ * the tile path (N > 64) on `stream` and returns without synchronising.
+ * N = 0 is a no-op that returns ARCHEAD_OK.  Faults inside kernels surface at
+ * the caller's next synchronisation with the stream. */
+ARCHEAD_API int archead_logits(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y,
+                   void* stream);
+
+/* Same as archead_logits with the path chosen by the caller (archead_path).
+ * ARCHEAD_PATH_DECODE requires N <= 64.  Both paths compute the same Y. */
+ARCHEAD_API int archead_logits_path(const archead_tensor* H, const archead_packed_head* head,
+                        archead_tensor* Y, int path, void* stream);
+
+/* Same as archead_logits_path, and records the caller's events ev_begin and
+ * ev_end (hipEvent_t handles, either may be NULL) on `stream` immediately
+ * before and after the main kernel (decode or tile), after the pre-projection
+ * kernels.  For timing the dominant kernel on the stream it runs on. */
+ARCHEAD_API int archead_logits_events(const archead_tensor* H, const archead_packed_head* head,
+                                      archead_tensor* Y, int path, void* stream, void* ev_begin,
+                                      void* ev_end);
+
+/* Static string naming a status code. */
+ARCHEAD_API const char* archead_status_string(int status);
+
+/* ARCHEAD_FORMAT_VERSION the library was built for. */
+ARCHEAD_API int archead_format_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARCHEAD_H */

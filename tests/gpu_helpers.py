@@ -1,0 +1,66 @@
+"""Shared plumbing of the GPU tests: move seeded inputs to the device, run the
+library through its C ABI, and compare with the oracle."""
+import sys
+
+import numpy as np
+
+import oracle
+
+TOL = 2e-3  # max|Y_gpu - Y_ref| <= TOL * max|Y_ref|
+
+
+def torch_mod():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch
+
+
+def ah_mod():
+    import compressed_output_head_amd as ah
+    return ah
+
+
+def device_H(H_bits):
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(H_bits).view(np.int16)).view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def run(head_dev, H_bits, path=0, y_dtype="f32", H_dev=None, poison=True):
+    torch = torch_mod()
+    ah = ah_mod()
+    H = device_H(H_bits) if H_dev is None else H_dev
+    dt = torch.float32 if y_dtype == "f32" else torch.bfloat16
+    Y = torch.empty((H.shape[0], head_dev.V), dtype=dt, device="cuda")
+    if poison:
+        Y.fill_(float("nan"))
+    ah.archead_logits_path(H, head_dev, Y, path)
+    torch.cuda.synchronize()
+    return Y
+
+
+def to_f64(Y):
+    torch = torch_mod()
+    return Y.float().cpu().numpy().astype(np.float64) if Y.dtype == torch.bfloat16 else \
+        Y.cpu().numpy().astype(np.float64)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_parity(Yg, Yr, what=""):
+    """Tolerance, no unwritten element, identical per-row argmax."""
+    assert not np.isnan(Yg).any(), f"{what}: unwritten (NaN) outputs"
+    scale = np.abs(Yr).max()
+    err = np.abs(Yg - Yr).max()
+    rel = err / scale if scale > 0 else err
+    log(f"  {what}: max|dY|/max|Y| = {rel:.3e}")
+    assert rel <= TOL, f"{what}: {rel:.3e} > {TOL}"
+    ag, ar = np.argmax(Yg, 1), oracle.row_argmax(Yr)
+    bad = np.flatnonzero(ag != ar)
+    if bad.size:
+        gaps = oracle.top2_gap(Yr[bad])
+        raise AssertionError(f"{what}: argmax differs on rows {bad[:8]} (oracle top-2 gaps {gaps[:8]})")
+    return rel

@@ -1,0 +1,190 @@
+"""The C-ABI library on the host: exports, layout, packer and argument checks.
+
+No test here launches a kernel: each call either is pure host work or fails
+validation before the first HIP call, so the file runs without a GPU.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.conftest import ROOT
+
+
+@pytest.fixture(scope="module")
+def ah():
+    lib_path = os.path.join(ROOT, "compressed_output_head_amd", "libarchead.so")
+    if not os.path.exists(lib_path):
+        import runpy
+        runpy.run_path(os.path.join(ROOT, "compressed_output_head_amd", "build.py"))["build"]()
+    import compressed_output_head_amd as m
+    return m
+
+
+def test_exports_match_header(ah):
+    hdr = open(os.path.join(ROOT, "include", "archead.h")).read()
+    declared = set(re.findall(r"ARCHEAD_API\s+[\w\s\*]*?\b(archead_\w+)\s*\(", hdr))
+    assert declared == set(ah.EXPORTS)
+    for name in declared:
+        assert hasattr(ah.lib, name), name
+    assert ah.archead_format_version() == oracle.FORMAT_VERSION
+
+
+DIMS = [(1024, 256, 16, 8, 64), (151936, 4096, 32, 32, 128), (151936, 4096, 64, 64, 128),
+        (128256, 8192, 64, 64, 128), (20, 256, 8, 8, 64), (1, 128, 0, 0, 32), (37, 384, 0, 24, 2),
+        (1000, 512, 6, 6, 128)]
+
+
+@pytest.mark.parametrize("dims", DIMS)
+def test_layout_matches_oracle(ah, dims):
+    a = ah.archead_pack_layout(*dims)
+    b = oracle.layout(*dims)
+    for n in ["header", "r_codes", "r_gcodes", "r_rowscale", "a_codes", "a_scales", "b_codes", "b_scales"]:
+        assert tuple(a[n]) == tuple(b[n]), n
+    assert a["total_bytes"] == b["total_bytes"] and a["payload_bytes"] == b["payload_bytes"]
+    assert a["V16"] == b["V16"] and a["alignment"] == 256
+
+
+@pytest.mark.parametrize("V,D,r_c,r_r,g", [(1024, 256, 16, 8, 64), (37, 128, 0, 0, 128), (50, 512, 0, 24, 32),
+                                           (16, 256, 40, 0, 256), (129, 384, 8, 8, 64), (3, 256, 6, 2, 8)])
+def test_library_packer_matches_oracle_packer(ah, V, D, r_c, r_r, g):
+    h = synth.draw_head(np.random.default_rng(V * 7 + D), V, D, r_c, r_r, g)
+    assert np.array_equal(ah.archead_pack(h), oracle.pack(h))
+
+
+def test_library_packer_golden_positions(ah, golden_dir):
+    G = json.load(open(os.path.join(golden_dir, "format_v1_cases.json")))
+    d = G["dims"]
+    h = synth.zero_head(d["V"], d["D"], d["r_c"], d["r_r"], d["g"])
+    for c in G["nibbles"]:
+        h.q4[c["v"], c["k"]] = c["code"]
+    buf = ah.archead_pack(h)
+    for c in G["nibbles"]:
+        byte = int(buf[c["byte"]])
+        nib = byte & 0xF if c["half"] == "lo" else byte >> 4
+        assert nib == c["code"] & 0xF, c
+
+
+def test_pack_rejects_bad_codes_and_small_buffers(ah):
+    h = synth.draw_head(np.random.default_rng(1), 32, 128, 8, 8, 32)
+    h.q4[3, 5] = 8
+    with pytest.raises(ah.ArcheadError) as e:
+        ah.archead_pack(h)
+    assert e.value.status == 9
+    h.q4[3, 5] = -9
+    with pytest.raises(ah.ArcheadError):
+        ah.archead_pack(h)
+    h.q4[3, 5] = 0
+    d = ah.ArcheadDims(32, 128, 8, 8, 32)
+    comp = ah.ArcheadHostComponents()
+    arrs = {}
+    for n in ("q4", "c8", "s_R", "A_c", "A_w", "s_Ac", "s_Aw", "B_c", "B_w", "s_Bc", "s_Bw"):
+        arrs[n] = np.ascontiguousarray(getattr(h, n))
+        setattr(comp, n, arrs[n].ctypes.data)
+    total = ah.archead_pack_layout(32, 128, 8, 8, 32)["total_bytes"]
+    out = np.zeros(total, np.uint8)
+    assert ah.lib.archead_pack(ctypes.byref(d), ctypes.byref(comp), out.ctypes.data, total - 1) == 10
+    assert ah.lib.archead_pack(ctypes.byref(d), ctypes.byref(comp), None, total) == 1
+    comp.A_w = None
+    assert ah.lib.archead_pack(ctypes.byref(d), ctypes.byref(comp), out.ctypes.data, total) == 1
+
+
+def test_layout_dims_errors(ah):
+    L = ah.ArcheadLayout()
+    for dims, want in [((0, 256, 0, 0, 64), 2), ((16, 200, 0, 0, 8), 2), ((16, 256, 0, 0, 3), 2),
+                       ((16, 256, -1, 0, 64), 2), ((16, 256, 0, 0, 96), 2), ((1 << 32, 256, 0, 0, 64), 3)]:
+        assert ah.lib.archead_pack_layout(ctypes.byref(ah.ArcheadDims(*dims)), ctypes.byref(L)) == want, dims
+    assert ah.lib.archead_pack_layout(None, ctypes.byref(L)) == 1
+    assert ah.lib.archead_pack_layout(ctypes.byref(ah.ArcheadDims(16, 256, 0, 0, 64)), None) == 1
+
+
+def test_workspace_bytes(ah):
+    # hf (N16*D*2) | hscale (N16*4) | z32 (N16*r*4) | zf (N16*2*(rc32+rr32)*2) | zscale, 256-aligned
+    up = lambda x: (x + 255) // 256 * 256
+    for (V, D, r_c, r_r, g), N in [((1024, 256, 16, 8, 64), 4), ((151936, 4096, 32, 32, 128), 1),
+                                   ((151936, 4096, 64, 64, 128), 4096), ((64, 128, 0, 0, 32), 17)]:
+        n16 = (N + 15) // 16 * 16
+        rc32, rr32 = (r_c + 31) // 32 * 32, (r_r + 31) // 32 * 32
+        want = (up(n16 * D * 2) + up(n16 * 4) + up(n16 * (r_c + r_r) * 4) +
+                up(n16 * 2 * (rc32 + rr32) * 2) + up(n16 * 4))
+        assert ah.archead_workspace_bytes(V, D, r_c, r_r, g, N) == want
+    assert ah.archead_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
+
+
+# ------------------------------------------------ argument checks of logits ---
+
+FAKE = 1 << 40  # never dereferenced: every call below fails validation first
+
+
+def _args(ah, N=4, V=1024, D=256, r_c=16, r_r=8, g=64, ydt=2, hdt=1, ws=None, buf=None):
+    try:
+        total = ah.archead_pack_layout(V, D, r_c, r_r, g)["total_bytes"]
+        need = ah.archead_workspace_bytes(V, D, r_c, r_r, g, N)
+    except ah.ArcheadError:
+        total = need = 1 << 20
+    H = ah.ArcheadTensor(FAKE, N, D, D, hdt)
+    Y = ah.ArcheadTensor(FAKE + (1 << 30), N, V, V, ydt)
+    P = ah.ArcheadPackedHead(ah.ArcheadDims(V, D, r_c, r_r, g), FAKE + (2 << 30),
+                             total if buf is None else buf, FAKE + (3 << 30), need if ws is None else ws)
+    return H, P, Y, need, total
+
+
+def _call(ah, H, P, Y, path=0):
+    return ah.lib.archead_logits_path(ctypes.byref(H), ctypes.byref(P), ctypes.byref(Y), path, None)
+
+
+def test_logits_error_paths(ah):
+    H, P, Y, need, total = _args(ah)
+    assert ah.lib.archead_logits(None, ctypes.byref(P), ctypes.byref(Y), None) == 1
+    assert ah.lib.archead_logits(ctypes.byref(H), None, ctypes.byref(Y), None) == 1
+    assert ah.lib.archead_logits(ctypes.byref(H), ctypes.byref(P), None, None) == 1
+
+    cases = []
+    H, P, Y, need, total = _args(ah, hdt=2); cases.append((H, P, Y, 0, 4))            # H not bf16
+    H, P, Y, need, total = _args(ah, ydt=3); cases.append((H, P, Y, 0, 4))            # Y dtype
+    H, P, Y, need, total = _args(ah); H.cols = 255; cases.append((H, P, Y, 0, 5))      # D mismatch
+    H, P, Y, need, total = _args(ah); Y.cols = 1000; cases.append((H, P, Y, 0, 5))     # V mismatch
+    H, P, Y, need, total = _args(ah); Y.rows = 5; cases.append((H, P, Y, 0, 5))        # N mismatch
+    H, P, Y, need, total = _args(ah); H.row_stride = 100; cases.append((H, P, Y, 0, 5))
+    H, P, Y, need, total = _args(ah); H.rows = Y.rows = -1; cases.append((H, P, Y, 0, 5))
+    H, P, Y, need, total = _args(ah, g=16); cases.append((H, P, Y, 0, 3))             # g unsupported
+    H, P, Y, need, total = _args(ah, r_c=12); cases.append((H, P, Y, 0, 3))           # rank % 8
+    H, P, Y, need, total = _args(ah, r_r=2048); cases.append((H, P, Y, 0, 3))         # rank cap
+    H, P, Y, need, total = _args(ah, V=0); cases.append((H, P, Y, 0, 2))
+    H, P, Y, need, total = _args(ah); cases.append((H, P, Y, 7, 3))                    # bad path
+    H, P, Y, need, total = _args(ah, N=65); cases.append((H, P, Y, 1, 3))             # decode > 64
+    H, P, Y, need, total = _args(ah); H.data = None; cases.append((H, P, Y, 0, 1))
+    H, P, Y, need, total = _args(ah); P.workspace = None; cases.append((H, P, Y, 0, 1))
+    H, P, Y, need, total = _args(ah); P.buffer = FAKE + 16; cases.append((H, P, Y, 0, 6))
+    H, P, Y, need, total = _args(ah); P.workspace = FAKE + 128; cases.append((H, P, Y, 0, 6))
+    H, P, Y, need, total = _args(ah); H.data = FAKE + 2; cases.append((H, P, Y, 0, 6))
+    H, P, Y, need, total = _args(ah); H.row_stride = 260; cases.append((H, P, Y, 0, 6))  # 520-byte rows
+    H, P, Y, need, total = _args(ah); Y.data = FAKE + 2; cases.append((H, P, Y, 0, 6))   # fp32 Y at 2 mod 4
+    H, P, Y, need, total = _args(ah, buf=100); cases.append((H, P, Y, 0, 10))
+    H, P, Y, need, total = _args(ah, ws=1); cases.append((H, P, Y, 0, 7))
+    H, P, Y, need, total = _args(ah, N=4096, V=151936, D=4096, r_c=64, r_r=64, g=128, ydt=1, ws=12345)
+    cases.append((H, P, Y, 2, 7))
+    for i, (H, P, Y, path, want) in enumerate(cases):
+        assert _call(ah, H, P, Y, path) == want, i
+
+
+def test_logits_zero_tokens_is_a_noop(ah):
+    H, P, Y, need, total = _args(ah, N=0)
+    H.data = Y.data = None
+    P.workspace = None
+    assert _call(ah, H, P, Y, 0) == 0
+    assert _call(ah, H, P, Y, 1) == 0
+    assert _call(ah, H, P, Y, 2) == 0
+
+
+def test_status_strings(ah):
+    for code in range(11):
+        s = ah.archead_status_string(code)
+        assert s.startswith("ARCHEAD_")
+        assert ah.STATUS[code] in s
+    assert "unknown" in ah.archead_status_string(99)
