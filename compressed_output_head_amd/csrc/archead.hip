@@ -64,7 +64,6 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens) {
   w.rr32 = (int)round_up((uint64_t)d->r_r, 32);
   w.zsteps = (w.rc32 + w.rr32) / 32;
   const uint64_t n16 = (uint64_t)w.n16, D = (uint64_t)d->D;
-  const uint64_t r = (uint64_t)d->r_c + (uint64_t)d->r_r;
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) {
     const uint64_t at = off;
@@ -73,9 +72,11 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens) {
   };
   w.hf = take(n16 * D * 2);
   w.hscale = take(n16 * 4);
-  w.z32 = take(n16 * r * 4);
   w.zf = take(n16 * (uint64_t)w.zsteps * 2 * 32 * 2);
   w.zscale = take(n16 * 4);
+  const uint64_t nsmall = n_tokens <= kDecodeLdsTokens ? (uint64_t)std::max<int64_t>(n_tokens, 0) : 0;
+  w.z32 = take(nsmall * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
+  w.hc = take(nsmall * D * 2);
   w.total = n16 ? off : 0;
   return w;
 }
@@ -184,8 +185,9 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
     memcpy(out + 8, u64, 16);
     memcpy(out + 24, u32b, 16);
   }
-  // residual tiles: byte 16*l + 4*s + c of tile (b, kt) holds row 16b + l%16,
-  // columns k = 128kt + 32s + 8(l/16) + 2c (low nibble) and k + 1 (high nibble)
+  // residual tiles, k-tile major: tile (b, kt) at (kt*nb + b)*1024; its byte
+  // 16*l + 4*s + c holds row 16b + l%16, columns k = 128kt + 32s + 8(l/16) + 2c
+  // (low nibble) and k + 1 (high nibble)
   uint8_t* rcodes = out + L.r_codes.offset;
   uint8_t* gcodes = out + L.r_gcodes.offset;
   parallel_for(nb, [&](int64_t b0, int64_t b1) {
@@ -195,7 +197,7 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
         if (v >= V) break;
         const int8_t* row = src->q4 + v * D;
         for (int64_t kt = 0; kt < nkt; ++kt) {
-          uint8_t* tile = rcodes + (b * nkt + kt) * kTileBytes;
+          uint8_t* tile = rcodes + (kt * nb + b) * kTileBytes;
           for (int qq = 0; qq < 4; ++qq)
             for (int s = 0; s < 4; ++s)
               for (int c = 0; c < 4; ++c) {
@@ -204,7 +206,7 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
                 tile[16 * (16 * qq + i) + 4 * s + c] = (uint8_t)(lo | (hi << 4));
               }
         }
-        for (int64_t t = 0; t < ng; ++t) gcodes[(b * ng + t) * 16 + i] = src->c8[v * ng + t];
+        memcpy(gcodes + v * ng, src->c8 + v * ng, (size_t)ng);
       }
     }
   });
@@ -289,16 +291,18 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   a.b_scales = reinterpret_cast<const uint16_t*>(buf + L.b_scales.offset);
   a.hf = reinterpret_cast<_Float16*>(ws + W.hf);
   a.hscale = reinterpret_cast<float*>(ws + W.hscale);
-  a.z32 = reinterpret_cast<float*>(ws + W.z32);
   a.zf = reinterpret_cast<_Float16*>(ws + W.zf);
   a.zscale = reinterpret_cast<float*>(ws + W.zscale);
+  a.z32 = reinterpret_cast<float*>(ws + W.z32);
+  a.hc = reinterpret_cast<_Float16*>(ws + W.hc);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
-  if (launch_prep(a, s) != hipSuccess) return ARCHEAD_E_HIP;
-  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return ARCHEAD_E_HIP;
   const bool decode = path == ARCHEAD_PATH_DECODE || (path == ARCHEAD_PATH_AUTO && N <= kDecodeMaxTokens);
-  const hipError_t e = decode ? launch_decode(a, s) : launch_tile(a, s);
+  const bool small = decode && decode_lds_eligible(a);
+  if ((small ? launch_prep_z(a, s) : launch_prep(a, s)) != hipSuccess) return ARCHEAD_E_HIP;
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return ARCHEAD_E_HIP;
+  const hipError_t e = small ? launch_decode_lds(a, s) : decode ? launch_decode(a, s) : launch_tile(a, s);
   if (e != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
   return ARCHEAD_OK;

@@ -15,6 +15,8 @@
 // applied in the epilogue.  The low-rank term is (Z * A^T) with Z split into
 // fp16 hi/lo and the INT8 A codes as exact fp16 integers, one accumulator per
 // part (c, w) so each part gets its own row scale.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -45,14 +47,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const FwdArgs a)
 
   const int ntiles = (int)(a.n16 >> 4);
   const int steps_per_group = a.g / 32;
-  const u4* wbase = reinterpret_cast<const u4*>(a.r_codes) + (blk0 * a.nkt) * 64 + lane;
+  const u4* wbase = reinterpret_cast<const u4*>(a.r_codes) + blk0 * 64 + lane;
   const h8* hbase = reinterpret_cast<const h8*>(a.hf) + lane;
 
   for (int kt = 0; kt < a.nkt; ++kt) {
     u4 w[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b)
-      w[b] = (b < nblk) ? __builtin_nontemporal_load(wbase + ((int64_t)b * a.nkt + kt) * 64)
+      w[b] = (b < nblk) ? __builtin_nontemporal_load(wbase + ((int64_t)kt * a.nb + b) * 64)
                         : u4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const FwdArgs a)
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
           const float c = (b < nblk)
-              ? (float)a.r_gcodes[((blk0 + b) * a.ng + grp) * 16 + i16] : 0.0f;
+              ? (float)a.r_gcodes[((blk0 + b) * 16 + i16) * a.ng + grp] : 0.0f;
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             acc[b][t] += c * part[b][t];
@@ -144,6 +146,282 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const FwdArgs a)
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// Small-N decode (N <= 16 and all of H plus Z fit in LDS), persistent.
+//
+// The grid holds only co-resident workgroups (at most kLdsWgPerCu per CU).
+// Every wave walks a grid-strided list of 16-row blocks (b, b + W, b + 2W, ...
+// with W the number of waves), so at any moment neighbouring waves read
+// neighbouring 1 KB tiles of the same k-tile plane.  Each wave keeps a ring of
+// P packed tiles in flight in registers, plus one vector of group codes per
+// chunk of 4 tiles (the lane's row codes for 512 columns, one small load).  The
+// ring runs across block boundaries, so a wave never drains its pipeline.  H
+// (already scaled fp16 from the pre-projection kernel) and Z (fp32) sit in
+// LDS; LDS reads use the separate lgkm counter and never wait behind the ring.
+// Only lanes that carry a real token read H; the other MFMA rows are zero.
+constexpr int kLdsWaves = 4;
+constexpr int kLdsThreads = 64 * kLdsWaves;
+#ifndef ARCHEAD_DECODE_WG_PER_CU
+#define ARCHEAD_DECODE_WG_PER_CU 4
+#endif
+constexpr int kLdsWgPerCu = ARCHEAD_DECODE_WG_PER_CU;
+constexpr int kEpiSteps = 2;  // low-rank 32-column steps whose A codes are prefetched
+
+// The lane's group codes for one chunk of 4 tiles (512 columns): 512/g bytes.
+template <int G> struct CodeVec;
+template <> struct CodeVec<256> { typedef uint16_t T; };
+template <> struct CodeVec<128> { typedef uint32_t T; };
+template <> struct CodeVec<64> { typedef u2 T; };
+template <> struct CodeVec<32> { typedef u4 T; };
+
+template <int G>
+__device__ __forceinline__ float code_at(const typename CodeVec<G>::T& v, int idx) {
+  if constexpr (G == 256 || G == 128) {
+    return (float)((((uint32_t)v) >> (8 * idx)) & 0xffu);
+  } else {
+    return (float)((v[idx >> 2] >> (8 * (idx & 3))) & 0xffu);
+  }
+}
+
+// LDS carve-up of the small-N kernel: H as fp16 [N][D + 8] (8 halves of
+// padding per row spread the rows over the banks), then Z as fp32 [N][r].
+__host__ __device__ inline size_t lds_h_bytes(int64_t N, int64_t D) { return (size_t)N * (D + 8) * 2; }
+__host__ __device__ inline size_t lds_bytes(int64_t N, int64_t D, int r) {
+  return lds_h_bytes(N, D) + (size_t)N * r * 4;
+}
+
+template <int P, int G>
+__global__ __launch_bounds__(kLdsThreads) void decode_lds_kernel(const FwdArgs a) {
+  static_assert(P % 4 == 0, "the ring holds whole 4-tile code chunks");
+  using CV = typename CodeVec<G>::T;
+  constexpr int NC = P / 4;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ float s_hs[kDecodeLdsTokens];
+  __shared__ int s_F[kDecodeLdsTokens];
+  _Float16* sH = reinterpret_cast<_Float16*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = (int)a.N;
+  const int D = (int)a.D;
+  const int ldh = D + 8;
+  const int r = a.r_c + a.r_r;
+  float* sZ = reinterpret_cast<float*>(smem + lds_h_bytes(N, D));
+  const int i16 = lane & 15, q = lane >> 4;
+  const int nkt = a.nkt;
+  const int ng = a.ng;
+  const int64_t nb = a.nb;
+  const int64_t nwaves = (int64_t)gridDim.x * kLdsWaves;
+  const int csteps = a.rc32 / 32, wsteps = a.rr32 / 32;
+  const int esteps = csteps + wsteps;
+
+  // residual tiles are k-tile major: tile kt of block b at (kt*nb + b)*1024
+  // bytes; group codes are row-major [V16][ng].  32-bit byte offsets from the
+  // section bases (the host checks both sections are below 4 GiB).
+  const uint32_t tstride = (uint32_t)nb * 1024u;
+  const unsigned char* wbase = a.r_codes;
+  const unsigned char* cbase = a.r_gcodes;
+  auto tile_at = [&](int64_t blk, int kt) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u4*>(
+        wbase + ((uint32_t)blk * 1024u + (uint32_t)kt * tstride + (uint32_t)lane * 16u)));
+  };
+  auto codes_at = [&](int64_t blk, int kt4) {  // codes of tiles kt4..kt4+3 for this lane's row
+    return *reinterpret_cast<const CV*>(
+        cbase + ((uint32_t)(blk * 16 + i16) * (uint32_t)ng + (uint32_t)(kt4 * 128 / G)));
+  };
+
+  int64_t b = (int64_t)blockIdx.x * kLdsWaves + wave;
+  const int64_t b0 = b < nb ? b : nb - 1;  // waves without work load a valid block, store nothing
+
+  // the weight stream does not depend on H: start it before staging H and Z
+  u4 wr[P];
+  CV cv[NC];
+#pragma unroll
+  for (int j = 0; j < P; ++j) wr[j] = tile_at(b0, j);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) cv[c] = codes_at(b0, 4 * c);
+
+  // prologue: H rows (scaled fp16), Z rows and per-token scales into LDS
+  const int per_row = D / 8;
+  for (int c = tid; c < N * per_row; c += kLdsThreads) {
+    const int n = c / per_row, k8 = c - n * per_row;
+    *reinterpret_cast<u4*>(sH + n * ldh + 8 * k8) =
+        *reinterpret_cast<const u4*>(a.hc + (int64_t)n * D + 8 * k8);
+  }
+  for (int c = tid; c < N * r; c += kLdsThreads) sZ[c] = a.z32[c];
+  for (int n = wave; n < N; n += kLdsWaves) {
+    float m = 0.0f;
+    for (int j = lane; j < r; j += 64) m = fmaxf(m, fabsf(a.z32[n * r + j]));
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) {
+      s_F[n] = row_exponent(m);
+      s_hs[n] = a.hscale[n];
+    }
+  }
+  __syncthreads();
+  if (b >= nb) return;
+
+  const bool real = i16 < N;
+  const _Float16* hrow = sH + (real ? i16 : 0) * ldh + 8 * q;
+  const int F = real ? s_F[i16] : 0;
+
+  for (; b < nb; b += nwaves) {
+    const int64_t bn = b + nwaves < nb ? b + nwaves : b;  // the ring's next block (or a harmless re-read)
+    const int64_t v = 16 * b + i16;
+    // epilogue operands of this block, loaded now so they arrive long before use
+    const uint16_t sRb = a.r_rowscale[v];
+    const uint16_t sAcb = a.r_c > 0 ? a.a_scales[v * a.nA] : (uint16_t)0;
+    const uint16_t sAwb = a.r_r > 0 ? a.a_scales[v * a.nA + a.nA - 1] : (uint16_t)0;
+    const int8_t* arow = a.a_codes + v * r;
+    u2 araw[kEpiSteps];
+#pragma unroll
+    for (int s = 0; s < kEpiSteps; ++s) {
+      araw[s] = u2{0u, 0u};
+      const bool part_c = s < csteps;
+      const int col = 32 * (part_c ? s : s - csteps) + 8 * q;
+      const int rank = part_c ? a.r_c : a.r_r;
+      if (s < esteps && col < rank) araw[s] = *reinterpret_cast<const u2*>(arow + (part_c ? 0 : a.r_c) + col);
+    }
+
+    f4 acc = {0.f, 0.f, 0.f, 0.f}, part = {0.f, 0.f, 0.f, 0.f};
+    for (int kt0 = 0; kt0 < nkt; kt0 += P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        // keep the scheduler from hoisting work of later ring slots
+        __builtin_amdgcn_sched_barrier(0);
+        const int kt = kt0 + j;
+        float c[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) c[s] = code_at<G>(cv[j / 4], (128 * (j & 3) + 32 * s) / G);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          h8 hv = h8{0, 0, 0, 0, 0, 0, 0, 0};
+          if (real) hv = *reinterpret_cast<const h8*>(hrow + 32 * (4 * kt + s));
+          part = mfma16(hv, unpack_q4(wr[j][s]), part);
+          // a group of g columns ends after this 32-column step
+          const bool flush = ((128 * (j & 3) + 32 * (s + 1)) % G) == 0;
+          if (flush) {
+            acc += c[s] * part;
+            part = f4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+        {
+          // refill the slot with the tile P positions ahead in this wave's sequence
+          const bool same = kt + P < nkt;
+          wr[j] = tile_at(same ? b : bn, same ? kt + P : kt + P - nkt);
+          if ((j & 3) == 3) {
+            const int k4 = kt - 3 + P;  // first tile of the chunk this code slot serves next
+            cv[j / 4] = codes_at(k4 < nkt ? b : bn, k4 < nkt ? k4 : k4 - nkt);
+          }
+        }
+      }
+    }
+
+    // epilogue: row scale, low-rank term (Z hi/lo from LDS against exact INT8
+    // A codes, one accumulator per part), store
+    f4 pc = {0.f, 0.f, 0.f, 0.f}, pw = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < esteps; ++s) {
+      const bool part_c = s < csteps;
+      const int col = 32 * (part_c ? s : s - csteps) + 8 * q;
+      const int rank = part_c ? a.r_c : a.r_r;
+      const int base = part_c ? 0 : a.r_c;
+      u2 raw = {0u, 0u};
+      if (s < kEpiSteps) {
+#pragma unroll
+        for (int t = 0; t < kEpiSteps; ++t)
+          if (t == s) raw = araw[t];
+      } else if (col < rank) {
+        raw = *reinterpret_cast<const u2*>(arow + base + col);
+      }
+      const h8 av = unpack_i8x8(raw[0], raw[1]);
+      h8 zh, zl;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int cc = col + k_order_z(jj);
+        const float z = (real && cc < rank) ? ldexpf(sZ[i16 * r + base + cc], F) : 0.0f;
+        zh[jj] = (_Float16)z;
+        zl[jj] = (_Float16)(z - (float)zh[jj]);
+      }
+      if (part_c) {
+        pc = mfma16(zh, av, pc);
+        pc = mfma16(zl, av, pc);
+      } else {
+        pw = mfma16(zh, av, pw);
+        pw = mfma16(zl, av, pw);
+      }
+    }
+    if (v < a.V) {
+      const float sR = f16_to_f32(sRb), sAc = f16_to_f32(sAcb), sAw = f16_to_f32(sAwb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = 4 * q + e;
+        if (n >= N) continue;
+        float y = s_hs[n] * (sR * acc[e]);
+        if (r > 0) y = fmaf(ldexpf(1.0f, -s_F[n]), fmaf(sAw, pw[e], sAc * pc[e]), y);
+        if (a.y_bf16)
+          reinterpret_cast<uint16_t*>(a.Y)[n * a.Y_stride + v] = f32_to_bf16(y);
+        else
+          reinterpret_cast<float*>(a.Y)[n * a.Y_stride + v] = y;
+      }
+    }
+  }
+}
+
+#ifndef ARCHEAD_RING_DEPTH
+#define ARCHEAD_RING_DEPTH 4
+#endif
+constexpr int kRingDepth = ARCHEAD_RING_DEPTH;  // largest packed-tile ring per wave
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int P, int G>
+hipError_t launch_lds_p(const FwdArgs& a, hipStream_t s) {
+  const size_t lds = lds_bytes(a.N, a.D, a.r_c + a.r_r);
+  // persistent grid: never more workgroups than can be resident at once
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_lds_kernel<P, G>, kLdsThreads, lds) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  per_cu = std::min(per_cu, kLdsWgPerCu);
+  const int64_t need = (a.nb + kLdsWaves - 1) / kLdsWaves;
+  const int64_t grid = std::min<int64_t>(need, (int64_t)device_cu_count() * per_cu);
+  hipLaunchKernelGGL((decode_lds_kernel<P, G>), dim3((unsigned)grid), dim3(kLdsThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_lds(const FwdArgs& a, hipStream_t s) {
+  if (kRingDepth >= 8 && a.nkt % 8 == 0) return launch_lds_p<(kRingDepth >= 8 ? 8 : 4), G>(a, s);
+  return launch_lds_p<4, G>(a, s);
+}
+
+}  // namespace
+
+bool decode_lds_eligible(const FwdArgs& a) {
+  const uint64_t rbytes = (uint64_t)a.nb * 16 * (uint64_t)a.D / 2;  // 32-bit section offsets
+  return a.N >= 1 && a.N <= kDecodeLdsTokens && a.nkt % 4 == 0 &&
+         lds_bytes(a.N, a.D, a.r_c + a.r_r) <= kDecodeLdsBytes && rbytes < (1ull << 32);
+}
+
+hipError_t launch_decode_lds(const FwdArgs& a, hipStream_t s) {
+  switch (a.g) {
+    case 32: return launch_lds<32>(a, s);
+    case 64: return launch_lds<64>(a, s);
+    case 128: return launch_lds<128>(a, s);
+    default: return launch_lds<256>(a, s);
+  }
+}
+
+namespace {
 
 template <int NT, int RB>
 hipError_t launch_nt(const FwdArgs& a, hipStream_t s) {

@@ -14,9 +14,10 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // Kernel k-order inside one 8-column run of an MFMA operand.  Operand slot j
-// (0..7) of a lane carries column kOrderH[j] of the run for H and the residual
-// codes, and column kOrderZ[j] for the pre-projection and the A codes.  Both
-// operands of every MFMA use the same order, so the dot product is unchanged.
+// (0..7) of a lane carries column k_order_h(j) of the run for H and the
+// residual codes, and column k_order_z(j) for the pre-projection and the A
+// codes.  Both operands of every MFMA use the same order, so the dot product
+// is unchanged.
 //   residual dword bytes (k0k1)(k2k3)(k4k5)(k6k7) unpack to slots k0 k4 k1 k5 k2 k6 k3 k7
 //   A-code dwords (j0 j1 j2 j3)(j4 j5 j6 j7) unpack to slots j0 j2 j1 j3 j4 j6 j5 j7
 __host__ __device__ constexpr int k_order_h(int j) { return (j >> 1) + 4 * (j & 1); }
@@ -27,35 +28,43 @@ __host__ __device__ constexpr int k_order_z(int j) {
 __device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 bits_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
-// 0x6400 is fp16 1024.0, whose ulp is 1: OR-ing an unsigned value u < 1024
-// into the low mantissa bits gives exactly 1024 + u.
+// 0x6400 is fp16 1024.0, whose ulp is 1: placing an unsigned value u < 1024
+// in the low mantissa bits gives exactly 1024 + u; placing a nibble u in bits
+// 4..7 gives exactly 1024 + 16u.
 constexpr uint32_t kF16Magic2 = 0x64006400u;
 
+// Two pairs of nibbles of one dword as fp16 pairs: lo nibbles of bytes 0 and 2
+// give (1024 + u0, 1024 + u2'), hi nibbles give (1024 + 16 u1, 1024 + 16 u3'),
+// where u = code + 8 (the XOR with 8 per nibble maps two's complement [-8, 7]
+// to offset binary).  Each expression compiles to one v_bitop3_b32.
+__device__ __forceinline__ uint32_t nib_lo_pair(uint32_t w) {
+  return ((w ^ 0x00080008u) & 0x000F000Fu) | kF16Magic2;
+}
+__device__ __forceinline__ uint32_t nib_hi_pair(uint32_t w) {
+  return ((w ^ 0x00800080u) & 0x00F000F0u) | kF16Magic2;
+}
+
 // Eight signed INT4 codes (one dword, low nibble first) -> eight exact fp16
-// values in k_order_h.  The XOR moves two's complement [-8,7] to offset-binary
-// u = q + 8, so 1024 + u - 1032 = q exactly.
+// values in k_order_h:  lo pairs: (1024 + u) - 1032 = q;  hi pairs:
+// (1024 + 16u) / 16 - 72 = q (both exact in fp16).
 __device__ __forceinline__ h8 unpack_q4(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
-  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const uint32_t r0 = h2_bits(bits_h2((x & 0x000F000Fu) | kF16Magic2) - bias);
-  const uint32_t r1 = h2_bits(bits_h2(((x >> 4) & 0x000F000Fu) | kF16Magic2) - bias);
-  const uint32_t r2 = h2_bits(bits_h2(((x >> 8) & 0x000F000Fu) | kF16Magic2) - bias);
-  const uint32_t r3 = h2_bits(bits_h2(((x >> 12) & 0x000F000Fu) | kF16Magic2) - bias);
+  const h2 lo_bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2 hi_bias = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t w8 = w >> 8;
+  const uint32_t r0 = h2_bits(bits_h2(nib_lo_pair(w)) + lo_bias);
+  const uint32_t r1 = h2_bits(__builtin_elementwise_fma(bits_h2(nib_hi_pair(w)), sixteenth, hi_bias));
+  const uint32_t r2 = h2_bits(bits_h2(nib_lo_pair(w8)) + lo_bias);
+  const uint32_t r3 = h2_bits(__builtin_elementwise_fma(bits_h2(nib_hi_pair(w8)), sixteenth, hi_bias));
   const u4 v = {r0, r1, r2, r3};
   return __builtin_bit_cast(h8, v);
 }
 
 // Same, each code multiplied by the group code c (exact: |q*c| <= 2040 < 2048).
 __device__ __forceinline__ h8 unpack_q4_scaled(uint32_t w, _Float16 c) {
-  const uint32_t x = w ^ 0x88888888u;
-  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const h2 cc = {c, c};
-  const uint32_t r0 = h2_bits((bits_h2((x & 0x000F000Fu) | kF16Magic2) - bias) * cc);
-  const uint32_t r1 = h2_bits((bits_h2(((x >> 4) & 0x000F000Fu) | kF16Magic2) - bias) * cc);
-  const uint32_t r2 = h2_bits((bits_h2(((x >> 8) & 0x000F000Fu) | kF16Magic2) - bias) * cc);
-  const uint32_t r3 = h2_bits((bits_h2(((x >> 12) & 0x000F000Fu) | kF16Magic2) - bias) * cc);
-  const u4 v = {r0, r1, r2, r3};
-  return __builtin_bit_cast(h8, v);
+  const h8 q = unpack_q4(w);
+  const h8 cc = {c, c, c, c, c, c, c, c};
+  return q * cc;
 }
 
 // Eight INT8 codes (two dwords) -> eight exact fp16 values in k_order_z.

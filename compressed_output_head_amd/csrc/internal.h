@@ -12,6 +12,10 @@ constexpr int kKTile = 128;        // columns per residual tile
 constexpr int kTileBytes = 1024;   // 16 rows x 128 columns of INT4
 constexpr int kMaxRank = 1024;     // per part (r_c, r_r)
 constexpr int kDecodeMaxTokens = 64;
+// Up to this many tokens the decode kernel may keep all of H in LDS.
+constexpr int kDecodeLdsTokens = 16;
+// LDS budget of that kernel: N*(D+8)*2 bytes of H plus N*r*4 bytes of Z.
+constexpr uint64_t kDecodeLdsBytes = 48 * 1024;
 
 inline uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -26,7 +30,7 @@ struct WorkspaceLayout {
   int64_t n16;          // tokens rounded up to 16
   int rc32, rr32;       // ranks rounded up to 32
   int zsteps;           // (rc32 + rr32) / 32
-  uint64_t hf, hscale, z32, zf, zscale, total;
+  uint64_t hf, hscale, zf, zscale, z32, hc, total;
 };
 WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens);
 
@@ -52,12 +56,16 @@ struct FwdArgs {
   // workspace
   _Float16* hf;               // [n16/16][D/32][64][8] converted, scaled H
   float* hscale;              // [n16]
-  float* z32;                 // [n16][r]
   _Float16* zf;               // [n16/16][2*zsteps][64][8] hi/lo pre-projection
   float* zscale;              // [n16]
+  float* z32;                 // [N][r] fp32 pre-projection (small-N decode path only)
+  _Float16* hc;               // [N][D] scaled fp16 H rows in kernel k-order (small-N decode path only)
 };
 
 hipError_t launch_prep(const FwdArgs& a, hipStream_t s);
+hipError_t launch_prep_z(const FwdArgs& a, hipStream_t s);
+bool decode_lds_eligible(const FwdArgs& a);
+hipError_t launch_decode_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_tile(const FwdArgs& a, hipStream_t s);
 

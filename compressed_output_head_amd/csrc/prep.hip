@@ -19,7 +19,8 @@ namespace archead {
 
 namespace {
 
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepWaves = kPrepThreads / 64;
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -29,106 +30,106 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_max(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kPrepWaves; ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+  return m;
+}
 
-// grid (n16, nJ): block (n, jc) converts token n (jc == 0) and computes
-// z32[n][4*jc + wave].
-__global__ __launch_bounds__(kPrepThreads) void prep_hz_kernel(const FwdArgs a) {
+// One workgroup per token row n (rows N..n16-1 are zero padding):
+//   1. S_n from max|H[n,:]|; hf (and hc for small N) = fp16(H[n,:] * 2^S_n)
+//   2. z[j] = sum_k H[n,k] B_hat[j,k] for all j < r (fp32, one wave per j, kept in LDS)
+//   3. F_n from max_j |z[j]|; zf = fp16 hi/lo split of z * 2^F_n
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const FwdArgs a) {
+  __shared__ float red[kPrepWaves];
+  __shared__ float zrow[2 * kMaxRank];
   const int64_t n = blockIdx.x;
-  const int jc = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool real = n < a.N;
   const uint16_t* hrow = a.H + (real ? n : 0) * a.H_stride;
   const int nchunk = (int)(a.D / 8);
-
-  if (jc == 0) {
-    __shared__ float red[kPrepThreads / 64];
-    float m = 0.0f;
-    if (real) {
-      for (int c = tid; c < nchunk; c += kPrepThreads) {
-        const u4 raw = *reinterpret_cast<const u4*>(hrow + 8 * c);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] & 0xffffu))));
-          m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] >> 16))));
-        }
-      }
-    }
-    m = wave_max(m);
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const int S = row_exponent(m);
-    if (tid == 0) a.hscale[n] = real ? ldexpf(1.0f, -S) : 0.0f;
-    const int64_t tile = n >> 4;
-    const int i = (int)(n & 15);
-    for (int c = tid; c < nchunk; c += kPrepThreads) {
-      const int64_t k0 = 8 * (int64_t)c;
-      const int64_t ks = k0 >> 5;
-      const int q = (int)((k0 >> 3) & 3);
-      float v[8];
-      if (real) {
-        const u4 raw = *reinterpret_cast<const u4*>(hrow + k0);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          v[2 * w] = bf16_to_f32((uint16_t)(raw[w] & 0xffffu));
-          v[2 * w + 1] = bf16_to_f32((uint16_t)(raw[w] >> 16));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-      }
-      h8 out;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) out[j] = (_Float16)ldexpf(v[k_order_h(j)], S);
-      *reinterpret_cast<h8*>(a.hf + (((tile * a.nks + ks) * 64) + 16 * q + i) * 8) = out;
-    }
-  }
-
-  const int r = a.r_c + a.r_r;
-  const int j = 4 * jc + wave;
-  if (j >= r) return;
-  float acc = 0.0f;
-  if (real) {
-    const int8_t* brow = a.b_codes + (int64_t)j * a.D;
-    const uint16_t* srow = a.b_scales + (int64_t)j * a.ng;
-    for (int c = lane; c < nchunk; c += 64) {
-      const int64_t k0 = 8 * (int64_t)c;
-      const u4 hraw = *reinterpret_cast<const u4*>(hrow + k0);
-      const u2 braw = *reinterpret_cast<const u2*>(brow + k0);
-      float part = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t bw = braw[w >> 1] >> (16 * (w & 1));
-        const float b0 = (float)(int8_t)(bw & 0xff);
-        const float b1 = (float)(int8_t)((bw >> 8) & 0xff);
-        part = fmaf(bf16_to_f32((uint16_t)(hraw[w] & 0xffffu)), b0, part);
-        part = fmaf(bf16_to_f32((uint16_t)(hraw[w] >> 16)), b1, part);
-      }
-      acc = fmaf(f16_to_f32(srow[k0 / a.g]), part, acc);
-    }
-    acc = wave_sum(acc);
-  }
-  if (lane == 0) a.z32[n * r + j] = acc;
-}
-
-// grid (n16), one wave per token: per-token exponent of Z and its fp16 hi/lo
-// operand fragments (zero where the rank is padded to 32).
-__global__ __launch_bounds__(64) void prep_zf_kernel(const FwdArgs a) {
-  const int64_t n = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int r = a.r_c + a.r_r;
-  const bool real = n < a.N;
-  const float* zrow = a.z32 + n * r;
-  float m = 0.0f;
-  if (real)
-    for (int j = lane; j < r; j += 64) m = fmaxf(m, fabsf(zrow[j]));
-  m = wave_max(m);
-  const int F = row_exponent(m);
-  if (lane == 0) a.zscale[n] = real ? ldexpf(1.0f, -F) : 0.0f;
   const int64_t tile = n >> 4;
   const int i = (int)(n & 15);
+
+  // 1. hidden-state row -> scaled fp16 operand fragments
+  float m = 0.0f;
+  if (real) {
+    for (int c = tid; c < nchunk; c += kPrepThreads) {
+      const u4 raw = *reinterpret_cast<const u4*>(hrow + 8 * c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] & 0xffffu))));
+        m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] >> 16))));
+      }
+    }
+  }
+  m = block_max(m, red);
+  const int S = row_exponent(m);
+  if (tid == 0) a.hscale[n] = real ? ldexpf(1.0f, -S) : 0.0f;
+  for (int c = tid; c < nchunk; c += kPrepThreads) {
+    const int64_t k0 = 8 * (int64_t)c;
+    const int64_t ks = k0 >> 5;
+    const int q = (int)((k0 >> 3) & 3);
+    float v[8];
+    if (real) {
+      const u4 raw = *reinterpret_cast<const u4*>(hrow + k0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        v[2 * w] = bf16_to_f32((uint16_t)(raw[w] & 0xffffu));
+        v[2 * w + 1] = bf16_to_f32((uint16_t)(raw[w] >> 16));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+    h8 out;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = (_Float16)ldexpf(v[k_order_h(j)], S);
+    *reinterpret_cast<h8*>(a.hf + (((tile * a.nks + ks) * 64) + 16 * q + i) * 8) = out;
+  }
+
+  const int r = a.r_c + a.r_r;
+  if (r == 0) return;
+  // 2. pre-projection z[j] for this token
+  for (int j = wave; j < r; j += kPrepWaves) {
+    float acc = 0.0f;
+    if (real) {
+      const int8_t* brow = a.b_codes + (int64_t)j * a.D;
+      const uint16_t* srow = a.b_scales + (int64_t)j * a.ng;
+      for (int c = lane; c < nchunk; c += 64) {
+        const int64_t k0 = 8 * (int64_t)c;
+        const u4 hraw = *reinterpret_cast<const u4*>(hrow + k0);
+        const u2 braw = *reinterpret_cast<const u2*>(brow + k0);
+        float part = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t bw = braw[w >> 1] >> (16 * (w & 1));
+          part = fmaf(bf16_to_f32((uint16_t)(hraw[w] & 0xffffu)), (float)(int8_t)(bw & 0xff), part);
+          part = fmaf(bf16_to_f32((uint16_t)(hraw[w] >> 16)), (float)(int8_t)((bw >> 8) & 0xff), part);
+        }
+        acc = fmaf(f16_to_f32(srow[k0 / a.g]), part, acc);
+      }
+      acc = wave_sum(acc);
+    }
+    if (lane == 0) zrow[j] = acc;
+  }
+  __syncthreads();
+
+  // 3. token exponent of z and its fp16 hi/lo operand fragments
+  float mz = 0.0f;
+  if (real)
+    for (int j = tid; j < r; j += kPrepThreads) mz = fmaxf(mz, fabsf(zrow[j]));
+  mz = block_max(mz, red);
+  const int F = row_exponent(mz);
+  if (tid == 0) a.zscale[n] = real ? ldexpf(1.0f, -F) : 0.0f;
   const int csteps = a.rc32 / 32;
-  for (int e = lane; e < a.zsteps * 4; e += 64) {
+  for (int e = tid; e < a.zsteps * 4; e += kPrepThreads) {
     const int s = e >> 2, q = e & 3;
     const bool part_c = s < csteps;
     const int sl = part_c ? s : s - csteps;
@@ -150,15 +151,100 @@ __global__ __launch_bounds__(64) void prep_zf_kernel(const FwdArgs a) {
   }
 }
 
+// Small-N pre-projection, grid (N, ceil(r/4) + 1):
+//   blockIdx.y < ceil(r/4): z32[n][j] = sum_k H[n,k] B_hat[j,k] in fp32, one
+//     wave per (token, j); every lane issues all its loads before the arithmetic.
+//   blockIdx.y == ceil(r/4): hscale[n] = 2^-S_n and hc[n][:] = fp16(H[n,:] 2^S_n)
+//     in kernel k-order (S_n as in prep_kernel).
+constexpr int kPrepZThreads = 256;
+constexpr int kPrepZMaxChunks = 16;  // D <= 64*8*16 = 8192 columns per lane loop
+
+__global__ __launch_bounds__(kPrepZThreads) void prep_z_kernel(const FwdArgs a) {
+  const int64_t n = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = a.r_c + a.r_r;
+  const int nJ = (r + 3) / 4;
+  const uint16_t* hrow = a.H + n * a.H_stride;
+  const int nchunk = (int)(a.D / 8);
+  if ((int)blockIdx.y == nJ) {
+    __shared__ float red[kPrepZThreads / 64];
+    float m = 0.0f;
+    for (int c = tid; c < nchunk; c += kPrepZThreads) {
+      const u4 raw = *reinterpret_cast<const u4*>(hrow + 8 * c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] & 0xffffu))));
+        m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] >> 16))));
+      }
+    }
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int S = row_exponent(m);
+    if (tid == 0) a.hscale[n] = ldexpf(1.0f, -S);
+    for (int c = tid; c < nchunk; c += kPrepZThreads) {
+      const u4 raw = *reinterpret_cast<const u4*>(hrow + 8 * c);
+      float v[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        v[2 * w] = bf16_to_f32((uint16_t)(raw[w] & 0xffffu));
+        v[2 * w + 1] = bf16_to_f32((uint16_t)(raw[w] >> 16));
+      }
+      h8 out;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[j] = (_Float16)ldexpf(v[k_order_h(j)], S);
+      *reinterpret_cast<h8*>(a.hc + n * a.D + 8 * c) = out;
+    }
+    return;
+  }
+  const int j = blockIdx.y * (kPrepZThreads / 64) + wave;
+  if (j >= r) return;
+  const int8_t* brow = a.b_codes + (int64_t)j * a.D;
+  const uint16_t* srow = a.b_scales + (int64_t)j * a.ng;
+  float acc = 0.0f;
+  for (int c0 = 0; c0 < nchunk; c0 += 64 * kPrepZMaxChunks) {
+    u4 hr[kPrepZMaxChunks];
+    u2 br[kPrepZMaxChunks];
+    uint16_t sr[kPrepZMaxChunks];
+#pragma unroll
+    for (int u = 0; u < kPrepZMaxChunks; ++u) {
+      const int c = c0 + lane + 64 * u;
+      if (c < nchunk) {
+        hr[u] = *reinterpret_cast<const u4*>(hrow + 8 * (int64_t)c);
+        br[u] = *reinterpret_cast<const u2*>(brow + 8 * (int64_t)c);
+        sr[u] = srow[(8 * c) / a.g];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepZMaxChunks; ++u) {
+      const int c = c0 + lane + 64 * u;
+      if (c < nchunk) {
+        float part = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t bw = br[u][w >> 1] >> (16 * (w & 1));
+          part = fmaf(bf16_to_f32((uint16_t)(hr[u][w] & 0xffffu)), (float)(int8_t)(bw & 0xff), part);
+          part = fmaf(bf16_to_f32((uint16_t)(hr[u][w] >> 16)), (float)(int8_t)((bw >> 8) & 0xff), part);
+        }
+        acc = fmaf(f16_to_f32(sr[u]), part, acc);
+      }
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) a.z32[n * r + j] = acc;
+}
+
 }  // namespace
 
-hipError_t launch_prep(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_prep_z(const FwdArgs& a, hipStream_t s) {
   const int r = a.r_c + a.r_r;
-  const int nJ = r > 0 ? (r + 3) / 4 : 1;
-  hipLaunchKernelGGL(prep_hz_kernel, dim3((unsigned)a.n16, (unsigned)nJ), dim3(kPrepThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || r == 0) return e;
-  hipLaunchKernelGGL(prep_zf_kernel, dim3((unsigned)a.n16), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(prep_z_kernel, dim3((unsigned)a.N, (unsigned)((r + 3) / 4 + 1)), dim3(kPrepZThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const FwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)a.n16), dim3(kPrepThreads), 0, s, a);
   return hipGetLastError();
 }
 

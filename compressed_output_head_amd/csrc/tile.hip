@@ -60,11 +60,11 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const FwdArgs a) {
       const int wb = p >> 6, l = p & 63;
       const int64_t B = blk0 + wb;
       if (B < a.nb) {
-        const u4 w = rc[(B * a.nkt + kt) * 64 + l];
+        const u4 w = rc[((int64_t)kt * a.nb + B) * 64 + l];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int grp = (kKTile * kt + 32 * s + 8 * (l >> 4)) / a.g;
-          const _Float16 c = (_Float16)(float)a.r_gcodes[(B * a.ng + grp) * 16 + (l & 15)];
+          const _Float16 c = (_Float16)(float)a.r_gcodes[(B * 16 + (l & 15)) * a.ng + grp];
           sW[wb][s][l] = unpack_q4_scaled(w[s], c);
         }
       } else {

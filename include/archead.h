@@ -80,12 +80,13 @@ typedef struct {
  *   header      64 B: u32 magic 0x48435241, u32 version, u64 V, u64 D,
  *                     u32 r_c, u32 r_r, u32 g, u32 flags (0), 24 zero bytes
  *   r_codes     SC4 codes in tiles of 16 rows x 128 columns (1024 B).  With
- *               V16 = V rounded up to 16, tile (b, kt) of the (V16/16) x (D/128)
- *               grid sits at (b*(D/128) + kt)*1024; its byte 16*l + 4*s + c
+ *               V16 = V rounded up to 16 and nb = V16/16 row blocks, tile
+ *               (b, kt) sits at (kt*nb + b)*1024 (k-tile major, so tiles read
+ *               at the same time by neighbouring waves are adjacent); byte 16*l + 4*s + c
  *               (l < 64, s < 4, c < 4) holds row 16*b + l%16 at columns
  *               k = 128*kt + 32*s + 8*(l/16) + 2*c (low nibble) and k+1 (high
  *               nibble), two's complement.  Rows >= V are zero.
- *   r_gcodes    uint8 group codes: byte (b*(D/g) + t)*16 + i is row 16*b+i, group t.
+ *   r_gcodes    uint8 group codes [V16][D/g], row-major: byte v*(D/g) + t is row v, group t.
  *   r_rowscale  fp16 per-row residual scale s_R [V16].
  *   a_codes     int8 [V16][r_c + r_r], row v = A_c[v,:] then A_w[v,:].
  *   a_scales    fp16 [V16][n_A], n_A = (r_c>0) + (r_r>0): s_Ac[v] then s_Aw[v].

@@ -40,13 +40,14 @@ Packed head, format version 1 (all integers little-endian).
   Sections in order, each starting on a 256-byte boundary:
    header     64 B: u32 magic 0x48435241, u32 version 1, u64 V, u64 D,
                     u32 r_c, u32 r_r, u32 g, u32 flags 0, 24 zero bytes
-   r_codes    nb*nkt tiles of 1024 B.  In tile (b, kt), byte 16*l + 4*s + c
+   r_codes    nkt*nb tiles of 1024 B, k-tile major: tile (b, kt) starts at
+              (kt*nb + b)*1024.  In tile (b, kt), byte 16*l + 4*s + c
               (l in [0,64), s in [0,4), c in [0,4)) holds the two INT4 codes
               (two's complement) of row v = 16*b + (l mod 16) at
               k = 128*kt + 32*s + 8*(l div 16) + 2*c   (low nibble)
               and k + 1                                (high nibble).
-   r_gcodes   nb*ng*16 B: byte (b*ng + t)*16 + i = uint8 group code of row
-              16*b + i, group t (columns t*g .. t*g+g-1).
+   r_gcodes   V16*ng B, row-major: byte v*ng + t = uint8 group code of row v,
+              group t (columns t*g .. t*g+g-1).
    r_rowscale V16 fp16: per-row residual scale s_R.
    a_codes    V16*r int8, row-major; row v = [A_c[v, :r_c] | A_w[v, :r_r]].
    a_scales   V16*nA fp16; row v = [s_Ac[v] if r_c>0, s_Aw[v] if r_r>0].
@@ -121,19 +122,19 @@ def persistent_bytes(V, D, r_c, r_r, g):
 
 def _nibbles_to_tiles(nib):
     """[V16, D] nibbles -> r_codes bytes.  Writing k = 128*kt + 32*s + 8*q + 2*c + h
-    and v = 16*b + i, the tile byte order is (b, kt, q, i, s, c) and h selects
-    the low (h=0) or high (h=1) nibble; lane l = 16*q + i."""
+    and v = 16*b + i, the byte order is (kt, b, q, i, s, c) and h selects the
+    low (h=0) or high (h=1) nibble; lane l = 16*q + i."""
     V16, D = nib.shape
     t = nib.reshape(V16 // 16, 16, D // 128, 4, 4, 4, 2)        # b i kt s q c h
-    t = t.transpose(0, 2, 4, 1, 3, 5, 6)                        # b kt q i s c h
+    t = t.transpose(2, 0, 4, 1, 3, 5, 6)                        # kt b q i s c h
     return (t[..., 0] | (t[..., 1] << 4)).astype(np.uint8).reshape(-1)
 
 
 def _tiles_to_nibbles(raw, V16, D):
     """Inverse of ``_nibbles_to_tiles``."""
-    t = raw.reshape(V16 // 16, D // 128, 4, 16, 4, 4)            # b kt q i s c
-    both = np.stack([t & 0xF, t >> 4], axis=-1)                  # b kt q i s c h
-    return both.transpose(0, 3, 1, 4, 2, 5, 6).reshape(V16, D)   # b i kt s q c h
+    t = raw.reshape(D // 128, V16 // 16, 4, 16, 4, 4)            # kt b q i s c
+    both = np.stack([t & 0xF, t >> 4], axis=-1)                  # kt b q i s c h
+    return both.transpose(1, 3, 0, 4, 2, 5, 6).reshape(V16, D)   # b i kt s q c h
 
 
 def pack(head) -> np.ndarray:
@@ -169,7 +170,7 @@ def pack(head) -> np.ndarray:
     ng = D // g
     c8 = np.zeros((V16, ng), np.uint8)
     c8[:V] = head.c8
-    put("r_gcodes", c8.reshape(V16 // 16, 16, ng).transpose(0, 2, 1))
+    put("r_gcodes", c8)
 
     sR = np.zeros(V16, np.float16)
     sR[:V] = head.s_R
@@ -210,7 +211,7 @@ def unpack(buf: np.ndarray, V, D, r_c, r_r, g) -> dict:
     nib = _tiles_to_nibbles(get("r_codes", np.uint8), V16, D)
     q4 = nib.astype(np.int8)
     q4[q4 >= 8] -= 16
-    c8 = get("r_gcodes", np.uint8).reshape(V16 // 16, ng, 16).transpose(0, 2, 1).reshape(V16, ng)
+    c8 = get("r_gcodes", np.uint8).reshape(V16, ng)
     s_R = get("r_rowscale", np.float16)
     A = get("a_codes", np.int8).reshape(V16, r_c + r_r)
     nA = int(r_c > 0) + int(r_r > 0)

@@ -153,7 +153,7 @@ def _tile_pack_loop(q4_padded):
     """Element-by-element reading of the residual tile order (tiny shapes only)."""
     V16, D = q4_padded.shape
     out = np.zeros(V16 * D // 2, np.uint8)
-    nkt = D // 128
+    nb = V16 // 16
     for v in range(V16):
         for k in range(0, D, 2):
             b, i = divmod(v, 16)
@@ -162,7 +162,7 @@ def _tile_pack_loop(q4_padded):
             q, rem8 = divmod(rem, 8)
             c = rem8 // 2
             lane = 16 * q + i
-            pos = (b * nkt + kt) * 1024 + 16 * lane + 4 * s + c
+            pos = (kt * nb + b) * 1024 + 16 * lane + 4 * s + c
             lo = int(q4_padded[v, k]) & 0xF
             hi = int(q4_padded[v, k + 1]) & 0xF
             out[pos] = lo | (hi << 4)
