@@ -226,7 +226,8 @@ def test_persistent_size_equals_sum_of_stored_tensors():
 
 def test_storage_ratio_matches_pages():
     """The pages quote 25.61% of the BF16 head for the packed Qwen3-8B head
-    (Sec. 5, comparison with GPTQ) and a rank-6 correction (Table 9 ablation);
+    (discussion of Table 7, comparison with GPTQ) and a rank-6 correction
+    (Table 9 ablation);
     read with r_c = r_r = 6 and g = 128 the format gives the same 25.61%, i.e. a
     3.90x reduction (the abstract's 3.7-3.9x range)."""
     V, D = 151936, 4096
