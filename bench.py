@@ -31,7 +31,14 @@ sys.path.insert(0, ROOT)
 METRIC = "packed-head logits: decode HBM GB/s and prefill TFLOP/s (% of roofline), V=151936"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
-KERNEL_SOURCES = ["prep.hip", "decode.hip", "tile.hip", "device_common.h"]
+# sources that decide each main kernel's code (a counter summary is only
+# reported while these are unchanged)
+KERNEL_SOURCES = {
+    "decode_lds_kernel": ["decode.hip", "device_common.h", "internal.h"],
+    "decode_kernel": ["decode.hip", "device_common.h", "internal.h"],
+    "tile_kernel": ["tile.hip", "device_common.h", "internal.h"],
+    "tile32_kernel": ["tile.hip", "device_common.h", "internal.h"],
+}
 
 
 def log(*a):
@@ -61,17 +68,18 @@ def algorithmic(cfg, L, N):
                 step_bytes=L["payload_bytes"] + 2 * N * D + N * V * ysz)
 
 
-def kernel_hash():
+def kernel_hash(kernel=None):
     h = hashlib.sha256()
-    for s in KERNEL_SOURCES:
+    names = KERNEL_SOURCES.get(kernel) or sorted({f for v in KERNEL_SOURCES.values() for f in v})
+    for s in names:
         with open(os.path.join(ROOT, "compressed_output_head_amd", "csrc", s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload, per_launch_units):
+def traffic_for(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the current sources of that kernel; else None."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
@@ -79,9 +87,65 @@ def traffic_for(workload, per_launch_units):
         t = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel") != kernel or t.get("kernel_hash") != kernel_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+COPY_CAL_BYTES = 256 << 20  # device-to-device copy used to calibrate the HBM byte counters
+COPY_CAL_REPS = 4
+
+
+def copy_calibration():
+    """COPY_CAL_REPS device-to-device copies of COPY_CAL_BYTES, issued as the
+    process's first GPU work so a counter run can find them as its first
+    copy dispatches."""
+    import torch
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(COPY_CAL_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _pmc_per_dispatch(path, counter):
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+
+def pmc_summary(workload, kernel, fetch_csv, write_csv, commands):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    of ``bench.py --copy-calibration`` into HBM bytes per launch of ``kernel``,
+    scaled by what the counters read for the calibration copies."""
+    out = {"workload": workload, "kernel": kernel, "kernel_hash": kernel_hash(kernel),
+           "copy_calibration_bytes": COPY_CAL_BYTES, "commands": commands}
+    total = 0.0
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        d = _pmc_per_dispatch(path, name)
+        cal = [v for k, v in d if "copyBuffer" in k][:COPY_CAL_REPS]
+        ker = [v for k, v in d if kernel in k]
+        if len(cal) < COPY_CAL_REPS or not ker:
+            raise SystemExit(f"{path}: {len(cal)} calibration copies, {len(ker)} dispatches of {kernel}")
+        factor = COPY_CAL_BYTES / (float(np.mean(cal)) * 1024.0)
+        per_launch = float(np.mean(ker)) * 1024.0 * factor
+        out[name] = {"kib_per_dispatch_mean": float(np.mean(ker)), "dispatches": len(ker),
+                     "copy_kib_mean": float(np.mean(cal)), "scale": round(factor, 4),
+                     "bytes_per_launch": round(per_launch)}
+        total += per_launch
+    out["hbm_bytes_per_launch"] = round(total)
+    return out
+
+
+def dominant_kernel(N):
+    """Name of the main kernel the library launches for N tokens (automatic path)."""
+    if N <= 16:
+        return "decode_lds_kernel"
+    if N <= 64:
+        return "decode_kernel"
+    return "tile_kernel"
 
 
 def run_workload(name, steps, warmup, path=0):
@@ -129,7 +193,7 @@ def run_workload(name, steps, warmup, path=0):
     torch.cuda.synchronize()
     kms = [evb[i].elapsed_time(eve[i]) for i in range(steps)]
     A = algorithmic(cfg, L, N)
-    return dict(cfg=cfg, L=L, A=A, ms=ms, kernel_ms=float(np.mean(kms)),
+    return dict(cfg=cfg, L=L, A=A, ms=ms, kernel=dominant_kernel(N), kernel_ms=float(np.mean(kms)),
                 kernel_ms_min=float(np.min(kms)), kernel_ms_max=float(np.max(kms)))
 
 
@@ -159,8 +223,8 @@ def roofline_decode(r):
     A = r["A"]
     achieved = A["main_bytes"] / (r["kernel_ms"] / 1e3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(r["cfg"]["name"], 1),
-            "kernel": "decode_kernel", "kernel_ms": round(r["kernel_ms"], 5),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(r["cfg"]["name"], r["kernel"]),
+            "kernel": r["kernel"], "kernel_ms": round(r["kernel_ms"], 5),
             "algorithmic_bytes_per_launch": A["main_bytes"]}
 
 
@@ -168,8 +232,8 @@ def roofline_tile(r):
     A = r["A"]
     achieved = A["main_flops"] / (r["kernel_ms"] / 1e3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic_for(r["cfg"]["name"], 1),
-            "kernel": "tile_kernel", "kernel_ms": round(r["kernel_ms"], 4),
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic_for(r["cfg"]["name"], r["kernel"]),
+            "kernel": r["kernel"], "kernel_ms": round(r["kernel_ms"], 4),
             "algorithmic_flops_per_launch": A["main_flops"]}
 
 
@@ -182,7 +246,20 @@ def main():
     ap.add_argument("--secondary", default="prefill", help="second workload ('' to skip)")
     ap.add_argument("--cpu-sample-rows", type=int, default=24576)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run the device copies that calibrate HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: write profiles/traffic_WORKLOAD.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--pmc-commands", nargs="*", default=[], help="the commands that made the --pmc runs")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        wl, kern, fcsv, wcsv = args.pmc_summary
+        t = pmc_summary(wl, kern, fcsv, wcsv, args.pmc_commands)
+        with open(os.path.join(ROOT, "profiles", f"traffic_{wl}.json"), "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -195,6 +272,8 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.copy_calibration:
+        copy_calibration()
     r = run_workload(args.config, args.steps, args.warmup)
     cfg, A = r["cfg"], r["A"]
     value = A["payload"] / (r["ms"] / 1e3) / 1e9
