@@ -145,7 +145,9 @@ def dominant_kernel(N):
         return "decode_lds_kernel"
     if N <= 64:
         return "decode_kernel"
-    return "tile_kernel"
+    if N <= 128:
+        return "tile_kernel"
+    return "tile32_kernel"
 
 
 def run_workload(name, steps, warmup, path=0):

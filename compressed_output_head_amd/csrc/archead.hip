@@ -63,21 +63,22 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens) {
   w.rc32 = (int)round_up((uint64_t)d->r_c, 32);
   w.rr32 = (int)round_up((uint64_t)d->r_r, 32);
   w.zsteps = (w.rc32 + w.rr32) / 32;
-  const uint64_t n16 = (uint64_t)w.n16, D = (uint64_t)d->D;
+  w.n32 = (int64_t)round_up((uint64_t)std::max<int64_t>(n_tokens, 0), 32);
+  const uint64_t n32 = (uint64_t)w.n32, D = (uint64_t)d->D;
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) {
     const uint64_t at = off;
     off = round_up(off + bytes, ARCHEAD_ALIGNMENT);
     return at;
   };
-  w.hf = take(n16 * D * 2);
-  w.hscale = take(n16 * 4);
-  w.zf = take(n16 * (uint64_t)w.zsteps * 2 * 32 * 2);
-  w.zscale = take(n16 * 4);
+  w.hf = take(n32 * D * 2);
+  w.hscale = take(n32 * 4);
+  w.zf = take(n32 * (uint64_t)w.zsteps * 2 * 32 * 2);
+  w.zscale = take(n32 * 4);
   const uint64_t nsmall = n_tokens <= kDecodeLdsTokens ? (uint64_t)std::max<int64_t>(n_tokens, 0) : 0;
   w.z32 = take(nsmall * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
   w.hc = take(nsmall * D * 2);
-  w.total = n16 ? off : 0;
+  w.total = n32 ? off : 0;
   return w;
 }
 
@@ -266,6 +267,7 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   a.D = d->D;
   a.N = N;
   a.n16 = W.n16;
+  a.n32 = W.n32;
   a.nb = L.padded_rows / 16;
   a.r_c = d->r_c;
   a.r_r = d->r_r;
@@ -300,7 +302,8 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   (void)hipGetLastError();  // start from a clean error state
   const bool decode = path == ARCHEAD_PATH_DECODE || (path == ARCHEAD_PATH_AUTO && N <= kDecodeMaxTokens);
   const bool small = decode && decode_lds_eligible(a);
-  if ((small ? launch_prep_z(a, s) : launch_prep(a, s)) != hipSuccess) return ARCHEAD_E_HIP;
+  const bool rows32 = !decode && tile32_eligible(a);  // launch_tile picks the same kernel
+  if ((small ? launch_prep_z(a, s) : launch_prep(a, rows32, s)) != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return ARCHEAD_E_HIP;
   const hipError_t e = small ? launch_decode_lds(a, s) : decode ? launch_decode(a, s) : launch_tile(a, s);
   if (e != hipSuccess) return ARCHEAD_E_HIP;

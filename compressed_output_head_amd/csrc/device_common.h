@@ -12,6 +12,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef float f16x __attribute__((ext_vector_type(16)));
 
 // Kernel k-order inside one 8-column run of an MFMA operand.  Operand slot j
 // (0..7) of a lane carries column k_order_h(j) of the run for H and the
@@ -106,8 +107,16 @@ __device__ __forceinline__ int row_exponent(float maxabs) {
   return 15 - e;
 }
 
+// 16 x 16 x 32: lane l holds A row l%16 / B column l%16, k 8*(l/16) .. +8;
+// result lane l holds rows 4*(l/16) + e, column l%16.
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 32 x 32 x 16: lane l holds A row l%32 / B column l%32, k 8*(l/32) .. +8;
+// result element v of lane l is row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+__device__ __forceinline__ f16x mfma32(h8 a, h8 b, f16x c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace archead

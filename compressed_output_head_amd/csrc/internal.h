@@ -28,6 +28,7 @@ void compute_layout(const archead_dims* d, archead_layout* L);
 // Device workspace of one call (all offsets 256-byte aligned).
 struct WorkspaceLayout {
   int64_t n16;          // tokens rounded up to 16
+  int64_t n32;          // tokens rounded up to 32 (rows of every per-token workspace section)
   int rc32, rr32;       // ranks rounded up to 32
   int zsteps;           // (rc32 + rr32) / 32
   uint64_t hf, hscale, zf, zscale, z32, hc, total;
@@ -37,7 +38,7 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens);
 // Everything a kernel needs, resolved to raw device pointers.
 struct FwdArgs {
   // dims
-  int64_t V, D, N, n16, nb;   // nb = V16/16 row blocks
+  int64_t V, D, N, n16, n32, nb;   // nb = V16/16 row blocks
   int r_c, r_r, g, ng, nkt, nks, rc32, rr32, zsteps, nA;
   // input / output
   const uint16_t* H;          // bf16 [N][H_stride]
@@ -54,15 +55,21 @@ struct FwdArgs {
   const int8_t* b_codes;
   const uint16_t* b_scales;
   // workspace
-  _Float16* hf;               // [n16/16][D/32][64][8] converted, scaled H
-  float* hscale;              // [n16]
-  _Float16* zf;               // [n16/16][2*zsteps][64][8] hi/lo pre-projection
-  float* zscale;              // [n16]
+  // hf/zf hold either the 16-row operand layout (16 x 16 x 32 MFMA kernels) or
+  // the 32-row layout (32 x 32 x 16 MFMA kernel), whichever the chosen main
+  // kernel reads:
+  //   16-row: hf [n16/16][D/32][64][8],          zf [n16/16][2*zsteps][64][8]
+  //   32-row: hf [n32/32][D/128][8][64][8],      zf [n32/32][4*zsteps][64][8]
+  _Float16* hf;               // converted, scaled H
+  float* hscale;              // [n32]
+  _Float16* zf;               // hi/lo pre-projection
+  float* zscale;              // [n32]
   float* z32;                 // [N][r] fp32 pre-projection (small-N decode path only)
   _Float16* hc;               // [N][D] scaled fp16 H rows in kernel k-order (small-N decode path only)
 };
 
-hipError_t launch_prep(const FwdArgs& a, hipStream_t s);
+hipError_t launch_prep(const FwdArgs& a, bool rows32, hipStream_t s);
+bool tile32_eligible(const FwdArgs& a);
 hipError_t launch_prep_z(const FwdArgs& a, hipStream_t s);
 bool decode_lds_eligible(const FwdArgs& a);
 hipError_t launch_decode_lds(const FwdArgs& a, hipStream_t s);

@@ -11,7 +11,9 @@
 //   zf  : Z * 2^F_n split into fp16 hi + lo (22 significant bits), per-token
 //         exponent F_n chosen the same way; zscale[n] = 2^-F_n.
 // Both are stored in MFMA operand order (see device_common.h) so the forward
-// kernels read each 16x32 operand fragment as one contiguous 1 KB block.
+// kernels read each operand fragment as one contiguous 1 KB block: 16 rows x
+// 32 columns for the 16 x 16 x 32 MFMA kernels, 32 rows x 16 columns for the
+// 32 x 32 x 16 MFMA kernel (layouts in internal.h).
 #include "device_common.h"
 #include "internal.h"
 
@@ -42,10 +44,16 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return m;
 }
 
-// One workgroup per token row n (rows N..n16-1 are zero padding):
-//   1. S_n from max|H[n,:]|; hf (and hc for small N) = fp16(H[n,:] * 2^S_n)
+// One workgroup per token row n (rows N..n16-1, or N..n32-1 for the 32-row
+// layout, are zero padding):
+//   1. S_n from max|H[n,:]|; hf = fp16(H[n,:] * 2^S_n)
 //   2. z[j] = sum_k H[n,k] B_hat[j,k] for all j < r (fp32, one wave per j, kept in LDS)
 //   3. F_n from max_j |z[j]|; zf = fp16 hi/lo split of z * 2^F_n
+//
+// 32-row layout: within a 128-column k-tile, 8-column run R (0..15) of token
+// n goes to MFMA step t = (R >> 2) + 4 * ((R >> 1) & 1), lane (n & 31) + 32 * (R & 1);
+// the residual codes are read in the same run order (tile32_kernel).
+template <bool ROWS32>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const FwdArgs a) {
   __shared__ float red[kPrepWaves];
   __shared__ float zrow[2 * kMaxRank];
@@ -54,8 +62,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const FwdArgs a) {
   const bool real = n < a.N;
   const uint16_t* hrow = a.H + (real ? n : 0) * a.H_stride;
   const int nchunk = (int)(a.D / 8);
-  const int64_t tile = n >> 4;
-  const int i = (int)(n & 15);
+  const int64_t tile = ROWS32 ? n >> 5 : n >> 4;
+  const int i = ROWS32 ? (int)(n & 31) : (int)(n & 15);
 
   // 1. hidden-state row -> scaled fp16 operand fragments
   float m = 0.0f;
@@ -91,7 +99,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const FwdArgs a) {
     h8 out;
 #pragma unroll
     for (int j = 0; j < 8; ++j) out[j] = (_Float16)ldexpf(v[k_order_h(j)], S);
-    *reinterpret_cast<h8*>(a.hf + (((tile * a.nks + ks) * 64) + 16 * q + i) * 8) = out;
+    int64_t frag;
+    if (ROWS32) {
+      const int64_t kt = k0 >> 7;
+      const int R = (int)((k0 >> 3) & 15);
+      const int t = (R >> 2) + 4 * ((R >> 1) & 1);
+      frag = ((tile * a.nkt + kt) * 8 + t) * 64 + 32 * (R & 1) + i;
+    } else {
+      frag = (tile * a.nks + ks) * 64 + 16 * q + i;
+    }
+    *reinterpret_cast<h8*>(a.hf + frag * 8) = out;
   }
 
   const int r = a.r_c + a.r_r;
@@ -128,9 +145,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const FwdArgs a) {
   mz = block_max(mz, red);
   const int F = row_exponent(mz);
   if (tid == 0) a.zscale[n] = real ? ldexpf(1.0f, -F) : 0.0f;
-  const int csteps = a.rc32 / 32;
-  for (int e = tid; e < a.zsteps * 4; e += kPrepThreads) {
-    const int s = e >> 2, q = e & 3;
+  // 16-row layout: fragments of 32 ranks, lane 16 q + i holds ranks 8 q ..;
+  // 32-row layout: fragments of 16 ranks, lane 32 q + i holds ranks 8 q ..
+  constexpr int kRanks = ROWS32 ? 16 : 32, kQ = ROWS32 ? 2 : 4, kRows = ROWS32 ? 32 : 16;
+  const int csteps = a.rc32 / kRanks, nsteps = (a.rc32 + a.rr32) / kRanks;
+  for (int e = tid; e < nsteps * kQ; e += kPrepThreads) {
+    const int s = e / kQ, q = e % kQ;
     const bool part_c = s < csteps;
     const int sl = part_c ? s : s - csteps;
     const int rank = part_c ? a.r_c : a.r_r;
@@ -138,14 +158,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const FwdArgs a) {
     h8 hi, lo;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const int col = 32 * sl + 8 * q + k_order_z(jj);
+      const int col = kRanks * sl + 8 * q + k_order_z(jj);
       float z = 0.0f;
       if (real && col < rank) z = ldexpf(zrow[base + col], F);
       const _Float16 zh = (_Float16)z;
       hi[jj] = zh;
       lo[jj] = (_Float16)(z - (float)zh);
     }
-    _Float16* dst = a.zf + ((tile * (2 * a.zsteps) + 2 * s) * 64 + 16 * q + i) * 8;
+    _Float16* dst = a.zf + ((tile * (2 * nsteps) + 2 * s) * 64 + kRows * q + i) * 8;
     *reinterpret_cast<h8*>(dst) = hi;
     *reinterpret_cast<h8*>(dst + 64 * 8) = lo;
   }
@@ -243,8 +263,11 @@ hipError_t launch_prep_z(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)a.n16), dim3(kPrepThreads), 0, s, a);
+hipError_t launch_prep(const FwdArgs& a, bool rows32, hipStream_t s) {
+  if (rows32)
+    hipLaunchKernelGGL(prep_kernel<true>, dim3((unsigned)a.n32), dim3(kPrepThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(prep_kernel<false>, dim3((unsigned)a.n16), dim3(kPrepThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@
 // Waves then run v_mfma_f32_16x16x32_f16 on LDS fragments.  The fp16 row scale
 // s_R, the per-token exponent and the low-rank term (fp16 hi/lo Z against
 // exact INT8 A codes, one accumulator per part) are applied in the epilogue.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -147,9 +149,293 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-N kernel on the 32 x 32 x 16 MFMA: 256 tokens x 256 vocabulary rows
+// per workgroup, four waves in a 2 x 2 grid, 128 x 128 per wave (16 result
+// tiles of 32 x 32, 256 fp32 accumulators per lane, kept in AGPRs).  The
+// hidden dimension advances 64 columns (4 MFMA steps) per stage.
+//
+//   H (32-row layout, written by the prep kernel): an LDS ring of 4 stages of
+//     8 token tiles x 4 steps x 1 KB fragments, filled by buffer loads straight
+//     into LDS two stages ahead; one barrier per stage.
+//   W: lane l of a wave reads, for 32-row vocabulary block CB, row l%16 of
+//     packed block 2 CB + (l/16)%2 at packed lane (l%16) + 16 q, q = l/32 in
+//     the first half of a k-tile and l/32 + 2 in the second; the 16 bytes give
+//     its four 8-column runs of that half, one per MFMA step, unpacked to exact
+//     fp16 integers q4 * c8 right before the MFMAs.  These loads run two stages
+//     ahead in a register ring.  Step t of half h thus covers runs
+//     R = 4 t + 2 h + l/32, the order the prep kernel gives H.
+// Every global read goes through a buffer resource: a wave-uniform offset plus
+// a small per-lane one, so no 64-bit per-lane address stays live.
+constexpr int kT32Threads = 256;
+constexpr int kT32TT = 8;  // 32-token tiles per workgroup
+constexpr int kT32CB = 8;  // 32-row vocabulary blocks per workgroup
+constexpr int kT32Slots = 4, kT32Dist = 2;
+constexpr int kT32HOps = 8, kT32WOps = 8;  // vector-memory operations per wave and stage
+constexpr int kT32Group = 4;  // token tiles that walk the vocabulary together
+constexpr int kXcds = 8;
+
+// s_waitcnt immediate: wait until at most n vector-memory operations of this
+// wave are outstanding (expcnt and lgkmcnt not waited on)
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+struct T32Grid {
+  int ntiles, ncb, ttiles, vtiles;
+};
+__host__ __device__ inline T32Grid t32_grid(const FwdArgs& a) {
+  T32Grid t;
+  t.ntiles = (int)(a.n32 >> 5);
+  t.ncb = (int)((a.nb + 1) >> 1);
+  t.ttiles = (t.ntiles + kT32TT - 1) / kT32TT;
+  t.vtiles = (t.ncb + kT32CB - 1) / kT32CB;
+  return t;
+}
+
+// GC: group codes per k-tile and row that one stage needs: 0 -> one (g >= 128),
+// 1 -> two (g = 64), 2 -> four (g = 32)
+template <int GC>
+__global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
+  __shared__ h8 sH[kT32Slots][kT32TT][4][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5, c32 = lane & 31;
+  const T32Grid G = t32_grid(a);
+
+  // Workgroups are dealt to the XCDs round robin; renumber them so each XCD
+  // owns one contiguous range, and walk it kT32Group token tiles at a time
+  // across the vocabulary, so the workgroups resident on one XCD share a few
+  // H row sets and packed vocabulary tiles in its L2.
+  int L;
+  {
+    const int grid = G.ttiles * G.vtiles, b = blockIdx.x;
+    const int per = grid / kXcds, rem = grid % kXcds, x = b % kXcds;
+    L = x * per + (x < rem ? x : rem) + b / kXcds;
+  }
+  int vt, ttile;
+  {
+    const int full = G.ttiles / kT32Group, span = kT32Group * G.vtiles;
+    if (L < full * span) {
+      const int rr = L % span;
+      vt = rr / kT32Group;
+      ttile = (L / span) * kT32Group + rr % kT32Group;
+    } else {
+      const int w = G.ttiles - full * kT32Group, rr = L - full * span;
+      vt = rr / w;
+      ttile = full * kT32Group + rr % w;
+    }
+  }
+  const int tt0 = ttile * kT32TT;           // first 32-token tile
+  const int cb0 = vt * kT32CB + wn * 4;     // first vocabulary block of this wave
+  const int nS = (int)(a.D / 64);           // stages
+
+  // H: wave w copies step w of the 8 token tiles; tiles past the last one are
+  // zero-filled (only the last row of workgroups has any)
+  const __amdgpu_buffer_rsrc_t hrs = buffer_rsrc(a.hf, (uint32_t)(a.n32 * a.D * 2));
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  const uint32_t hT = (uint32_t)a.nkt * 8192u;  // bytes per token tile
+  const bool hfull = tt0 + kT32TT <= G.ntiles;
+  auto load_h = [&](int ks, int slot) {
+    const uint32_t base = (uint32_t)ks * 4096u + (uint32_t)wave * 1024u;
+    if (hfull) {
+#pragma unroll
+      for (int i = 0; i < kT32TT; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][i][wave][0], 16, lane16,
+                                                 (uint32_t)(tt0 + i) * hT + base, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kT32TT; ++i) {
+        if (tt0 + i < G.ntiles)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][i][wave][0], 16, lane16,
+                                                   (uint32_t)(tt0 + i) * hT + base, 0, 0);
+        else
+          sH[slot][i][wave][lane] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  };
+
+  // W: per-lane byte offsets of this lane's row in each of its 4 blocks (a
+  // block past the end re-reads the last one; its results are never stored)
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(a.r_codes, (uint32_t)(a.nb * 16 * (a.D / 2)));
+  const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(a.r_gcodes, (uint32_t)(a.nb * 16 * a.ng));
+  const uint32_t tstride = (uint32_t)a.nb * 1024u;
+  const int lg = __builtin_ctz((unsigned)a.g);
+  uint32_t wvoff[4], cvoff[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
+    int b = 2 * CB + ((lane >> 4) & 1);
+    if (b >= a.nb) b = (int)a.nb - 1;
+    wvoff[cb] = (uint32_t)b * 1024u + (uint32_t)(lane & 15) * 16u + (uint32_t)g * 256u;
+    cvoff[cb] = ((uint32_t)b * 16u + (uint32_t)(lane & 15)) * (uint32_t)a.ng;
+  }
+  u4 wr[kT32Dist][4];
+  uint32_t wc[kT32Dist][4];
+  auto load_w = [&](int ks, int slot) {
+    const int kt = ks >> 1, half = ks & 1;
+    const uint32_t soff = (uint32_t)kt * tstride + 512u * (uint32_t)half;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      wr[slot][cb] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff[cb], soff, 0));
+      if constexpr (GC == 2)
+        wc[slot][cb] = __builtin_amdgcn_raw_buffer_load_b32(crs, cvoff[cb], 4u * (uint32_t)kt, 0);
+      else if constexpr (GC == 1)
+        wc[slot][cb] = __builtin_amdgcn_raw_buffer_load_b16(crs, cvoff[cb], 2u * (uint32_t)kt, 0);
+      else
+        wc[slot][cb] = __builtin_amdgcn_raw_buffer_load_b8(crs, cvoff[cb], (uint32_t)(kKTile * kt) >> lg, 0);
+    }
+  };
+
+  f16x acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[m][cb] = f16x{};
+
+#pragma unroll
+  for (int ks = 0; ks < kT32Dist; ++ks) load_h(ks < nS ? ks : nS - 1, ks);
+#pragma unroll
+  for (int ks = 0; ks < kT32Dist; ++ks) load_w(ks < nS ? ks : nS - 1, ks);
+
+  // One stage.  On entry this wave has in flight, oldest first, the H copies
+  // and W loads of stage ks, then those of stage ks+1; waiting down to the
+  // last two batches completes stage ks.  The barrier then makes every wave's
+  // copies of stage ks visible and retires all reads of the slot refilled next.
+  auto stage = [&](int ks, auto WS_) {
+    constexpr int ws = decltype(WS_)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kT32HOps + kT32WOps));
+    __syncthreads();
+    load_h(ks + kT32Dist < nS ? ks + kT32Dist : nS - 1, (ks + kT32Dist) & (kT32Slots - 1));
+    const int hs = ks & (kT32Slots - 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      h8 av[4], bv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) av[m] = sH[hs][4 * wm + m][t][lane];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint32_t code = GC == 2 ? (wc[ws][cb] >> (8 * t)) & 0xffu
+                            : GC == 1 ? (wc[ws][cb] >> (8 * (t >> 1))) & 0xffu
+                                      : wc[ws][cb] & 0xffu;
+        bv[cb] = unpack_q4_scaled(wr[ws][cb][t], (_Float16)(float)code);
+      }
+      if (t == 3) load_w(ks + kT32Dist < nS ? ks + kT32Dist : nS - 1, ws);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[m][cb] = mfma32(av[m], bv[cb], acc[m][cb]);
+    }
+  };
+  for (int ks = 0; ks < nS; ks += 2) {  // nS is even (D is a multiple of 128)
+    stage(ks, std::integral_constant<int, 0>{});
+    stage(ks + 1, std::integral_constant<int, 1>{});
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // epilogue: per token tile m the low-rank term (Z hi/lo against exact INT8
+  // A codes, 16 ranks per MFMA step), then scales and the store
+  const int r = a.r_c + a.r_r;
+  const int csteps = a.rc32 / 16, esteps = (a.rc32 + a.rr32) / 16;
+  const h8* zf = reinterpret_cast<const h8*>(a.zf) + lane;
+  float sR[4], sAc[4], sAw[4];
+  const int8_t* arow[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
+    int64_t v = 32 * (int64_t)CB + c32;
+    if (v >= 16 * a.nb) v = 16 * a.nb - 1;
+    sR[cb] = f16_to_f32(a.r_rowscale[v]);
+    sAc[cb] = a.r_c > 0 ? f16_to_f32(a.a_scales[v * a.nA]) : 0.0f;
+    sAw[cb] = a.r_r > 0 ? f16_to_f32(a.a_scales[v * a.nA + a.nA - 1]) : 0.0f;
+    arow[cb] = a.a_codes + v * r;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int T = tt0 + 4 * wm + m;
+    if (T >= G.ntiles) continue;
+    // two vocabulary blocks at a time keep the low-rank accumulators to 64 VGPRs
+#pragma unroll
+    for (int cp = 0; cp < 4; cp += 2) {
+      f16x pc[2], pw[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        pc[j] = f16x{};
+        pw[j] = f16x{};
+      }
+      for (int s = 0; s < esteps; ++s) {
+        const bool part_c = s < csteps;
+        const int col = 16 * (part_c ? s : s - csteps) + 8 * g;
+        const int rank = part_c ? a.r_c : a.r_r;
+        const int base = part_c ? 0 : a.r_c;
+        const h8 zh = zf[((int64_t)T * 2 * esteps + 2 * s) * 64];
+        const h8 zl = zf[((int64_t)T * 2 * esteps + 2 * s + 1) * 64];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          u2 raw = {0u, 0u};
+          if (col < rank) raw = *reinterpret_cast<const u2*>(arow[cp + j] + base + col);
+          const h8 av = unpack_i8x8(raw[0], raw[1]);
+          if (part_c) {
+            pc[j] = mfma32(zh, av, pc[j]);
+            pc[j] = mfma32(zl, av, pc[j]);
+          } else {
+            pw[j] = mfma32(zh, av, pw[j]);
+            pw[j] = mfma32(zl, av, pw[j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t tok = 32 * (int64_t)T + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (tok < a.N) {
+          const float hs = a.hscale[tok], zs = a.zscale[tok];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int cb = cp + j;
+            const int64_t voc = 32 * (int64_t)(cb0 + cb) + c32;
+            if (cb0 + cb < G.ncb && voc < a.V) {
+              float y = hs * (sR[cb] * acc[m][cb][v]);
+              if (r > 0) y = fmaf(zs, fmaf(sAw[cb], pw[j][v], sAc[cb] * pc[j][v]), y);
+              if (a.y_bf16)
+                reinterpret_cast<uint16_t*>(a.Y)[tok * a.Y_stride + voc] = f32_to_bf16(y);
+              else
+                reinterpret_cast<float*>(a.Y)[tok * a.Y_stride + voc] = y;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
+// The 32 x 32 x 16 kernel serves N > 128 when every section it reads fits
+// 32-bit buffer offsets.
+bool tile32_eligible(const FwdArgs& a) {
+  if (a.N <= 128) return false;
+  if ((uint64_t)a.nb * 16 * (uint64_t)a.D / 2 >= (1ull << 32)) return false;
+  if ((uint64_t)a.nb * 16 * (uint64_t)a.ng >= (1ull << 32)) return false;
+  if ((uint64_t)a.n32 * (uint64_t)a.D * 2 >= (1ull << 32)) return false;
+  const T32Grid G = t32_grid(a);
+  return (int64_t)G.ttiles * G.vtiles < (1ll << 31);
+}
+
 hipError_t launch_tile(const FwdArgs& a, hipStream_t s) {
+  if (tile32_eligible(a)) {
+    const T32Grid G = t32_grid(a);
+    const dim3 grid((unsigned)(G.ttiles * G.vtiles)), block(kT32Threads);
+    if (a.g == 32)
+      hipLaunchKernelGGL(tile32_kernel<2>, grid, block, 0, s, a);
+    else if (a.g == 64)
+      hipLaunchKernelGGL(tile32_kernel<1>, grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(tile32_kernel<0>, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   constexpr int TM = 64, TN = 64, WM = 2, WN = 2;
   using C = TileCfg<TM, TN, WM, WN>;
   const int64_t gx = (a.nb + C::kWB - 1) / C::kWB;

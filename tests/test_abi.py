@@ -109,9 +109,9 @@ def test_workspace_bytes(ah):
     up = lambda x: (x + 255) // 256 * 256
     for (V, D, r_c, r_r, g), N in [((1024, 256, 16, 8, 64), 4), ((151936, 4096, 32, 32, 128), 1),
                                    ((151936, 4096, 64, 64, 128), 4096), ((64, 128, 0, 0, 32), 17)]:
-        n16 = (N + 15) // 16 * 16
+        n32 = (N + 31) // 32 * 32
         rc32, rr32 = (r_c + 31) // 32 * 32, (r_r + 31) // 32 * 32
-        want = (up(n16 * D * 2) + up(n16 * 4) + up(n16 * 2 * (rc32 + rr32) * 2) + up(n16 * 4) +
+        want = (up(n32 * D * 2) + up(n32 * 4) + up(n32 * 2 * (rc32 + rr32) * 2) + up(n32 * 4) +
                 up(N * (r_c + r_r) * 4 if N <= 16 else 0) + up(N * D * 2 if N <= 16 else 0))
         assert ah.archead_workspace_bytes(V, D, r_c, r_r, g, N) == want
     assert ah.archead_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0

@@ -59,11 +59,37 @@ def test_shapes_and_ragged_tails(shape, N):
     assert np.array_equal(auto, outs[DECODE if N <= 64 else TILE])
 
 
-@pytest.mark.parametrize("path", [DECODE, TILE])
+LARGE_N_SHAPES = [
+    (1000, 512, 16, 8, 64),   # odd number of 16-row blocks: the last 32-row block is half empty
+    (2048, 1024, 32, 32, 128),
+    (530, 512, 40, 72, 256),
+    (777, 256, 8, 0, 32),
+    (1000, 512, 0, 0, 128),
+]
+
+
+@pytest.mark.parametrize("shape", LARGE_N_SHAPES)
+@pytest.mark.parametrize("N", [129, 300, 1100])
+def test_large_n_tiles(shape, N):
+    """N > 128: 256x256 workgroup tiles, ragged in tokens and vocabulary, with
+    token-tile counts that leave partial groups and grid sizes that are not
+    multiples of the XCD count."""
+    V, D, r_c, r_r, g = shape
+    log(f"large-N shape V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N}")
+    inp = synth.make("tiny", seed=V + N, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=4)
+    head = _head(inp)
+    Yr = oracle.logits(inp.H_bits, inp.head)
+    Yt = to_f64(run(head, inp.H_bits, TILE))
+    check_parity(Yt, Yr, "path=tile")
+    assert np.array_equal(to_f64(run(head, inp.H_bits, 0)), Yt)
+
+
+@pytest.mark.parametrize("path,rows", [(DECODE, 64), (TILE, 64), (TILE, 256)])
 @pytest.mark.parametrize("g", [32, 64, 128, 256])
-def test_one_hot_rows_recover_weights_bit_exactly(path, g):
+def test_one_hot_rows_recover_weights_bit_exactly(path, g, rows):
     """H = unit rows e_k, r_c = r_r = 0: Y[n, v] = q4[v,k] * c8[v,k//g] * s_R[v],
-    a single product of exact operands, so the GPU must return it exactly."""
+    a single product of exact operands, so the GPU must return it exactly.
+    256 rows take the large-N kernel, 64 rows the small-N ones."""
     V, D = 300, 512
     inp = synth.make("tiny", seed=g, V=V, D=D, N=1, r_c=0, r_r=0, g=g)
     h = inp.head
@@ -78,8 +104,8 @@ def test_one_hot_rows_recover_weights_bit_exactly(path, g):
     h.s_R.view(np.uint16)[7] = 0x7BFF          # 65504
     h.s_R.view(np.uint16)[8] = 0x8400          # negative scale
     ks = np.array(sorted(set([0, 1, 7, 8, 31, 32, 33, 63, 64, 127, 128, 255, 256, 300, 511] +
-                             list(range(2, D, 37)))))
-    ks = ks[ks < D][:64]
+                             list(range(2, D, 37 if rows <= 64 else 3)))))
+    ks = ks[ks < D][:rows]
     eye = np.zeros((ks.size, D), np.float32)
     eye[np.arange(ks.size), ks] = 1.0
     Hb = synth.f32_to_bf16_bits(eye)
