@@ -11,6 +11,7 @@
 // Waves then run v_mfma_f32_16x16x32_f16 on LDS fragments.  The fp16 row scale
 // s_R, the per-token exponent and the low-rank term (fp16 hi/lo Z against
 // exact INT8 A codes, one accumulator per part) are applied in the epilogue.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -173,15 +174,20 @@ constexpr int kT32CB = 8;  // 32-row vocabulary blocks per workgroup
 constexpr int kT32Slots = 4, kT32Dist = 2;
 constexpr int kT32HOps = 8, kT32WOps = 8;  // vector-memory operations per wave and stage
 constexpr int kT32Group = 4;  // token tiles that walk the vocabulary together
+constexpr int kEpiChunk = 4;  // low-rank rank steps whose loads are issued together
 constexpr int kXcds = 8;
 
 // s_waitcnt immediate: wait until at most n vector-memory operations of this
 // wave are outstanding (expcnt and lgkmcnt not waited on)
-constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
+__device__ constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+struct Acc4 {
+  f16x v[4];
+};
 
 struct T32Grid {
   int ntiles, ncb, ttiles, vtiles;
@@ -200,6 +206,8 @@ __host__ __device__ inline T32Grid t32_grid(const FwdArgs& a) {
 template <int GC>
 __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   __shared__ h8 sH[kT32Slots][kT32TT][4][64];
+  __shared__ float sTok[kT32TT * 32][2];  // hscale, zscale of the workgroup's tokens
+  __shared__ float sVoc[kT32CB * 32][3];  // s_R, s_Ac, s_Aw of its vocabulary rows
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -232,6 +240,18 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   const int tt0 = ttile * kT32TT;           // first 32-token tile
   const int cb0 = vt * kT32CB + wn * 4;     // first vocabulary block of this wave
   const int nS = (int)(a.D / 64);           // stages
+
+  // per-token and per-row scales of the epilogue, staged once; the first
+  // barrier of the main loop publishes them
+  {
+    const int64_t tok = std::min<int64_t>(32 * (int64_t)tt0 + tid, a.n32 - 1);
+    sTok[tid][0] = a.hscale[tok];
+    sTok[tid][1] = a.zscale[tok];
+    const int64_t v = std::min<int64_t>(32 * (int64_t)vt * kT32CB + tid, 16 * a.nb - 1);
+    sVoc[tid][0] = f16_to_f32(a.r_rowscale[v]);
+    sVoc[tid][1] = a.r_c > 0 ? f16_to_f32(a.a_scales[v * a.nA]) : 0.0f;
+    sVoc[tid][2] = a.r_r > 0 ? f16_to_f32(a.a_scales[v * a.nA + a.nA - 1]) : 0.0f;
+  }
 
   // H: wave w copies step w of the 8 token tiles; tiles past the last one are
   // zero-filled (only the last row of workgroups has any)
@@ -305,29 +325,36 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   // and W loads of stage ks, then those of stage ks+1; waiting down to the
   // last two batches completes stage ks.  The barrier then makes every wave's
   // copies of stage ks visible and retires all reads of the slot refilled next.
+  // The last two stages reload their own stage instead of prefetching, which
+  // keeps the count of operations in flight the same.
   auto stage = [&](int ks, auto WS_) {
     constexpr int ws = decltype(WS_)::value;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(kT32HOps + kT32WOps));
     __syncthreads();
-    load_h(ks + kT32Dist < nS ? ks + kT32Dist : nS - 1, (ks + kT32Dist) & (kT32Slots - 1));
+    const int kn = ks + kT32Dist < nS ? ks + kT32Dist : nS - 1;
+    load_h(kn, (ks + kT32Dist) & (kT32Slots - 1));
     const int hs = ks & (kT32Slots - 1);
+    // unpack the whole stage first so the W slot can be refilled at once
+    h8 bvs[4][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      h8 av[4], bv[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) av[m] = sH[hs][4 * wm + m][t][lane];
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const uint32_t code = GC == 2 ? (wc[ws][cb] >> (8 * t)) & 0xffu
                             : GC == 1 ? (wc[ws][cb] >> (8 * (t >> 1))) & 0xffu
                                       : wc[ws][cb] & 0xffu;
-        bv[cb] = unpack_q4_scaled(wr[ws][cb][t], (_Float16)(float)code);
+        bvs[t][cb] = unpack_q4_scaled(wr[ws][cb][t], (_Float16)(float)code);
       }
-      if (t == 3) load_w(ks + kT32Dist < nS ? ks + kT32Dist : nS - 1, ws);
+    load_w(kn, ws);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      h8 av[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) av[m] = sH[hs][4 * wm + m][t][lane];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[m][cb] = mfma32(av[m], bv[cb], acc[m][cb]);
+        for (int cb = 0; cb < 4; ++cb) acc[m][cb] = mfma32(av[m], bvs[t][cb], acc[m][cb]);
     }
   };
   for (int ks = 0; ks < nS; ks += 2) {  // nS is even (D is a multiple of 128)
@@ -336,79 +363,101 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  // epilogue: per token tile m the low-rank term (Z hi/lo against exact INT8
-  // A codes, 16 ranks per MFMA step), then scales and the store
   const int r = a.r_c + a.r_r;
   const int csteps = a.rc32 / 16, esteps = (a.rc32 + a.rr32) / 16;
-  const h8* zf = reinterpret_cast<const h8*>(a.zf) + lane;
+  // epilogue: per token tile m the low-rank term (Z hi/lo against exact INT8
+  // A codes, 16 ranks per MFMA step, each part in its own accumulators), then
+  // the scales and the store.
   float sR[4], sAc[4], sAw[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const float* sv = sVoc[32 * (4 * wn + cb) + c32];
+    sR[cb] = sv[0];
+    sAc[cb] = sv[1];
+    sAw[cb] = sv[2];
+  }
   const int8_t* arow[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
     int64_t v = 32 * (int64_t)CB + c32;
     if (v >= 16 * a.nb) v = 16 * a.nb - 1;
-    sR[cb] = f16_to_f32(a.r_rowscale[v]);
-    sAc[cb] = a.r_c > 0 ? f16_to_f32(a.a_scales[v * a.nA]) : 0.0f;
-    sAw[cb] = a.r_r > 0 ? f16_to_f32(a.a_scales[v * a.nA + a.nA - 1]) : 0.0f;
     arow[cb] = a.a_codes + v * r;
   }
+  // A codes of this lane's row in block cb for rank step s (zero past the part's rank)
+  auto a_code = [&](int cb, int s) {
+    const bool part_c = s < csteps;
+    const int col = 16 * (part_c ? s : s - csteps) + 8 * g;
+    u2 raw = {0u, 0u};
+    if (col < (part_c ? a.r_c : a.r_r)) raw = *reinterpret_cast<const u2*>(arow[cb] + (part_c ? 0 : a.r_c) + col);
+    return raw;
+  };
+  auto store_tile = [&](int m, const f16x (&am)[4], const Acc4& pc, const Acc4& pw) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int T = tt0 + 4 * wm + m;
-    if (T >= G.ntiles) continue;
-    // two vocabulary blocks at a time keep the low-rank accumulators to 64 VGPRs
+    for (int v = 0; v < 16; ++v) {
+      const int tl = 32 * (4 * wm + m) + 8 * (v >> 2) + 4 * g + (v & 3);  // token within the workgroup
+      const int64_t tok = 32 * (int64_t)tt0 + tl;
+      if (tok < a.N) {
+        const float hs = sTok[tl][0], zs = sTok[tl][1];
 #pragma unroll
-    for (int cp = 0; cp < 4; cp += 2) {
-      f16x pc[2], pw[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        pc[j] = f16x{};
-        pw[j] = f16x{};
-      }
-      for (int s = 0; s < esteps; ++s) {
-        const bool part_c = s < csteps;
-        const int col = 16 * (part_c ? s : s - csteps) + 8 * g;
-        const int rank = part_c ? a.r_c : a.r_r;
-        const int base = part_c ? 0 : a.r_c;
-        const h8 zh = zf[((int64_t)T * 2 * esteps + 2 * s) * 64];
-        const h8 zl = zf[((int64_t)T * 2 * esteps + 2 * s + 1) * 64];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u2 raw = {0u, 0u};
-          if (col < rank) raw = *reinterpret_cast<const u2*>(arow[cp + j] + base + col);
-          const h8 av = unpack_i8x8(raw[0], raw[1]);
-          if (part_c) {
-            pc[j] = mfma32(zh, av, pc[j]);
-            pc[j] = mfma32(zl, av, pc[j]);
-          } else {
-            pw[j] = mfma32(zh, av, pw[j]);
-            pw[j] = mfma32(zl, av, pw[j]);
-          }
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t tok = 32 * (int64_t)T + 8 * (v >> 2) + 4 * g + (v & 3);
-        if (tok < a.N) {
-          const float hs = a.hscale[tok], zs = a.zscale[tok];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int cb = cp + j;
-            const int64_t voc = 32 * (int64_t)(cb0 + cb) + c32;
-            if (cb0 + cb < G.ncb && voc < a.V) {
-              float y = hs * (sR[cb] * acc[m][cb][v]);
-              if (r > 0) y = fmaf(zs, fmaf(sAw[cb], pw[j][v], sAc[cb] * pc[j][v]), y);
-              if (a.y_bf16)
-                reinterpret_cast<uint16_t*>(a.Y)[tok * a.Y_stride + voc] = f32_to_bf16(y);
-              else
-                reinterpret_cast<float*>(a.Y)[tok * a.Y_stride + voc] = y;
-            }
+        for (int cb = 0; cb < 4; ++cb) {
+          const int64_t voc = 32 * (int64_t)(cb0 + cb) + c32;
+          if (cb0 + cb < G.ncb && voc < a.V) {
+            float y = hs * (sR[cb] * am[cb][v]);
+            if (r > 0) y = fmaf(zs, fmaf(sAw[cb], pw.v[cb][v], sAc[cb] * pc.v[cb][v]), y);
+            if (a.y_bf16)
+              reinterpret_cast<uint16_t*>(a.Y)[tok * a.Y_stride + voc] = f32_to_bf16(y);
+            else
+              reinterpret_cast<float*>(a.Y)[tok * a.Y_stride + voc] = y;
           }
         }
       }
     }
-  }
+  };
+
+  // the low-rank term in chunks of kEpiChunk rank steps, every load of a
+  // chunk issued before its MFMAs
+  const h8* zf = reinterpret_cast<const h8*>(a.zf) + lane;
+  auto low_rank_part = [&](int T, int s_begin, int s_end) {
+    Acc4 p;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) p.v[cb] = f16x{};
+    for (int s0 = s_begin; s0 < s_end; s0 += kEpiChunk) {
+      h8 zh[kEpiChunk], zl[kEpiChunk];
+      u2 ac[kEpiChunk][4];
+#pragma unroll
+      for (int j = 0; j < kEpiChunk; ++j) {
+        const int s = s0 + j;
+        const bool live = s < s_end;
+        const int64_t zi = ((int64_t)T * 2 * esteps + 2 * (live ? s : s_begin)) * 64;
+        zh[j] = live ? zf[zi] : h8{0, 0, 0, 0, 0, 0, 0, 0};
+        zl[j] = live ? zf[zi + 64] : h8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) ac[j][cb] = live ? a_code(cb, s) : u2{0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < kEpiChunk; ++j)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const h8 av = unpack_i8x8(ac[j][cb][0], ac[j][cb][1]);
+          p.v[cb] = mfma32(zh[j], av, p.v[cb]);
+          p.v[cb] = mfma32(zl[j], av, p.v[cb]);
+        }
+    }
+    return p;
+  };
+  auto tile = [&](auto M_) {
+    constexpr int m = decltype(M_)::value;
+    const int T = tt0 + 4 * wm + m;
+    if (T >= G.ntiles) return;
+    const Acc4 pc = low_rank_part(T, 0, csteps);
+    const Acc4 pw = low_rank_part(T, csteps, esteps);
+    store_tile(m, acc[m], pc, pw);
+  };
+  tile(std::integral_constant<int, 0>{});
+  tile(std::integral_constant<int, 1>{});
+  tile(std::integral_constant<int, 2>{});
+  tile(std::integral_constant<int, 3>{});
 }
 
 }  // namespace

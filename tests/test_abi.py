@@ -189,3 +189,17 @@ def test_status_strings(ah):
         assert s.startswith("ARCHEAD_")
         assert ah.STATUS[code] in s
     assert "unknown" in ah.archead_status_string(99)
+
+
+def test_every_kernel_has_its_host_launch_stub(ah):
+    """A kernel whose host-side instantiation is dropped leaves an undefined
+    launch stub behind, and the library then fails to load on a GPU machine."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", ah.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    stubs = [l for l in out.splitlines() if "device_stub" in l]
+    assert not stubs, stubs
+
