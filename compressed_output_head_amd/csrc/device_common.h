@@ -97,6 +97,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Four fp32 values as bf16 (round to nearest even, NaN stays NaN), packed in
+// order into two dwords (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ u2 pack_bf16x4(float a, float b, float c, float d) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 lo = {(__bf16)a, (__bf16)b}, hi = {(__bf16)c, (__bf16)d};
+  return u2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // Power-of-two exponent S that brings the largest magnitude m of a row into
 // [2^14, 2^15) (fp16 keeps every bf16 value of the row above 2^-17 * 2^(-S)
 // exact).  Rows that are all zero or not finite get S = 0.

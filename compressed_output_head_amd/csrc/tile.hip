@@ -171,10 +171,11 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const FwdArgs a) {
 constexpr int kT32Threads = 256;
 constexpr int kT32TT = 8;  // 32-token tiles per workgroup
 constexpr int kT32CB = 8;  // 32-row vocabulary blocks per workgroup
-constexpr int kT32Slots = 4, kT32Dist = 2;
+constexpr int kT32Dist = 2;  // stages of prefetch; the H ring has 4 slots
 constexpr int kT32HOps = 8, kT32WOps = 8;  // vector-memory operations per wave and stage
 constexpr int kT32Group = 4;  // token tiles that walk the vocabulary together
 constexpr int kEpiChunk = 4;  // low-rank rank steps whose loads are issued together
+constexpr int kEpiLdsSteps = 8;  // up to 128 padded ranks: Z of the workgroup fits the H ring
 constexpr int kXcds = 8;
 
 // s_waitcnt immediate: wait until at most n vector-memory operations of this
@@ -205,9 +206,12 @@ __host__ __device__ inline T32Grid t32_grid(const FwdArgs& a) {
 // 1 -> two (g = 64), 2 -> four (g = 32)
 template <int GC>
 __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
-  __shared__ h8 sH[kT32Slots][kT32TT][4][64];
+  // the H ring: one LDS array per slot, so the compiler can tell a slot being
+  // filled by buffer-to-LDS copies from the slot being read and does not wait
+  // for the copies before every read
+  __shared__ h8 sH[4][kT32TT][4][64];
   __shared__ float sTok[kT32TT * 32][2];  // hscale, zscale of the workgroup's tokens
-  __shared__ float sVoc[kT32CB * 32][3];  // s_R, s_Ac, s_Aw of its vocabulary rows
+  __shared__ __align__(16) float sVR[kT32CB * 32], sVC[kT32CB * 32], sVW[kT32CB * 32];  // s_R, s_Ac, s_Aw
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -248,30 +252,35 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     sTok[tid][0] = a.hscale[tok];
     sTok[tid][1] = a.zscale[tok];
     const int64_t v = std::min<int64_t>(32 * (int64_t)vt * kT32CB + tid, 16 * a.nb - 1);
-    sVoc[tid][0] = f16_to_f32(a.r_rowscale[v]);
-    sVoc[tid][1] = a.r_c > 0 ? f16_to_f32(a.a_scales[v * a.nA]) : 0.0f;
-    sVoc[tid][2] = a.r_r > 0 ? f16_to_f32(a.a_scales[v * a.nA + a.nA - 1]) : 0.0f;
+    sVR[tid] = f16_to_f32(a.r_rowscale[v]);
+    sVC[tid] = a.r_c > 0 ? f16_to_f32(a.a_scales[v * a.nA]) : 0.0f;
+    sVW[tid] = a.r_r > 0 ? f16_to_f32(a.a_scales[v * a.nA + a.nA - 1]) : 0.0f;
   }
 
-  // H: wave w copies step w of the 8 token tiles; tiles past the last one are
-  // zero-filled (only the last row of workgroups has any)
+  // H: wave w copies step w of the 8 token tiles.  Tiles past the last one
+  // re-read the last tile (their results are never stored), so every stage
+  // issues the same straight-line copies and the compiler's count of
+  // operations in flight stays exact.
   const __amdgpu_buffer_rsrc_t hrs = buffer_rsrc(a.hf, (uint32_t)(a.n32 * a.D * 2));
   const uint32_t lane16 = (uint32_t)lane * 16u;
   const uint32_t hT = (uint32_t)a.nkt * 8192u;  // bytes per token tile
+  uint32_t hoff[kT32TT];
+#pragma unroll
+  for (int i = 0; i < kT32TT; ++i)
+    hoff[i] = (uint32_t)(tt0 + i < G.ntiles ? tt0 + i : G.ntiles - 1) * hT + (uint32_t)wave * 1024u;
   const bool hfull = tt0 + kT32TT <= G.ntiles;
   auto load_h = [&](int ks, int slot) {
-    const uint32_t base = (uint32_t)ks * 4096u + (uint32_t)wave * 1024u;
     if (hfull) {
 #pragma unroll
       for (int i = 0; i < kT32TT; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][i][wave][0], 16, lane16,
-                                                 (uint32_t)(tt0 + i) * hT + base, 0, 0);
+                                                 hoff[i] + (uint32_t)ks * 4096u, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < kT32TT; ++i) {
         if (tt0 + i < G.ntiles)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][i][wave][0], 16, lane16,
-                                                   (uint32_t)(tt0 + i) * hT + base, 0, 0);
+                                                   hoff[i] + (uint32_t)ks * 4096u, 0, 0);
         else
           sH[slot][i][wave][lane] = h8{0, 0, 0, 0, 0, 0, 0, 0};
       }
@@ -316,24 +325,25 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[m][cb] = f16x{};
 
+  load_h(0, 0);
+  load_h(1, 1);  // nS >= 2
 #pragma unroll
-  for (int ks = 0; ks < kT32Dist; ++ks) load_h(ks < nS ? ks : nS - 1, ks);
-#pragma unroll
-  for (int ks = 0; ks < kT32Dist; ++ks) load_w(ks < nS ? ks : nS - 1, ks);
+  for (int ks = 0; ks < kT32Dist; ++ks) load_w(ks, ks);
 
-  // One stage.  On entry this wave has in flight, oldest first, the H copies
-  // and W loads of stage ks, then those of stage ks+1; waiting down to the
-  // last two batches completes stage ks.  The barrier then makes every wave's
-  // copies of stage ks visible and retires all reads of the slot refilled next.
-  // The last two stages reload their own stage instead of prefetching, which
-  // keeps the count of operations in flight the same.
-  auto stage = [&](int ks, auto WS_) {
-    constexpr int ws = decltype(WS_)::value;
+  // One stage; S = ks mod 4 picks the ring slots at compile time.  On entry
+  // this wave has in flight, oldest first, the H copies and W loads of stage
+  // ks, then those of stage ks+1; waiting down to the last two batches
+  // completes stage ks.  The barrier then makes every wave's copies of stage ks
+  // visible and retires all reads of the slot refilled next.  The last two
+  // stages reload their own stage instead of prefetching, which keeps the
+  // count of operations in flight the same.
+  auto stage = [&](int ks, auto S_) {
+    constexpr int S = decltype(S_)::value, ws = S & 1;
+    h8(&cur)[kT32TT][4][64] = sH[ks & 3];
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(kT32HOps + kT32WOps));
     __syncthreads();
     const int kn = ks + kT32Dist < nS ? ks + kT32Dist : nS - 1;
-    load_h(kn, (ks + kT32Dist) & (kT32Slots - 1));
-    const int hs = ks & (kT32Slots - 1);
+    load_h(kn, (ks + 2) & 3);
     // unpack the whole stage first so the W slot can be refilled at once
     h8 bvs[4][4];
 #pragma unroll
@@ -350,14 +360,21 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     for (int t = 0; t < 4; ++t) {
       h8 av[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) av[m] = sH[hs][4 * wm + m][t][lane];
+      for (int m = 0; m < 4; ++m) av[m] = cur[4 * wm + m][t][lane];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[m][cb] = mfma32(av[m], bvs[t][cb], acc[m][cb]);
+        for (int cb = 0; cb < 4; ++cb) acc[m][cb] = mfma32(bvs[t][cb], av[m], acc[m][cb]);
     }
   };
-  for (int ks = 0; ks < nS; ks += 2) {  // nS is even (D is a multiple of 128)
+  int ks = 0;
+  for (; ks + 4 <= nS; ks += 4) {
+    stage(ks, std::integral_constant<int, 0>{});
+    stage(ks + 1, std::integral_constant<int, 1>{});
+    stage(ks + 2, std::integral_constant<int, 2>{});
+    stage(ks + 3, std::integral_constant<int, 3>{});
+  }
+  if (ks < nS) {  // nS is even: two stages remain
     stage(ks, std::integral_constant<int, 0>{});
     stage(ks + 1, std::integral_constant<int, 1>{});
   }
@@ -365,17 +382,12 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 
   const int r = a.r_c + a.r_r;
   const int csteps = a.rc32 / 16, esteps = (a.rc32 + a.rr32) / 16;
-  // epilogue: per token tile m the low-rank term (Z hi/lo against exact INT8
-  // A codes, 16 ranks per MFMA step, each part in its own accumulators), then
-  // the scales and the store.
-  float sR[4], sAc[4], sAw[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const float* sv = sVoc[32 * (4 * wn + cb) + c32];
-    sR[cb] = sv[0];
-    sAc[cb] = sv[1];
-    sAw[cb] = sv[2];
-  }
+  // Epilogue.  Result tile (m, cb): element v of lane l is vocabulary row
+  // 32 CB + 8 (v/4) + 4 (l/32) + v%4 and token 32 T + l%32, so each lane holds
+  // runs of 4 consecutive logits of one token.  The low-rank term (Z hi/lo
+  // against exact INT8 A codes, 16 ranks per MFMA step, one accumulator per
+  // part) is added with the scales, and each run is stored at once.
+  const bool vec = ((uintptr_t)a.Y & 15) == 0 && (a.Y_stride & 3) == 0;
   const int8_t* arow[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
@@ -392,31 +404,112 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     if (col < (part_c ? a.r_c : a.r_r)) raw = *reinterpret_cast<const u2*>(arow[cb] + (part_c ? 0 : a.r_c) + col);
     return raw;
   };
-  auto store_tile = [&](int m, const f16x (&am)[4], const Acc4& pc, const Acc4& pw) {
+  auto store = [&](int m, int cb, const f16x& am, const f16x& pc, const f16x& pw) {
+    const int tl = 32 * (4 * wm + m) + c32;  // token within the workgroup
+    const int64_t tok = 32 * (int64_t)tt0 + tl;
+    if (tok >= a.N || cb0 + cb >= G.ncb) return;
+    const float hs = sTok[tl][0], zs = sTok[tl][1];
+    const int64_t row = tok * a.Y_stride;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tl = 32 * (4 * wm + m) + 8 * (v >> 2) + 4 * g + (v & 3);  // token within the workgroup
-      const int64_t tok = 32 * (int64_t)tt0 + tl;
-      if (tok < a.N) {
-        const float hs = sTok[tl][0], zs = sTok[tl][1];
+    for (int vg = 0; vg < 4; ++vg) {
+      const int lr = 32 * (4 * wn + cb) + 8 * vg + 4 * g;  // vocabulary row within the workgroup
+      const int64_t voc0 = 32 * (int64_t)vt * kT32CB + lr;
+      const f4 sr = *reinterpret_cast<const f4*>(&sVR[lr]);
+      const f4 sc = *reinterpret_cast<const f4*>(&sVC[lr]);
+      const f4 sw = *reinterpret_cast<const f4*>(&sVW[lr]);
+      float y[4];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const int64_t voc = 32 * (int64_t)(cb0 + cb) + c32;
-          if (cb0 + cb < G.ncb && voc < a.V) {
-            float y = hs * (sR[cb] * am[cb][v]);
-            if (r > 0) y = fmaf(zs, fmaf(sAw[cb], pw.v[cb][v], sAc[cb] * pc.v[cb][v]), y);
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * vg + e;
+        y[e] = hs * (sr[e] * am[v]);
+        if (r > 0) y[e] = fmaf(zs, fmaf(sw[e], pw[v], sc[e] * pc[v]), y[e]);
+      }
+      if (vec && voc0 + 3 < a.V) {
+        if (a.y_bf16)
+          *reinterpret_cast<u2*>(reinterpret_cast<uint16_t*>(a.Y) + row + voc0) = pack_bf16x4(y[0], y[1], y[2], y[3]);
+        else
+          *reinterpret_cast<f4*>(reinterpret_cast<float*>(a.Y) + row + voc0) = f4{y[0], y[1], y[2], y[3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (voc0 + e < a.V) {
             if (a.y_bf16)
-              reinterpret_cast<uint16_t*>(a.Y)[tok * a.Y_stride + voc] = f32_to_bf16(y);
+              reinterpret_cast<uint16_t*>(a.Y)[row + voc0 + e] = f32_to_bf16(y[e]);
             else
-              reinterpret_cast<float*>(a.Y)[tok * a.Y_stride + voc] = y;
+              reinterpret_cast<float*>(a.Y)[row + voc0 + e] = y[e];
           }
         }
       }
     }
   };
 
-  // the low-rank term in chunks of kEpiChunk rank steps, every load of a
-  // chunk issued before its MFMAs
+  if (esteps <= kEpiLdsSteps) {
+    // Z of the workgroup's 8 token tiles (16 KB per 16 ranks) into the idle
+    // H ring and all A codes of this lane into registers: one round trip
+    __syncthreads();  // every wave is done reading the ring
+    const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(a.zf, (uint32_t)(a.n32 * (a.rc32 + a.rr32) * 4));
+    const int zper = 2 * esteps;  // 1 KB fragments per token tile
+    for (int f = wave; f < kT32TT * zper; f += 4) {
+      const int tt = f / zper, rem = f - tt * zper;
+      const int T = tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1;  // padding tiles are never stored
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, &sH[f >> 5][(f & 31) >> 2][f & 3][0], 16, lane16,
+                                               (uint32_t)(T * zper + rem) * 1024u, 0, 0);
+    }
+    u2 ac[4][kEpiLdsSteps];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int s = 0; s < kEpiLdsSteps; ++s) ac[cb][s] = s < esteps ? a_code(cb, s) : u2{0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto tile_pair = [&](auto M_, auto P_) {
+      constexpr int m = decltype(M_)::value, cp = 2 * decltype(P_)::value;
+      if (tt0 + 4 * wm + m >= G.ntiles) return;
+      const int f0 = (4 * wm + m) * zper;
+      f16x pc[2], pw[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        pc[j] = f16x{};
+        pw[j] = f16x{};
+      }
+#pragma unroll
+      for (int s = 0; s < kEpiLdsSteps; ++s) {
+        if (s < esteps) {
+          const int fh = f0 + 2 * s, fl = fh + 1;
+          const h8 zh = sH[fh >> 5][(fh & 31) >> 2][fh & 3][lane];
+          const h8 zl = sH[fl >> 5][(fl & 31) >> 2][fl & 3][lane];
+          h8 av[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) av[j] = unpack_i8x8(ac[cp + j][s][0], ac[cp + j][s][1]);
+          if (s < csteps) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) pc[j] = mfma32(av[j], zh, pc[j]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) pc[j] = mfma32(av[j], zl, pc[j]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) pw[j] = mfma32(av[j], zh, pw[j]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) pw[j] = mfma32(av[j], zl, pw[j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) store(m, cp + j, acc[m][cp + j], pc[j], pw[j]);
+    };
+    tile_pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    tile_pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+    tile_pair(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    tile_pair(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    tile_pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{});
+    tile_pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+    tile_pair(std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{});
+    tile_pair(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
+    return;
+  }
+
+  // more ranks: chunks of kEpiChunk rank steps, every load of a chunk issued
+  // before its MFMAs
   const h8* zf = reinterpret_cast<const h8*>(a.zf) + lane;
   auto low_rank_part = [&](int T, int s_begin, int s_end) {
     Acc4 p;
@@ -440,8 +533,8 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const h8 av = unpack_i8x8(ac[j][cb][0], ac[j][cb][1]);
-          p.v[cb] = mfma32(zh[j], av, p.v[cb]);
-          p.v[cb] = mfma32(zl[j], av, p.v[cb]);
+          p.v[cb] = mfma32(av, zh[j], p.v[cb]);
+          p.v[cb] = mfma32(av, zl[j], p.v[cb]);
         }
     }
     return p;
@@ -452,7 +545,8 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     if (T >= G.ntiles) return;
     const Acc4 pc = low_rank_part(T, 0, csteps);
     const Acc4 pw = low_rank_part(T, csteps, esteps);
-    store_tile(m, acc[m], pc, pw);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) store(m, cb, acc[m][cb], pc.v[cb], pw.v[cb]);
   };
   tile(std::integral_constant<int, 0>{});
   tile(std::integral_constant<int, 1>{});
