@@ -36,6 +36,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 KERNEL_SOURCES = {
     "decode_lds_kernel": ["decode.hip", "device_common.h", "internal.h"],
     "decode_kernel": ["decode.hip", "device_common.h", "internal.h"],
+    "mid_kernel": ["mid.hip", "device_common.h", "internal.h"],
     "tile_kernel": ["tile.hip", "device_common.h", "internal.h"],
     "tile32_kernel": ["tile.hip", "device_common.h", "internal.h"],
 }
@@ -144,9 +145,7 @@ def dominant_kernel(N):
     if N <= 16:
         return "decode_lds_kernel"
     if N <= 64:
-        return "decode_kernel"
-    if N <= 128:
-        return "tile_kernel"
+        return "mid_kernel"
     return "tile32_kernel"
 
 

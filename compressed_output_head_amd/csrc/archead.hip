@@ -301,11 +301,18 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
   const bool decode = path == ARCHEAD_PATH_DECODE || (path == ARCHEAD_PATH_AUTO && N <= kDecodeMaxTokens);
+  // decode path: the LDS kernel for a few tokens, else the batched kernel
+  // (the 16-row decode kernel only when offsets exceed 32 bits); tile path: the
+  // 32-row kernel unless offsets exceed 32 bits (launch_tile decides the same way)
   const bool small = decode && decode_lds_eligible(a);
-  const bool rows32 = !decode && tile32_eligible(a);  // launch_tile picks the same kernel
+  const bool mid = decode && !small && mid_eligible(a);
+  const bool rows32 = mid || (!decode && tile32_eligible(a));
   if ((small ? launch_prep_z(a, s) : launch_prep(a, rows32, s)) != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return ARCHEAD_E_HIP;
-  const hipError_t e = small ? launch_decode_lds(a, s) : decode ? launch_decode(a, s) : launch_tile(a, s);
+  const hipError_t e = small ? launch_decode_lds(a, s)
+                       : mid ? launch_mid(a, s)
+                       : decode ? launch_decode(a, s)
+                                : launch_tile(a, s);
   if (e != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
   return ARCHEAD_OK;

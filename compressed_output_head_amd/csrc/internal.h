@@ -74,6 +74,8 @@ hipError_t launch_prep_z(const FwdArgs& a, hipStream_t s);
 bool decode_lds_eligible(const FwdArgs& a);
 hipError_t launch_decode_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
+bool mid_eligible(const FwdArgs& a);
+hipError_t launch_mid(const FwdArgs& a, hipStream_t s);
 hipError_t launch_tile(const FwdArgs& a, hipStream_t s);
 
 }  // namespace archead

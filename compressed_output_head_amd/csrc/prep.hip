@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const FwdArgs a) {
   const int F = row_exponent(mz);
   if (tid == 0) a.zscale[n] = real ? ldexpf(1.0f, -F) : 0.0f;
   // 16-row layout: fragments of 32 ranks, lane 16 q + i holds ranks 8 q ..;
-  // 32-row layout: fragments of 16 ranks, lane 32 q + i holds ranks 8 q ..
+  // 32-row layout: fragments of 16 ranks, lane 32 q + i (order below)
   constexpr int kRanks = ROWS32 ? 16 : 32, kQ = ROWS32 ? 2 : 4, kRows = ROWS32 ? 32 : 16;
   const int csteps = a.rc32 / kRanks, nsteps = (a.rc32 + a.rr32) / kRanks;
   for (int e = tid; e < nsteps * kQ; e += kPrepThreads) {
@@ -158,7 +158,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const FwdArgs a) {
     h8 hi, lo;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const int col = kRanks * sl + 8 * q + k_order_z(jj);
+      // 32-row layout: steps come in pairs; lane half q of the pair (2j, 2j+1)
+      // holds ranks 32 j + 16 q + 8 (s & 1) .., so one 16-byte load of A codes
+      // feeds both steps of a pair
+      const int col = ROWS32 ? 32 * (sl >> 1) + 16 * q + 8 * (sl & 1) + k_order_z(jj)
+                             : kRanks * sl + 8 * q + k_order_z(jj);
       float z = 0.0f;
       if (real && col < rank) z = ldexpf(zrow[base + col], F);
       const _Float16 zh = (_Float16)z;

@@ -399,7 +399,8 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   // A codes of this lane's row in block cb for rank step s (zero past the part's rank)
   auto a_code = [&](int cb, int s) {
     const bool part_c = s < csteps;
-    const int col = 16 * (part_c ? s : s - csteps) + 8 * g;
+    const int sl = part_c ? s : s - csteps;
+    const int col = 32 * (sl >> 1) + 16 * g + 8 * (sl & 1);  // rank order of the 32-row Z layout
     u2 raw = {0u, 0u};
     if (col < (part_c ? a.r_c : a.r_r)) raw = *reinterpret_cast<const u2*>(arow[cb] + (part_c ? 0 : a.r_c) + col);
     return raw;
