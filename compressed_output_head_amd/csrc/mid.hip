@@ -276,8 +276,9 @@ __global__ __launch_bounds__(kMidThreads) void mid_kernel(const FwdArgs a) {
       // residual k-tiles 2 cj + h: step t covers runs R = 4 (t % 4) + 2 (t / 4) + lane / 32
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        if (2 * cj + h >= M.nkt) break;  // odd k-tile count
-        const uint32_t codes = h == 0 ? w.x0 : w.x1;
+        // a k-tile past an odd count gets group code 0, so it adds exact zeros
+        // (branching around it would make the accumulators change registers)
+        const uint32_t codes = 2 * cj + h < M.nkt ? (h == 0 ? w.x0 : w.x1) : 0u;
         h8 bv[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -296,21 +297,23 @@ __global__ __launch_bounds__(kMidThreads) void mid_kernel(const FwdArgs a) {
       const int lb = cj - M.rst;
       keep_ac = w.x0;
       keep_aw = w.x1;
+      // every step feeds both parts, with the other part's codes zeroed:
+      // branching per step would make the accumulators change registers
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const u4 pr = w.w[i >> 1];
         const bool on = (w.mask >> i) & 1u;  // bit 2 (i / 2) + i % 2
-        const h8 bv = unpack_i8x8(on ? pr[2 * (i & 1)] : 0u, on ? pr[2 * (i & 1) + 1] : 0u);
-        if (8 * lb + i < M.csteps) {
+        const bool in_c = 8 * lb + i < M.csteps;
+        const uint32_t lo = on ? pr[2 * (i & 1)] : 0u, hi = on ? pr[2 * (i & 1) + 1] : 0u;
+        const h8 bc = unpack_i8x8(in_c ? lo : 0u, in_c ? hi : 0u);
+        const h8 bw = unpack_i8x8(in_c ? 0u : lo, in_c ? 0u : hi);
 #pragma unroll
-          for (int m = 0; m < NT; ++m) pc[m] = mfma32(cur[m][2 * i][lane], bv, pc[m]);
-#pragma unroll
-          for (int m = 0; m < NT; ++m) pc[m] = mfma32(cur[m][2 * i + 1][lane], bv, pc[m]);
-        } else {
-#pragma unroll
-          for (int m = 0; m < NT; ++m) pw[m] = mfma32(cur[m][2 * i][lane], bv, pw[m]);
-#pragma unroll
-          for (int m = 0; m < NT; ++m) pw[m] = mfma32(cur[m][2 * i + 1][lane], bv, pw[m]);
+        for (int m = 0; m < NT; ++m) {
+          const h8 zh = cur[m][2 * i][lane], zl = cur[m][2 * i + 1][lane];
+          pc[m] = mfma32(zh, bc, pc[m]);
+          pw[m] = mfma32(zh, bw, pw[m]);
+          pc[m] = mfma32(zl, bc, pc[m]);
+          pw[m] = mfma32(zl, bw, pw[m]);
         }
       }
     }

@@ -168,13 +168,21 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const FwdArgs a) {
 //     R = 4 t + 2 h + l/32, the order the prep kernel gives H.
 // Every global read goes through a buffer resource: a wave-uniform offset plus
 // a small per-lane one, so no 64-bit per-lane address stays live.
-constexpr int kT32Threads = 256;
 constexpr int kT32TT = 8;  // 32-token tiles per workgroup
 constexpr int kT32CB = 8;  // 32-row vocabulary blocks per workgroup
+#ifndef ARCHEAD_T32_WN
+#define ARCHEAD_T32_WN 4
+#endif
+constexpr int kT32WN = ARCHEAD_T32_WN;       // waves along the vocabulary
+constexpr int kT32WM = 2;                    // waves along the tokens (4 token tiles each)
+constexpr int kT32Waves = kT32WM * kT32WN;
+constexpr int kT32Threads = 64 * kT32Waves;
+constexpr int kT32WCB = kT32CB / kT32WN;     // vocabulary blocks per wave
 constexpr int kT32Dist = 2;  // stages of prefetch; the H ring has 4 slots
-constexpr int kT32HOps = 8, kT32WOps = 8;  // vector-memory operations per wave and stage
+constexpr int kT32HOps = kT32TT * 4 / kT32Waves;  // H copies per wave and stage
+constexpr int kT32WOps = 2 * kT32WCB;            // code loads per wave and stage
 constexpr int kT32Group = 4;  // token tiles that walk the vocabulary together
-constexpr int kEpiChunk = 4;  // low-rank rank steps whose loads are issued together
+constexpr int kEpiChunk = kT32WCB >= 4 ? 4 : 2;  // low-rank rank steps whose loads are issued together
 constexpr int kEpiLdsSteps = 8;  // up to 128 padded ranks: Z of the workgroup fits the H ring
 constexpr int kXcds = 8;
 
@@ -186,8 +194,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-struct Acc4 {
-  f16x v[4];
+struct Acc4 {  // low-rank accumulators of one wave's vocabulary blocks
+  f16x v[kT32WCB];
 };
 
 struct T32Grid {
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   __shared__ __align__(16) float sVR[kT32CB * 32], sVC[kT32CB * 32], sVW[kT32CB * 32];  // s_R, s_Ac, s_Aw
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kT32WN, wn = wave % kT32WN;
   const int g = lane >> 5, c32 = lane & 31;
   const T32Grid G = t32_grid(a);
 
@@ -242,12 +250,12 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     }
   }
   const int tt0 = ttile * kT32TT;           // first 32-token tile
-  const int cb0 = vt * kT32CB + wn * 4;     // first vocabulary block of this wave
+  const int cb0 = vt * kT32CB + wn * kT32WCB;  // first vocabulary block of this wave
   const int nS = (int)(a.D / 64);           // stages
 
   // per-token and per-row scales of the epilogue, staged once; the first
   // barrier of the main loop publishes them
-  {
+  if (tid < kT32TT * 32) {
     const int64_t tok = std::min<int64_t>(32 * (int64_t)tt0 + tid, a.n32 - 1);
     sTok[tid][0] = a.hscale[tok];
     sTok[tid][1] = a.zscale[tok];
@@ -257,32 +265,37 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     sVW[tid] = a.r_r > 0 ? f16_to_f32(a.a_scales[v * a.nA + a.nA - 1]) : 0.0f;
   }
 
-  // H: wave w copies step w of the 8 token tiles.  Tiles past the last one
-  // re-read the last tile (their results are never stored), so every stage
-  // issues the same straight-line copies and the compiler's count of
-  // operations in flight stays exact.
+  // H: the 32 fragments of a stage (8 token tiles x 4 MFMA steps) are spread
+  // over the waves, fragment f = kT32Waves i + wave being token tile f / 4,
+  // step f % 4.  Tiles past the last one are zero-filled (only the last row
+  // of workgroups has any).
   const __amdgpu_buffer_rsrc_t hrs = buffer_rsrc(a.hf, (uint32_t)(a.n32 * a.D * 2));
   const uint32_t lane16 = (uint32_t)lane * 16u;
   const uint32_t hT = (uint32_t)a.nkt * 8192u;  // bytes per token tile
-  uint32_t hoff[kT32TT];
+  uint32_t hoff[kT32HOps];
 #pragma unroll
-  for (int i = 0; i < kT32TT; ++i)
-    hoff[i] = (uint32_t)(tt0 + i < G.ntiles ? tt0 + i : G.ntiles - 1) * hT + (uint32_t)wave * 1024u;
+  for (int i = 0; i < kT32HOps; ++i) {
+    const int f = kT32Waves * i + wave, tt = f >> 2;
+    hoff[i] = (uint32_t)(tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1) * hT + (uint32_t)(f & 3) * 1024u;
+  }
   const bool hfull = tt0 + kT32TT <= G.ntiles;
   auto load_h = [&](int ks, int slot) {
     if (hfull) {
 #pragma unroll
-      for (int i = 0; i < kT32TT; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][i][wave][0], 16, lane16,
+      for (int i = 0; i < kT32HOps; ++i) {
+        const int f = kT32Waves * i + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][f >> 2][f & 3][0], 16, lane16,
                                                  hoff[i] + (uint32_t)ks * 4096u, 0, 0);
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < kT32TT; ++i) {
-        if (tt0 + i < G.ntiles)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][i][wave][0], 16, lane16,
+      for (int i = 0; i < kT32HOps; ++i) {
+        const int f = kT32Waves * i + wave;
+        if (tt0 + (f >> 2) < G.ntiles)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][f >> 2][f & 3][0], 16, lane16,
                                                    hoff[i] + (uint32_t)ks * 4096u, 0, 0);
         else
-          sH[slot][i][wave][lane] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+          sH[slot][f >> 2][f & 3][lane] = h8{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
   };
@@ -293,22 +306,22 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(a.r_gcodes, (uint32_t)(a.nb * 16 * a.ng));
   const uint32_t tstride = (uint32_t)a.nb * 1024u;
   const int lg = __builtin_ctz((unsigned)a.g);
-  uint32_t wvoff[4], cvoff[4];
+  uint32_t wvoff[kT32WCB], cvoff[kT32WCB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < kT32WCB; ++cb) {
     const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
     int b = 2 * CB + ((lane >> 4) & 1);
     if (b >= a.nb) b = (int)a.nb - 1;
     wvoff[cb] = (uint32_t)b * 1024u + (uint32_t)(lane & 15) * 16u + (uint32_t)g * 256u;
     cvoff[cb] = ((uint32_t)b * 16u + (uint32_t)(lane & 15)) * (uint32_t)a.ng;
   }
-  u4 wr[kT32Dist][4];
-  uint32_t wc[kT32Dist][4];
+  u4 wr[kT32Dist][kT32WCB];
+  uint32_t wc[kT32Dist][kT32WCB];
   auto load_w = [&](int ks, int slot) {
     const int kt = ks >> 1, half = ks & 1;
     const uint32_t soff = (uint32_t)kt * tstride + 512u * (uint32_t)half;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kT32WCB; ++cb) {
       wr[slot][cb] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff[cb], soff, 0));
       if constexpr (GC == 2)
         wc[slot][cb] = __builtin_amdgcn_raw_buffer_load_b32(crs, cvoff[cb], 4u * (uint32_t)kt, 0);
@@ -319,11 +332,11 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     }
   };
 
-  f16x acc[4][4];
+  f16x acc[4][kT32WCB];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[m][cb] = f16x{};
+    for (int cb = 0; cb < kT32WCB; ++cb) acc[m][cb] = f16x{};
 
   load_h(0, 0);
   load_h(1, 1);  // nS >= 2
@@ -345,11 +358,11 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     const int kn = ks + kT32Dist < nS ? ks + kT32Dist : nS - 1;
     load_h(kn, (ks + 2) & 3);
     // unpack the whole stage first so the W slot can be refilled at once
-    h8 bvs[4][4];
+    h8 bvs[4][kT32WCB];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < kT32WCB; ++cb) {
         const uint32_t code = GC == 2 ? (wc[ws][cb] >> (8 * t)) & 0xffu
                             : GC == 1 ? (wc[ws][cb] >> (8 * (t >> 1))) & 0xffu
                                       : wc[ws][cb] & 0xffu;
@@ -364,7 +377,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[m][cb] = mfma32(bvs[t][cb], av[m], acc[m][cb]);
+        for (int cb = 0; cb < kT32WCB; ++cb) acc[m][cb] = mfma32(bvs[t][cb], av[m], acc[m][cb]);
     }
   };
   int ks = 0;
@@ -388,9 +401,9 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   // against exact INT8 A codes, 16 ranks per MFMA step, one accumulator per
   // part) is added with the scales, and each run is stored at once.
   const bool vec = ((uintptr_t)a.Y & 15) == 0 && (a.Y_stride & 3) == 0;
-  const int8_t* arow[4];
+  const int8_t* arow[kT32WCB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < kT32WCB; ++cb) {
     const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
     int64_t v = 32 * (int64_t)CB + c32;
     if (v >= 16 * a.nb) v = 16 * a.nb - 1;
@@ -413,7 +426,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     const int64_t row = tok * a.Y_stride;
 #pragma unroll
     for (int vg = 0; vg < 4; ++vg) {
-      const int lr = 32 * (4 * wn + cb) + 8 * vg + 4 * g;  // vocabulary row within the workgroup
+      const int lr = 32 * (kT32WCB * wn + cb) + 8 * vg + 4 * g;  // vocabulary row within the workgroup
       const int64_t voc0 = 32 * (int64_t)vt * kT32CB + lr;
       const f4 sr = *reinterpret_cast<const f4*>(&sVR[lr]);
       const f4 sc = *reinterpret_cast<const f4*>(&sVC[lr]);
@@ -450,26 +463,29 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     __syncthreads();  // every wave is done reading the ring
     const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(a.zf, (uint32_t)(a.n32 * (a.rc32 + a.rr32) * 4));
     const int zper = 2 * esteps;  // 1 KB fragments per token tile
-    for (int f = wave; f < kT32TT * zper; f += 4) {
+    for (int f = wave; f < kT32TT * zper; f += kT32Waves) {
       const int tt = f / zper, rem = f - tt * zper;
       const int T = tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1;  // padding tiles are never stored
       __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, &sH[f >> 5][(f & 31) >> 2][f & 3][0], 16, lane16,
                                                (uint32_t)(T * zper + rem) * 1024u, 0, 0);
     }
-    u2 ac[4][kEpiLdsSteps];
+    u2 ac[kT32WCB][kEpiLdsSteps];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < kT32WCB; ++cb)
 #pragma unroll
       for (int s = 0; s < kEpiLdsSteps; ++s) ac[cb][s] = s < esteps ? a_code(cb, s) : u2{0u, 0u};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // kEpiBlocks vocabulary blocks at a time: with 8 waves per workgroup the
+    // registers only hold one block's low-rank accumulators next to the tile's
+    constexpr int kEpiBlocks = kT32WCB >= 4 ? 2 : 1;
     auto tile_pair = [&](auto M_, auto P_) {
-      constexpr int m = decltype(M_)::value, cp = 2 * decltype(P_)::value;
+      constexpr int m = decltype(M_)::value, cp = kEpiBlocks * decltype(P_)::value;
       if (tt0 + 4 * wm + m >= G.ntiles) return;
       const int f0 = (4 * wm + m) * zper;
-      f16x pc[2], pw[2];
+      f16x pc[kEpiBlocks], pw[kEpiBlocks];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kEpiBlocks; ++j) {
         pc[j] = f16x{};
         pw[j] = f16x{};
       }
@@ -479,33 +495,33 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
           const int fh = f0 + 2 * s, fl = fh + 1;
           const h8 zh = sH[fh >> 5][(fh & 31) >> 2][fh & 3][lane];
           const h8 zl = sH[fl >> 5][(fl & 31) >> 2][fl & 3][lane];
-          h8 av[2];
+          h8 av[kEpiBlocks];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) av[j] = unpack_i8x8(ac[cp + j][s][0], ac[cp + j][s][1]);
+          for (int j = 0; j < kEpiBlocks; ++j) av[j] = unpack_i8x8(ac[cp + j][s][0], ac[cp + j][s][1]);
           if (s < csteps) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) pc[j] = mfma32(av[j], zh, pc[j]);
+            for (int j = 0; j < kEpiBlocks; ++j) pc[j] = mfma32(av[j], zh, pc[j]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) pc[j] = mfma32(av[j], zl, pc[j]);
+            for (int j = 0; j < kEpiBlocks; ++j) pc[j] = mfma32(av[j], zl, pc[j]);
           } else {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) pw[j] = mfma32(av[j], zh, pw[j]);
+            for (int j = 0; j < kEpiBlocks; ++j) pw[j] = mfma32(av[j], zh, pw[j]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) pw[j] = mfma32(av[j], zl, pw[j]);
+            for (int j = 0; j < kEpiBlocks; ++j) pw[j] = mfma32(av[j], zl, pw[j]);
           }
         }
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) store(m, cp + j, acc[m][cp + j], pc[j], pw[j]);
+      for (int j = 0; j < kEpiBlocks; ++j) store(m, cp + j, acc[m][cp + j], pc[j], pw[j]);
     };
-    tile_pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    tile_pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-    tile_pair(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
-    tile_pair(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-    tile_pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{});
-    tile_pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
-    tile_pair(std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{});
-    tile_pair(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
+    auto tile_pairs = [&](auto M_) {
+      tile_pair(M_, std::integral_constant<int, 0>{});
+      tile_pair(M_, std::integral_constant<int, 1>{});  // kT32WCB == 2 * kEpiBlocks
+    };
+    tile_pairs(std::integral_constant<int, 0>{});
+    tile_pairs(std::integral_constant<int, 1>{});
+    tile_pairs(std::integral_constant<int, 2>{});
+    tile_pairs(std::integral_constant<int, 3>{});
     return;
   }
 
@@ -515,7 +531,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   auto low_rank_part = [&](int T, int s_begin, int s_end) {
     Acc4 p;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) p.v[cb] = f16x{};
+    for (int cb = 0; cb < kT32WCB; ++cb) p.v[cb] = f16x{};
     for (int s0 = s_begin; s0 < s_end; s0 += kEpiChunk) {
       h8 zh[kEpiChunk], zl[kEpiChunk];
       u2 ac[kEpiChunk][4];
@@ -527,12 +543,12 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
         zh[j] = live ? zf[zi] : h8{0, 0, 0, 0, 0, 0, 0, 0};
         zl[j] = live ? zf[zi + 64] : h8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) ac[j][cb] = live ? a_code(cb, s) : u2{0u, 0u};
+        for (int cb = 0; cb < kT32WCB; ++cb) ac[j][cb] = live ? a_code(cb, s) : u2{0u, 0u};
       }
 #pragma unroll
       for (int j = 0; j < kEpiChunk; ++j)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < kT32WCB; ++cb) {
           const h8 av = unpack_i8x8(ac[j][cb][0], ac[j][cb][1]);
           p.v[cb] = mfma32(av, zh[j], p.v[cb]);
           p.v[cb] = mfma32(av, zl[j], p.v[cb]);
@@ -547,7 +563,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     const Acc4 pc = low_rank_part(T, 0, csteps);
     const Acc4 pw = low_rank_part(T, csteps, esteps);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) store(m, cb, acc[m][cb], pc.v[cb], pw.v[cb]);
+    for (int cb = 0; cb < kT32WCB; ++cb) store(m, cb, acc[m][cb], pc.v[cb], pw.v[cb]);
   };
   tile(std::integral_constant<int, 0>{});
   tile(std::integral_constant<int, 1>{});
