@@ -198,10 +198,18 @@ def run_workload(name, steps, warmup, path=0):
                 kernel_ms_min=float(np.min(kms)), kernel_ms_max=float(np.max(kms)))
 
 
+def tile_workload(N):
+    """Workloads of more than 64 tokens run the MFMA tile kernel and are
+    reported in TFLOP/s against the MFMA peak; smaller ones in GB/s of packed
+    head bytes against the HBM peak."""
+    return N > 64
+
+
 def cpu_baseline(name, sample_rows, min_seconds=10.0):
     """The oracle as it stands, timed on a bounded sample of the workload:
     the first ``sample_rows`` vocabulary rows, repeated until at least
-    ``min_seconds`` of host time have passed."""
+    ``min_seconds`` of host time have passed.  Reported in the workload's own
+    unit: GB/s of packed bytes of those rows, or TFLOP/s of their logits."""
     import synth
     import oracle
     try:
@@ -219,11 +227,17 @@ def cpu_baseline(name, sample_rows, min_seconds=10.0):
         if time.time() - t0 >= min_seconds:
             break
     dt = time.time() - t0
+    what = (f"fp64 oracle (unpack, rebuild W_hat, H W_hat^T) on vocabulary rows 0..{cols.size - 1} "
+            f"of the {name} workload, {reps} passes in {dt:.1f}s; ")
+    if tile_workload(cfg["N"]):
+        r = cfg["r_c"] + cfg["r_r"]
+        flops = 2 * cfg["N"] * cols.size * (cfg["D"] + r) * reps
+        return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                    sample=what + "TFLOP/s of the logits of those rows (2 N (D + r_c + r_r) per logit)")
     L = oracle.layout(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"])
     sample_bytes = L["payload_bytes"] * cols.size / cfg["V"] * reps
     return dict(value=round(sample_bytes / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"fp64 oracle (unpack, rebuild W_hat, H W_hat^T) on vocabulary rows 0..{cols.size - 1} "
-                       f"of the {name} workload, {reps} passes in {dt:.1f}s; GB/s of packed bytes of those rows")
+                sample=what + "GB/s of packed bytes of those rows")
 
 
 def roofline_decode(r):
@@ -244,14 +258,25 @@ def roofline_tile(r):
             "algorithmic_flops_per_launch": A["main_flops"]}
 
 
+def summary(r):
+    """(value, unit, roofline) of one workload run: whole-call throughput in
+    the workload's unit, and the dominant kernel against its roofline."""
+    A = r["A"]
+    if tile_workload(r["cfg"]["N"]):
+        return round(A["total_flops"] / (r["ms"] / 1e3) / 1e12, 2), "TFLOP/s", roofline_tile(r)
+    return round(A["payload"] / (r["ms"] / 1e3) / 1e9, 1), "GB/s", roofline_decode(r)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode", help="headline workload (decode or batched)")
+    ap.add_argument("--config", default="decode", help="headline workload (decode, batched, prefill, head70b)")
     ap.add_argument("--secondary", default="prefill", help="second workload ('' to skip)")
-    ap.add_argument("--cpu-sample-rows", type=int, default=151936)
+    ap.add_argument("--cpu-sample-rows", type=int, default=None,
+                    help="vocabulary rows the CPU oracle is timed on (default: all for decode-type "
+                         "workloads, 4096 for tile-type ones)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run the device copies that calibrate HBM byte counters")
@@ -283,12 +308,12 @@ def main():
         copy_calibration()
     r = run_workload(args.config, args.steps, args.warmup)
     cfg, A = r["cfg"], r["A"]
-    value = A["payload"] / (r["ms"] / 1e3) / 1e9
-    log(f"[bench] {args.config}: {r['ms'] * 1e3:.1f} us/step, decode kernel {r['kernel_ms'] * 1e3:.1f} us")
+    value, unit, roof = summary(r)
+    log(f"[bench] {args.config}: {r['ms'] * 1e3:.1f} us/step, {r['kernel']} {r['kernel_ms'] * 1e3:.1f} us")
     out = {
         "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
+        "value": value,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -301,22 +326,24 @@ def main():
         "config": {"workload": cfg["name"], "V": cfg["V"], "D": cfg["D"], "N": cfg["N"], "r_c": cfg["r_c"],
                    "r_r": cfg["r_r"], "g": cfg["g"], "logits": cfg["y_dtype"],
                    "packed_payload_bytes": A["payload"], "head_copies_rotated": 2},
-        "roofline": roofline_decode(r),
+        "roofline": roof,
     }
     if args.secondary:
-        s = run_workload(args.secondary, max(5, args.steps // 5), max(2, args.warmup // 5))
-        tf = s["A"]["total_flops"] / (s["ms"] / 1e3) / 1e12
-        log(f"[bench] {args.secondary}: {s['ms']:.3f} ms/step, tile kernel {s['kernel_ms']:.3f} ms")
+        steps2 = max(5, args.steps // 5)
+        s = run_workload(args.secondary, steps2, max(2, args.warmup // 5))
+        v2, u2, roof2 = summary(s)
+        log(f"[bench] {args.secondary}: {s['ms']:.3f} ms/step, {s['kernel']} {s['kernel_ms']:.3f} ms")
         out["secondary"] = {
-            "workload": s["cfg"]["name"], "value": round(tf, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(s["ms"], 4), "steps": max(5, args.steps // 5),
+            "workload": s["cfg"]["name"], "value": v2, "unit": u2,
+            "ms_per_step": round(s["ms"], 4), "steps": steps2,
             "config": {k: s["cfg"][k] for k in ("V", "D", "N", "r_c", "r_r", "g")} | {"logits": s["cfg"]["y_dtype"]},
-            "roofline": roofline_tile(s),
+            "roofline": roof2,
         }
     out["kernel_sources"] = kernel_hash()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_rows)
+        rows = args.cpu_sample_rows or (4096 if tile_workload(cfg["N"]) else cfg["V"])
+        out["cpu_baseline"] = cpu_baseline(args.config, rows)
     print(json.dumps(out), flush=True)
 
 

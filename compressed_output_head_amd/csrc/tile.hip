@@ -152,35 +152,36 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Large-N kernel on the 32 x 32 x 16 MFMA: 256 tokens x 256 vocabulary rows
-// per workgroup, four waves in a 2 x 2 grid, 128 x 128 per wave (16 result
-// tiles of 32 x 32, 256 fp32 accumulators per lane, kept in AGPRs).  The
+// per workgroup, eight waves in a 2 x 4 grid (two per SIMD), 128 x 64 per
+// wave (8 result tiles of 32 x 32, 128 fp32 accumulators per lane).  The
 // hidden dimension advances 64 columns (4 MFMA steps) per stage.
 //
 //   H (32-row layout, written by the prep kernel): an LDS ring of 4 stages of
 //     8 token tiles x 4 steps x 1 KB fragments, filled by buffer loads straight
-//     into LDS two stages ahead; one barrier per stage.
+//     into LDS three stages ahead; one barrier per stage.
 //   W: lane l of a wave reads, for 32-row vocabulary block CB, row l%16 of
 //     packed block 2 CB + (l/16)%2 at packed lane (l%16) + 16 q, q = l/32 in
 //     the first half of a k-tile and l/32 + 2 in the second; the 16 bytes give
-//     its four 8-column runs of that half, one per MFMA step, unpacked to exact
-//     fp16 integers q4 * c8 right before the MFMAs.  These loads run two stages
-//     ahead in a register ring.  Step t of half h thus covers runs
+//     its four 8-column runs of that half, one per MFMA step.  These loads run
+//     four stages ahead in a register ring.  Step t of half h thus covers runs
 //     R = 4 t + 2 h + l/32, the order the prep kernel gives H.
-// Every global read goes through a buffer resource: a wave-uniform offset plus
-// a small per-lane one, so no 64-bit per-lane address stays live.
+//   Group codes: the workgroup's 256 rows of codes are copied to LDS once.
+// Each MFMA step's operands (4 H fragments from LDS, the W fragments unpacked
+// to exact fp16 integers q4 * c8) are fetched while the previous step's MFMAs
+// run, and the next stage's first step is fetched right after the barrier
+// that publishes it.  Every global read goes through a buffer resource: a
+// wave-uniform offset plus a small per-lane one.
 constexpr int kT32TT = 8;  // 32-token tiles per workgroup
 constexpr int kT32CB = 8;  // 32-row vocabulary blocks per workgroup
-#ifndef ARCHEAD_T32_WN
-#define ARCHEAD_T32_WN 4
-#endif
-constexpr int kT32WN = ARCHEAD_T32_WN;       // waves along the vocabulary
+constexpr int kT32WN = 4;                    // waves along the vocabulary
 constexpr int kT32WM = 2;                    // waves along the tokens (4 token tiles each)
 constexpr int kT32Waves = kT32WM * kT32WN;
 constexpr int kT32Threads = 64 * kT32Waves;
 constexpr int kT32WCB = kT32CB / kT32WN;     // vocabulary blocks per wave
-constexpr int kT32Dist = 2;  // stages of prefetch; the H ring has 4 slots
+constexpr int kT32Ahead = 4;  // stages between a load's issue and its stage (H: 4 LDS slots, W: 4 register slots)
 constexpr int kT32HOps = kT32TT * 4 / kT32Waves;  // H copies per wave and stage
-constexpr int kT32WOps = 2 * kT32WCB;            // code loads per wave and stage
+constexpr int kT32WOps = kT32WCB;                // W loads per wave and stage
+constexpr int kT32MaxCodes = 64;  // group codes per row the workgroup can hold in LDS
 constexpr int kT32Group = 4;  // token tiles that walk the vocabulary together
 constexpr int kEpiChunk = kT32WCB >= 4 ? 4 : 2;  // low-rank rank steps whose loads are issued together
 constexpr int kEpiLdsSteps = 8;  // up to 128 padded ranks: Z of the workgroup fits the H ring
@@ -190,8 +191,28 @@ constexpr int kXcds = 8;
 // wave are outstanding (expcnt and lgkmcnt not waited on)
 __device__ constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
 
+// Workgroup barrier for the LDS ring: this wave's copies up to the last n
+// vector-memory operations and all its LDS reads are complete, then every
+// wave meets.  Buffer-to-LDS copies land in LDS when their vmcnt retires, so
+// after the barrier every wave's copies are visible.  No fence is emitted (a
+// fence would wait for every copy in flight); the empty asm statements with a
+// memory clobber keep the compiler from moving memory accesses across.
+template <int n>
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (n & 0xF) | (((n >> 4) & 3) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// A buffer resource over [base, base + bytes).  The size is made wave-uniform
+// explicitly: a resource the compiler believes divergent is used through a
+// loop over lanes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 struct Acc4 {  // low-rank accumulators of one wave's vocabulary blocks
@@ -212,12 +233,16 @@ __host__ __device__ inline T32Grid t32_grid(const FwdArgs& a) {
 
 // GC: group codes per k-tile and row that one stage needs: 0 -> one (g >= 128),
 // 1 -> two (g = 64), 2 -> four (g = 32)
+// The H ring is four separate LDS arrays, one per slot, chosen at compile
+// time: with one array the compiler cannot tell the slot being filled by
+// buffer-to-LDS copies from the slot being read, and makes every read wait
+// for all copies in flight.  T32_SLOT(S) names slot S (S a constant).
+#define T32_SLOT(S) (*((S) == 0 ? &sH0 : (S) == 1 ? &sH1 : (S) == 2 ? &sH2 : &sH3))
+
 template <int GC>
 __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
-  // the H ring: one LDS array per slot, so the compiler can tell a slot being
-  // filled by buffer-to-LDS copies from the slot being read and does not wait
-  // for the copies before every read
-  __shared__ h8 sH[4][kT32TT][4][64];
+  __shared__ h8 sH0[kT32TT][4][64], sH1[kT32TT][4][64], sH2[kT32TT][4][64], sH3[kT32TT][4][64];
+  __shared__ __align__(16) uint8_t sCode[kT32CB * 32 * kT32MaxCodes];  // [row][ng]
   __shared__ float sTok[kT32TT * 32][2];  // hscale, zscale of the workgroup's tokens
   __shared__ __align__(16) float sVR[kT32CB * 32], sVC[kT32CB * 32], sVW[kT32CB * 32];  // s_R, s_Ac, s_Aw
   const int tid = threadIdx.x, lane = tid & 63;
@@ -251,10 +276,80 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   }
   const int tt0 = ttile * kT32TT;           // first 32-token tile
   const int cb0 = vt * kT32CB + wn * kT32WCB;  // first vocabulary block of this wave
-  const int nS = (int)(a.D / 64);           // stages
+  const int nS = (int)(a.D / 64);           // stages (even, at least 2)
 
-  // per-token and per-row scales of the epilogue, staged once; the first
-  // barrier of the main loop publishes them
+  // H: the 32 fragments of a stage (8 token tiles x 4 MFMA steps) are spread
+  // over the waves, fragment f = kT32Waves i + wave being token tile f / 4,
+  // step f % 4.  Token tiles past the last re-read the last one: their rows
+  // are never stored.
+  const __amdgpu_buffer_rsrc_t hrs = buffer_rsrc(a.hf, (uint32_t)(a.n32 * a.D * 2));
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  const uint32_t hT = (uint32_t)a.nkt * 8192u;  // bytes per token tile
+  uint32_t hoff[kT32HOps];
+#pragma unroll
+  for (int i = 0; i < kT32HOps; ++i) {
+    const int f = kT32Waves * i + wave, tt = f >> 2;
+    hoff[i] = (uint32_t)(tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1) * hT + (uint32_t)(f & 3) * 1024u;
+  }
+  auto load_h = [&](int ks, auto S_) {
+    constexpr int S = decltype(S_)::value;
+#pragma unroll
+    for (int i = 0; i < kT32HOps; ++i) {
+      const int f = kT32Waves * i + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &T32_SLOT(S)[f >> 2][f & 3][0], 16, lane16,
+                                               hoff[i] + (uint32_t)ks * 4096u, 0, 0);
+    }
+  };
+
+  // W: per-lane byte offsets of this lane's row in each of its blocks (a
+  // block past the end re-reads the last one; its results are never stored)
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(a.r_codes, (uint32_t)(a.nb * 16 * (a.D / 2)));
+  const uint32_t tstride = (uint32_t)a.nb * 1024u;
+  uint32_t wvoff[kT32WCB];
+#pragma unroll
+  for (int cb = 0; cb < kT32WCB; ++cb) {
+    const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
+    int b = 2 * CB + ((lane >> 4) & 1);
+    if (b >= a.nb) b = (int)a.nb - 1;
+    wvoff[cb] = (uint32_t)b * 1024u + (uint32_t)(lane & 15) * 16u + (uint32_t)g * 256u;
+  }
+  u4 wr[kT32Ahead][kT32WCB];
+  auto load_w = [&](int ks, auto S_) {
+    constexpr int S = decltype(S_)::value;
+    const uint32_t soff = (uint32_t)(ks >> 1) * tstride + 512u * (uint32_t)(ks & 1);
+#pragma unroll
+    for (int cb = 0; cb < kT32WCB; ++cb)
+      wr[S][cb] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff[cb], soff, 0));
+  };
+
+  // prologue: the workgroup's group codes (at most two 16-byte pieces per
+  // thread), then the first kT32Ahead stages of W and H in flight; the codes
+  // go on to LDS as soon as they arrive
+  const int cbytes = kT32CB * 32 * a.ng;
+  u4 craw[2];
+  {
+    const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(a.r_gcodes, (uint32_t)(a.nb * 16 * a.ng));
+    const uint32_t base = (uint32_t)vt * (uint32_t)cbytes;  // rows past the end read as zero
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int o = 16 * (tid + i * kT32Threads);
+      craw[i] = o < cbytes ? __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(crs, base + (uint32_t)o, 0, 0))
+                           : u4{0u, 0u, 0u, 0u};
+    }
+  }
+  load_w(0, std::integral_constant<int, 0>{});
+  load_h(0, std::integral_constant<int, 0>{});
+  load_w(1, std::integral_constant<int, 1>{});
+  load_h(1, std::integral_constant<int, 1>{});
+  load_w(std::min(2, nS - 1), std::integral_constant<int, 2>{});
+  load_h(std::min(2, nS - 1), std::integral_constant<int, 2>{});
+  load_w(std::min(3, nS - 1), std::integral_constant<int, 3>{});
+  load_h(std::min(3, nS - 1), std::integral_constant<int, 3>{});
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int o = 16 * (tid + i * kT32Threads);
+    if (o < cbytes) *reinterpret_cast<u4*>(&sCode[o]) = craw[i];
+  }
   if (tid < kT32TT * 32) {
     const int64_t tok = std::min<int64_t>(32 * (int64_t)tt0 + tid, a.n32 - 1);
     sTok[tid][0] = a.hscale[tok];
@@ -265,70 +360,24 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     sVW[tid] = a.r_r > 0 ? f16_to_f32(a.a_scales[v * a.nA + a.nA - 1]) : 0.0f;
   }
 
-  // H: the 32 fragments of a stage (8 token tiles x 4 MFMA steps) are spread
-  // over the waves, fragment f = kT32Waves i + wave being token tile f / 4,
-  // step f % 4.  Tiles past the last one are zero-filled (only the last row
-  // of workgroups has any).
-  const __amdgpu_buffer_rsrc_t hrs = buffer_rsrc(a.hf, (uint32_t)(a.n32 * a.D * 2));
-  const uint32_t lane16 = (uint32_t)lane * 16u;
-  const uint32_t hT = (uint32_t)a.nkt * 8192u;  // bytes per token tile
-  uint32_t hoff[kT32HOps];
-#pragma unroll
-  for (int i = 0; i < kT32HOps; ++i) {
-    const int f = kT32Waves * i + wave, tt = f >> 2;
-    hoff[i] = (uint32_t)(tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1) * hT + (uint32_t)(f & 3) * 1024u;
-  }
-  const bool hfull = tt0 + kT32TT <= G.ntiles;
-  auto load_h = [&](int ks, int slot) {
-    if (hfull) {
-#pragma unroll
-      for (int i = 0; i < kT32HOps; ++i) {
-        const int f = kT32Waves * i + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][f >> 2][f & 3][0], 16, lane16,
-                                                 hoff[i] + (uint32_t)ks * 4096u, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kT32HOps; ++i) {
-        const int f = kT32Waves * i + wave;
-        if (tt0 + (f >> 2) < G.ntiles)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &sH[slot][f >> 2][f & 3][0], 16, lane16,
-                                                   hoff[i] + (uint32_t)ks * 4096u, 0, 0);
-        else
-          sH[slot][f >> 2][f & 3][lane] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-  };
-
-  // W: per-lane byte offsets of this lane's row in each of its 4 blocks (a
-  // block past the end re-reads the last one; its results are never stored)
-  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(a.r_codes, (uint32_t)(a.nb * 16 * (a.D / 2)));
-  const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(a.r_gcodes, (uint32_t)(a.nb * 16 * a.ng));
-  const uint32_t tstride = (uint32_t)a.nb * 1024u;
+  // group codes of this lane's rows for one stage: the code of each of the
+  // stage's 4 MFMA steps is byte (GC == 2 ? t : GC == 1 ? t / 2 : 0)
   const int lg = __builtin_ctz((unsigned)a.g);
-  uint32_t wvoff[kT32WCB], cvoff[kT32WCB];
+  uint32_t crow[kT32WCB];
 #pragma unroll
-  for (int cb = 0; cb < kT32WCB; ++cb) {
-    const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
-    int b = 2 * CB + ((lane >> 4) & 1);
-    if (b >= a.nb) b = (int)a.nb - 1;
-    wvoff[cb] = (uint32_t)b * 1024u + (uint32_t)(lane & 15) * 16u + (uint32_t)g * 256u;
-    cvoff[cb] = ((uint32_t)b * 16u + (uint32_t)(lane & 15)) * (uint32_t)a.ng;
-  }
-  u4 wr[kT32Dist][kT32WCB];
-  uint32_t wc[kT32Dist][kT32WCB];
-  auto load_w = [&](int ks, int slot) {
-    const int kt = ks >> 1, half = ks & 1;
-    const uint32_t soff = (uint32_t)kt * tstride + 512u * (uint32_t)half;
+  for (int cb = 0; cb < kT32WCB; ++cb)
+    crow[cb] = (uint32_t)(32 * (wn * kT32WCB + cb) + 16 * ((lane >> 4) & 1) + (lane & 15)) * (uint32_t)a.ng;
+  uint32_t cd[2][kT32WCB];
+  auto read_codes = [&](int ks, uint32_t(&dst)[kT32WCB]) {
+    const int kt = ks >> 1;
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb) {
-      wr[slot][cb] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff[cb], soff, 0));
       if constexpr (GC == 2)
-        wc[slot][cb] = __builtin_amdgcn_raw_buffer_load_b32(crs, cvoff[cb], 4u * (uint32_t)kt, 0);
+        dst[cb] = *reinterpret_cast<const uint32_t*>(&sCode[crow[cb] + 4 * kt]);
       else if constexpr (GC == 1)
-        wc[slot][cb] = __builtin_amdgcn_raw_buffer_load_b16(crs, cvoff[cb], 2u * (uint32_t)kt, 0);
+        dst[cb] = *reinterpret_cast<const uint16_t*>(&sCode[crow[cb] + 2 * kt]);
       else
-        wc[slot][cb] = __builtin_amdgcn_raw_buffer_load_b8(crs, cvoff[cb], (uint32_t)(kKTile * kt) >> lg, 0);
+        dst[cb] = sCode[crow[cb] + ((kKTile * kt) >> lg)];
     }
   };
 
@@ -338,58 +387,78 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb) acc[m][cb] = f16x{};
 
-  load_h(0, 0);
-  load_h(1, 1);  // nS >= 2
+  // operands of one MFMA step, double buffered by step parity
+  h8 av[2][4], bw[2][kT32WCB];
+  auto fetch = [&](auto S_, auto T_, auto P_) {
+    constexpr int S = decltype(S_)::value, T = decltype(T_)::value, P = decltype(P_)::value;
 #pragma unroll
-  for (int ks = 0; ks < kT32Dist; ++ks) load_w(ks, ks);
-
-  // One stage; S = ks mod 4 picks the ring slots at compile time.  On entry
-  // this wave has in flight, oldest first, the H copies and W loads of stage
-  // ks, then those of stage ks+1; waiting down to the last two batches
-  // completes stage ks.  The barrier then makes every wave's copies of stage ks
-  // visible and retires all reads of the slot refilled next.  The last two
-  // stages reload their own stage instead of prefetching, which keeps the
-  // count of operations in flight the same.
-  auto stage = [&](int ks, auto S_) {
-    constexpr int S = decltype(S_)::value, ws = S & 1;
-    h8(&cur)[kT32TT][4][64] = sH[ks & 3];
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kT32HOps + kT32WOps));
-    __syncthreads();
-    const int kn = ks + kT32Dist < nS ? ks + kT32Dist : nS - 1;
-    load_h(kn, (ks + 2) & 3);
-    // unpack the whole stage first so the W slot can be refilled at once
-    h8 bvs[4][kT32WCB];
+    for (int m = 0; m < 4; ++m) av[P][m] = T32_SLOT(S)[4 * wm + m][T][lane];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int cb = 0; cb < kT32WCB; ++cb) {
-        const uint32_t code = GC == 2 ? (wc[ws][cb] >> (8 * t)) & 0xffu
-                            : GC == 1 ? (wc[ws][cb] >> (8 * (t >> 1))) & 0xffu
-                                      : wc[ws][cb] & 0xffu;
-        bvs[t][cb] = unpack_q4_scaled(wr[ws][cb][t], (_Float16)(float)code);
-      }
-    load_w(kn, ws);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      h8 av[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) av[m] = cur[4 * wm + m][t][lane];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int cb = 0; cb < kT32WCB; ++cb) acc[m][cb] = mfma32(bvs[t][cb], av[m], acc[m][cb]);
+    for (int cb = 0; cb < kT32WCB; ++cb) {
+      const uint32_t c = cd[S & 1][cb];
+      const uint32_t code = GC == 2 ? (c >> (8 * T)) & 0xffu : GC == 1 ? (c >> (8 * (T >> 1))) & 0xffu : c;
+      bw[P][cb] = unpack_q4_scaled(wr[S][cb][T], (_Float16)(float)code);
     }
+  };
+  auto mma = [&](auto P_) {
+    constexpr int P = decltype(P_)::value;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int cb = 0; cb < kT32WCB; ++cb) acc[m][cb] = mfma32(bw[P][cb], av[P][m], acc[m][cb]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // stage 0 complete: wait past the loads of stages 1..3, then publish every
+  // wave's copies and the codes
+  stage_barrier<3 * (kT32WOps + kT32HOps)>();
+  read_codes(0, cd[0]);
+  fetch(I0{}, I0{}, I0{});
+
+  // One stage; S = ks mod 4 is its ring slot (H in LDS, W in registers) at
+  // compile time.  The loads of stage ks + 4 go into the slot this stage
+  // frees: W once the last step is unpacked, H after the barrier that ends
+  // every wave's reads of it.  Loads past the last stage repeat the last one,
+  // which keeps the count of operations in flight the same.
+  auto stage = [&](int ks, auto S_) {
+    constexpr int S = decltype(S_)::value;
+    constexpr std::integral_constant<int, S> Sc{};
+    constexpr std::integral_constant<int, (S + 1) & 3> Sn{};
+    const int kn = ks + kT32Ahead < nS ? ks + kT32Ahead : nS - 1;
+    // each MFMA step is its own scheduling region, so that no unpacking of
+    // registers still being loaded is hoisted into it
+    fetch(Sc, I1{}, I1{});
+    read_codes(ks + 1 < nS ? ks + 1 : ks, cd[(S + 1) & 1]);
+    mma(I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(Sc, I2{}, I0{});
+    mma(I1{});
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(Sc, I3{}, I1{});
+    load_w(kn, Sc);
+    mma(I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    // stage ks + 1 is complete once this wave has at most the loads of the
+    // three stages after it (W of ks + 4 included) in flight
+    stage_barrier<3 * kT32WOps + 2 * kT32HOps>();
+    load_h(kn, Sc);
+    fetch(Sn, I0{}, I0{});  // past the last stage: harmless reads, never used
+    mma(I1{});
+    __builtin_amdgcn_sched_barrier(0);
   };
   int ks = 0;
   for (; ks + 4 <= nS; ks += 4) {
-    stage(ks, std::integral_constant<int, 0>{});
-    stage(ks + 1, std::integral_constant<int, 1>{});
-    stage(ks + 2, std::integral_constant<int, 2>{});
-    stage(ks + 3, std::integral_constant<int, 3>{});
+    stage(ks, I0{});
+    stage(ks + 1, I1{});
+    stage(ks + 2, I2{});
+    stage(ks + 3, I3{});
   }
   if (ks < nS) {  // nS is even: two stages remain
-    stage(ks, std::integral_constant<int, 0>{});
-    stage(ks + 1, std::integral_constant<int, 1>{});
+    stage(ks, I0{});
+    stage(ks + 1, I1{});
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -462,13 +531,22 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     // H ring and all A codes of this lane into registers: one round trip
     __syncthreads();  // every wave is done reading the ring
     const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(a.zf, (uint32_t)(a.n32 * (a.rc32 + a.rr32) * 4));
-    const int zper = 2 * esteps;  // 1 KB fragments per token tile
-    for (int f = wave; f < kT32TT * zper; f += kT32Waves) {
-      const int tt = f / zper, rem = f - tt * zper;
-      const int T = tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1;  // padding tiles are never stored
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, &sH[f >> 5][(f & 31) >> 2][f & 3][0], 16, lane16,
-                                               (uint32_t)(T * zper + rem) * 1024u, 0, 0);
-    }
+    // slot m holds the Z fragments of token tiles m and m + 4 (the tiles of
+    // wave rows 0 and 1 at position m): fragment wr * zper + rem of the slot
+    const int zper = 2 * esteps;  // 1 KB fragments per token tile, at most 16
+    auto load_z = [&](auto S_) {
+      constexpr int S = decltype(S_)::value;
+      for (int f = wave; f < 2 * zper; f += kT32Waves) {
+        const int w2 = f >= zper ? 1 : 0, rem = f - w2 * zper, tt = S + 4 * w2;
+        const int T = tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1;  // padding tiles are never stored
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, &T32_SLOT(S)[f >> 2][f & 3][0], 16, lane16,
+                                                 (uint32_t)(T * zper + rem) * 1024u, 0, 0);
+      }
+    };
+    load_z(std::integral_constant<int, 0>{});
+    load_z(std::integral_constant<int, 1>{});
+    load_z(std::integral_constant<int, 2>{});
+    load_z(std::integral_constant<int, 3>{});
     u2 ac[kT32WCB][kEpiLdsSteps];
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb)
@@ -482,7 +560,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     auto tile_pair = [&](auto M_, auto P_) {
       constexpr int m = decltype(M_)::value, cp = kEpiBlocks * decltype(P_)::value;
       if (tt0 + 4 * wm + m >= G.ntiles) return;
-      const int f0 = (4 * wm + m) * zper;
+      const int f0 = wm * zper;  // in slot m
       f16x pc[kEpiBlocks], pw[kEpiBlocks];
 #pragma unroll
       for (int j = 0; j < kEpiBlocks; ++j) {
@@ -493,8 +571,8 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
       for (int s = 0; s < kEpiLdsSteps; ++s) {
         if (s < esteps) {
           const int fh = f0 + 2 * s, fl = fh + 1;
-          const h8 zh = sH[fh >> 5][(fh & 31) >> 2][fh & 3][lane];
-          const h8 zl = sH[fl >> 5][(fl & 31) >> 2][fl & 3][lane];
+          const h8 zh = T32_SLOT(m)[fh >> 2][fh & 3][lane];
+          const h8 zl = T32_SLOT(m)[fl >> 2][fl & 3][lane];
           h8 av[kEpiBlocks];
 #pragma unroll
           for (int j = 0; j < kEpiBlocks; ++j) av[j] = unpack_i8x8(ac[cp + j][s][0], ac[cp + j][s][1]);
@@ -571,6 +649,8 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   tile(std::integral_constant<int, 3>{});
 }
 
+#undef T32_SLOT
+
 }  // namespace
 
 // The 32 x 32 x 16 kernel serves N > 128 when every section it reads fits
@@ -578,7 +658,8 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 bool tile32_eligible(const FwdArgs& a) {
   if (a.N <= 128) return false;
   if ((uint64_t)a.nb * 16 * (uint64_t)a.D / 2 >= (1ull << 32)) return false;
-  if ((uint64_t)a.nb * 16 * (uint64_t)a.ng >= (1ull << 32)) return false;
+  if (a.ng > kT32MaxCodes) return false;
+  if (((uint64_t)a.nb * 16 + kT32CB * 32) * (uint64_t)a.ng >= (1ull << 32)) return false;
   if ((uint64_t)a.n32 * (uint64_t)a.D * 2 >= (1ull << 32)) return false;
   const T32Grid G = t32_grid(a);
   return (int64_t)G.ttiles * G.vtiles < (1ll << 31);
