@@ -173,15 +173,23 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const FwdArgs a) {
 // wave-uniform offset plus a small per-lane one.
 constexpr int kT32TT = 8;  // 32-token tiles per workgroup
 constexpr int kT32CB = 8;  // 32-row vocabulary blocks per workgroup
-constexpr int kT32WN = 4;                    // waves along the vocabulary
-constexpr int kT32WM = 2;                    // waves along the tokens (4 token tiles each)
-constexpr int kT32Waves = kT32WM * kT32WN;
+#ifndef ARCHEAD_T32_WM
+#define ARCHEAD_T32_WM 1
+#endif
+constexpr int kT32Waves = 8;
+constexpr int kT32WM = ARCHEAD_T32_WM;       // waves along the tokens
+constexpr int kT32WN = kT32Waves / kT32WM;   // waves along the vocabulary
 constexpr int kT32Threads = 64 * kT32Waves;
+constexpr int kT32MT = kT32TT / kT32WM;      // token tiles per wave
 constexpr int kT32WCB = kT32CB / kT32WN;     // vocabulary blocks per wave
+static_assert(kT32MT % 4 == 0, "the epilogue's Z slots assume whole groups of 4 token tiles per wave");
 constexpr int kT32Ahead = 4;  // stages between a load's issue and its stage (H: 4 LDS slots, W: 4 register slots)
 constexpr int kT32HOps = kT32TT * 4 / kT32Waves;  // H copies per wave and stage
 constexpr int kT32WOps = kT32WCB;                // W loads per wave and stage
 constexpr int kT32MaxCodes = 64;  // group codes per row the workgroup can hold in LDS
+// LDS row stride of the group codes: an odd number of dwords, so the 32 rows
+// one wave reads at a time fall in 32 different banks
+__host__ __device__ constexpr int t32_code_stride(int ng) { return 4 * (((ng + 3) / 4) | 1); }
 constexpr int kT32Group = 4;  // token tiles that walk the vocabulary together
 constexpr int kEpiChunk = kT32WCB >= 4 ? 4 : 2;  // low-rank rank steps whose loads are issued together
 constexpr int kEpiLdsSteps = 8;  // up to 128 padded ranks: Z of the workgroup fits the H ring
@@ -215,6 +223,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
                                            (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// f(integral_constant<I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 struct Acc4 {  // low-rank accumulators of one wave's vocabulary blocks
   f16x v[kT32WCB];
 };
@@ -242,7 +259,7 @@ __host__ __device__ inline T32Grid t32_grid(const FwdArgs& a) {
 template <int GC>
 __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   __shared__ h8 sH0[kT32TT][4][64], sH1[kT32TT][4][64], sH2[kT32TT][4][64], sH3[kT32TT][4][64];
-  __shared__ __align__(16) uint8_t sCode[kT32CB * 32 * kT32MaxCodes];  // [row][ng]
+  __shared__ __align__(16) uint8_t sCode[kT32CB * 32 * t32_code_stride(kT32MaxCodes)];  // [row][stride]
   __shared__ float sTok[kT32TT * 32][2];  // hscale, zscale of the workgroup's tokens
   __shared__ __align__(16) float sVR[kT32CB * 32], sVC[kT32CB * 32], sVW[kT32CB * 32];  // s_R, s_Ac, s_Aw
   const int tid = threadIdx.x, lane = tid & 63;
@@ -322,19 +339,82 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
       wr[S][cb] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff[cb], soff, 0));
   };
 
-  // prologue: the workgroup's group codes (at most two 16-byte pieces per
-  // thread), then the first kT32Ahead stages of W and H in flight; the codes
-  // go on to LDS as soon as they arrive
-  const int cbytes = kT32CB * 32 * a.ng;
-  u4 craw[2];
-  {
-    const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(a.r_gcodes, (uint32_t)(a.nb * 16 * a.ng));
-    const uint32_t base = (uint32_t)vt * (uint32_t)cbytes;  // rows past the end read as zero
+  // Low-rank operands.  With at most kEpiLdsSteps rank steps (the common
+  // case) Z of the workgroup's token tiles is copied into the H ring during
+  // the last four stages, one slot per stage, and this lane's A codes are
+  // loaded with the prologue.
+  const int r = a.r_c + a.r_r;
+  const int csteps = a.rc32 / 16, esteps = (a.rc32 + a.rr32) / 16;
+  const bool zlds = esteps <= kEpiLdsSteps;
+  const int zper = 2 * esteps;  // 1 KB Z fragments per token tile (hi, lo per step)
+  const int8_t* arow[kT32WCB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int o = 16 * (tid + i * kT32Threads);
-      craw[i] = o < cbytes ? __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(crs, base + (uint32_t)o, 0, 0))
-                           : u4{0u, 0u, 0u, 0u};
+  for (int cb = 0; cb < kT32WCB; ++cb) {
+    const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
+    int64_t v = 32 * (int64_t)CB + c32;
+    if (v >= 16 * a.nb) v = 16 * a.nb - 1;
+    arow[cb] = a.a_codes + v * r;
+  }
+  // A codes of this lane's row in block cb for rank step s (zero past the part's rank)
+  auto a_code = [&](int cb, int s) {
+    const bool part_c = s < csteps;
+    const int sl = part_c ? s : s - csteps;
+    const int col = 32 * (sl >> 1) + 16 * g + 8 * (sl & 1);  // rank order of the 32-row Z layout
+    u2 raw = {0u, 0u};
+    if (col < (part_c ? a.r_c : a.r_r)) raw = *reinterpret_cast<const u2*>(arow[cb] + (part_c ? 0 : a.r_c) + col);
+    return raw;
+  };
+  u2 ac[kT32WCB][kEpiLdsSteps];
+#pragma unroll
+  for (int cb = 0; cb < kT32WCB; ++cb)
+#pragma unroll
+    for (int s = 0; s < kEpiLdsSteps; ++s) ac[cb][s] = zlds && s < esteps ? a_code(cb, s) : u2{0u, 0u};
+  // Entry j of the copy sequence into slot j % 4: H stage j for j < nS; past
+  // the last stage, Z of the workgroup (or the last stage again when Z is
+  // read from memory in the epilogue).  Slot S holds the Z fragments of token
+  // tiles S and S + 4, fragment w2 * zper + rem at the position an H fragment
+  // would take; positions past 2 zper repeat the last fragment.  The source
+  // is a uniform select, so every copy has the same form as an H copy.
+  const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(a.zf, (uint32_t)(a.n32 * (a.rc32 + a.rr32) * 4));
+  auto load_slot = [&](int j, auto S_) {
+    constexpr int S = decltype(S_)::value;
+    const bool zsrc = j >= nS && zlds;
+    const int jh = j < nS ? j : nS - 1;
+#pragma unroll
+    for (int i = 0; i < kT32HOps; ++i) {
+      const int f = kT32Waves * i + wave;
+      const int fz = f < 2 * zper ? f : 2 * zper - 1;
+      const int w2 = fz >= zper ? 1 : 0, rem = fz - w2 * zper, tt = S + 4 * w2;
+      const int T = tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1;  // padding tiles are never stored
+      const uint32_t off = zsrc ? (uint32_t)(T * zper + rem) * 1024u : hoff[i] + (uint32_t)jh * 4096u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zsrc ? zrs : hrs, &T32_SLOT(S)[f >> 2][f & 3][0], 16, lane16,
+                                               off, 0, 0);
+    }
+  };
+
+  // prologue: the workgroup's group codes into registers (row tid / 2, half
+  // tid % 2 of its ng codes: dwords when rows are dword aligned, else bytes),
+  // then the first kT32Ahead stages of W and H in flight; the codes go on to
+  // LDS as soon as they arrive.  Rows past the end read as zero.
+  const int ng = a.ng, cstride = t32_code_stride(ng);
+  const int crow_ = tid >> 1, chalf = tid & 1;
+  uint32_t craw[kT32MaxCodes / 8];
+  const bool cdw = (ng & 3) == 0;
+  {
+    const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(a.r_gcodes, (uint32_t)(a.nb * 16 * ng));
+    const uint32_t rbase = ((uint32_t)vt * (kT32CB * 32) + (uint32_t)crow_) * (uint32_t)ng;
+    if (cdw) {
+#pragma unroll
+      for (int j = 0; j < kT32MaxCodes / 8; ++j) {
+        const int d = 2 * j + chalf;  // dword of the row
+        craw[j] = 4 * d < ng ? __builtin_amdgcn_raw_buffer_load_b32(crs, rbase + 4u * (uint32_t)d, 0, 0) : 0u;
+      }
+    } else {  // fewer than 4 codes per row, or a count that is not a multiple of 4: bytes
+#pragma unroll
+      for (int j = 0; j < kT32MaxCodes / 8; ++j) {
+        const int c = 2 * j + chalf;
+        craw[j] = c < ng ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(crs, rbase + (uint32_t)c, 0, 0) : 0u;
+      }
     }
   }
   load_w(0, std::integral_constant<int, 0>{});
@@ -342,13 +422,21 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   load_w(1, std::integral_constant<int, 1>{});
   load_h(1, std::integral_constant<int, 1>{});
   load_w(std::min(2, nS - 1), std::integral_constant<int, 2>{});
-  load_h(std::min(2, nS - 1), std::integral_constant<int, 2>{});
+  load_slot(2, std::integral_constant<int, 2>{});
   load_w(std::min(3, nS - 1), std::integral_constant<int, 3>{});
-  load_h(std::min(3, nS - 1), std::integral_constant<int, 3>{});
+  load_slot(3, std::integral_constant<int, 3>{});
+  if (cdw) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int o = 16 * (tid + i * kT32Threads);
-    if (o < cbytes) *reinterpret_cast<u4*>(&sCode[o]) = craw[i];
+    for (int j = 0; j < kT32MaxCodes / 8; ++j) {
+      const int d = 2 * j + chalf;
+      if (4 * d < ng) *reinterpret_cast<uint32_t*>(&sCode[crow_ * cstride + 4 * d]) = craw[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kT32MaxCodes / 8; ++j) {
+      const int c = 2 * j + chalf;
+      if (c < ng) sCode[crow_ * cstride + c] = (uint8_t)craw[j];
+    }
   }
   if (tid < kT32TT * 32) {
     const int64_t tok = std::min<int64_t>(32 * (int64_t)tt0 + tid, a.n32 - 1);
@@ -366,7 +454,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   uint32_t crow[kT32WCB];
 #pragma unroll
   for (int cb = 0; cb < kT32WCB; ++cb)
-    crow[cb] = (uint32_t)(32 * (wn * kT32WCB + cb) + 16 * ((lane >> 4) & 1) + (lane & 15)) * (uint32_t)a.ng;
+    crow[cb] = (uint32_t)(32 * (wn * kT32WCB + cb) + 16 * ((lane >> 4) & 1) + (lane & 15)) * (uint32_t)cstride;
   uint32_t cd[2][kT32WCB];
   auto read_codes = [&](int ks, uint32_t(&dst)[kT32WCB]) {
     const int kt = ks >> 1;
@@ -381,18 +469,18 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     }
   };
 
-  f16x acc[4][kT32WCB];
+  f16x acc[kT32MT][kT32WCB];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < kT32MT; ++m)
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb) acc[m][cb] = f16x{};
 
   // operands of one MFMA step, double buffered by step parity
-  h8 av[2][4], bw[2][kT32WCB];
+  h8 av[2][kT32MT], bw[2][kT32WCB];
   auto fetch = [&](auto S_, auto T_, auto P_) {
     constexpr int S = decltype(S_)::value, T = decltype(T_)::value, P = decltype(P_)::value;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) av[P][m] = T32_SLOT(S)[4 * wm + m][T][lane];
+    for (int m = 0; m < kT32MT; ++m) av[P][m] = T32_SLOT(S)[kT32MT * wm + m][T][lane];
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb) {
       const uint32_t c = cd[S & 1][cb];
@@ -403,7 +491,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   auto mma = [&](auto P_) {
     constexpr int P = decltype(P_)::value;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kT32MT; ++m)
 #pragma unroll
       for (int cb = 0; cb < kT32WCB; ++cb) acc[m][cb] = mfma32(bw[P][cb], av[P][m], acc[m][cb]);
   };
@@ -421,8 +509,9 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   // One stage; S = ks mod 4 is its ring slot (H in LDS, W in registers) at
   // compile time.  The loads of stage ks + 4 go into the slot this stage
   // frees: W once the last step is unpacked, H after the barrier that ends
-  // every wave's reads of it.  Loads past the last stage repeat the last one,
-  // which keeps the count of operations in flight the same.
+  // every wave's reads of it.  Past the last stage the H slot receives Z
+  // instead (or the last stage again), and W repeats the last stage, which
+  // keeps the count of operations in flight the same.
   auto stage = [&](int ks, auto S_) {
     constexpr int S = decltype(S_)::value;
     constexpr std::integral_constant<int, S> Sc{};
@@ -444,7 +533,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     // stage ks + 1 is complete once this wave has at most the loads of the
     // three stages after it (W of ks + 4 included) in flight
     stage_barrier<3 * kT32WOps + 2 * kT32HOps>();
-    load_h(kn, Sc);
+    load_slot(ks + kT32Ahead, Sc);
     fetch(Sn, I0{}, I0{});  // past the last stage: harmless reads, never used
     mma(I1{});
     __builtin_amdgcn_sched_barrier(0);
@@ -462,33 +551,14 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  const int r = a.r_c + a.r_r;
-  const int csteps = a.rc32 / 16, esteps = (a.rc32 + a.rr32) / 16;
   // Epilogue.  Result tile (m, cb): element v of lane l is vocabulary row
   // 32 CB + 8 (v/4) + 4 (l/32) + v%4 and token 32 T + l%32, so each lane holds
   // runs of 4 consecutive logits of one token.  The low-rank term (Z hi/lo
   // against exact INT8 A codes, 16 ranks per MFMA step, one accumulator per
   // part) is added with the scales, and each run is stored at once.
   const bool vec = ((uintptr_t)a.Y & 15) == 0 && (a.Y_stride & 3) == 0;
-  const int8_t* arow[kT32WCB];
-#pragma unroll
-  for (int cb = 0; cb < kT32WCB; ++cb) {
-    const int CB = cb0 + cb < G.ncb ? cb0 + cb : G.ncb - 1;
-    int64_t v = 32 * (int64_t)CB + c32;
-    if (v >= 16 * a.nb) v = 16 * a.nb - 1;
-    arow[cb] = a.a_codes + v * r;
-  }
-  // A codes of this lane's row in block cb for rank step s (zero past the part's rank)
-  auto a_code = [&](int cb, int s) {
-    const bool part_c = s < csteps;
-    const int sl = part_c ? s : s - csteps;
-    const int col = 32 * (sl >> 1) + 16 * g + 8 * (sl & 1);  // rank order of the 32-row Z layout
-    u2 raw = {0u, 0u};
-    if (col < (part_c ? a.r_c : a.r_r)) raw = *reinterpret_cast<const u2*>(arow[cb] + (part_c ? 0 : a.r_c) + col);
-    return raw;
-  };
   auto store = [&](int m, int cb, const f16x& am, const f16x& pc, const f16x& pw) {
-    const int tl = 32 * (4 * wm + m) + c32;  // token within the workgroup
+    const int tl = 32 * (kT32MT * wm + m) + c32;  // token within the workgroup
     const int64_t tok = 32 * (int64_t)tt0 + tl;
     if (tok >= a.N || cb0 + cb >= G.ncb) return;
     const float hs = sTok[tl][0], zs = sTok[tl][1];
@@ -526,41 +596,109 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     }
   };
 
-  if (esteps <= kEpiLdsSteps) {
-    // Z of the workgroup's 8 token tiles (16 KB per 16 ranks) into the idle
-    // H ring and all A codes of this lane into registers: one round trip
-    __syncthreads();  // every wave is done reading the ring
-    const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(a.zf, (uint32_t)(a.n32 * (a.rc32 + a.rr32) * 4));
-    // slot m holds the Z fragments of token tiles m and m + 4 (the tiles of
-    // wave rows 0 and 1 at position m): fragment wr * zper + rem of the slot
-    const int zper = 2 * esteps;  // 1 KB fragments per token tile, at most 16
-    auto load_z = [&](auto S_) {
-      constexpr int S = decltype(S_)::value;
-      for (int f = wave; f < 2 * zper; f += kT32Waves) {
-        const int w2 = f >= zper ? 1 : 0, rem = f - w2 * zper, tt = S + 4 * w2;
-        const int T = tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1;  // padding tiles are never stored
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, &T32_SLOT(S)[f >> 2][f & 3][0], 16, lane16,
-                                                 (uint32_t)(T * zper + rem) * 1024u, 0, 0);
-      }
+  // Whole workgroup tile in range (every token and vocabulary row exists),
+  // aligned rows and an output span within 32-bit offsets: a straight-line
+  // epilogue with the split between the two low-rank parts fixed at compile
+  // time (csteps is even), the row scales in registers and buffer stores at
+  // uniform offsets.
+  const uint64_t es = a.y_bf16 ? 2 : 4;
+  const bool fast = zlds && vec && 32 * (int64_t)(tt0 + kT32TT) <= a.N &&
+                    32 * ((int64_t)vt * kT32CB + kT32CB) <= a.V &&
+                    (uint64_t)a.N * (uint64_t)a.Y_stride * es < (1ull << 32);
+  if (fast) {
+    __syncthreads();  // every wave's Z copies (complete after the wait above) are visible
+    const __amdgpu_buffer_rsrc_t yrs = buffer_rsrc(a.Y, (uint32_t)((uint64_t)a.N * (uint64_t)a.Y_stride * es));
+    // lane part of the output offset: token c32 of the tile, the lane's run of block cb
+    uint32_t yoff[kT32WCB];
+#pragma unroll
+    for (int cb = 0; cb < kT32WCB; ++cb)
+      yoff[cb] = (uint32_t)(((uint64_t)c32 * (uint64_t)a.Y_stride +
+                             32 * ((uint64_t)vt * kT32CB + kT32WCB * wn + cb) + 4 * g) * es);
+    // The wave's tiles (m, cb) one at a time, each its own scheduling region
+    // (the two waves of a SIMD overlap one's scaling with the other's MFMAs).
+    auto epilogue = [&](auto CS_) {
+      constexpr int CS = decltype(CS_)::value;
+      constexpr int kTiles = kT32MT * kT32WCB;
+      auto low_rank = [&](auto J_, f16x& pc, f16x& pw) {
+        constexpr int m = decltype(J_)::value / kT32WCB, cb = decltype(J_)::value % kT32WCB;
+        const int tt = kT32MT * wm + m;
+        const int f0 = (tt >> 2) * zper;  // Z of token tile tt: slot tt % 4 = m % 4
+        pc = f16x{};
+        pw = f16x{};
+        static_for<0, kEpiLdsSteps>([&](auto S_) {
+          constexpr int s = decltype(S_)::value;
+          const int fh = f0 + 2 * s, fl = fh + 1;  // within the slot (past 2 zper: copies, A codes are 0)
+          const h8 zh = T32_SLOT(m & 3)[fh >> 2][fh & 3][lane];
+          const h8 zl = T32_SLOT(m & 3)[fl >> 2][fl & 3][lane];
+          const h8 av = unpack_i8x8(ac[cb][s][0], ac[cb][s][1]);
+          if constexpr (s < CS) {
+            pc = mfma32(av, zh, pc);
+            pc = mfma32(av, zl, pc);
+          } else {
+            pw = mfma32(av, zh, pw);
+            pw = mfma32(av, zl, pw);
+          }
+        });
+      };
+      auto finish = [&](auto J_, const f16x& pc, const f16x& pw) {
+        constexpr int m = decltype(J_)::value / kT32WCB, cb = decltype(J_)::value % kT32WCB;
+        const int tt = kT32MT * wm + m;
+        const float hs = sTok[32 * tt + c32][0], zs = sTok[32 * tt + c32][1];
+        const uint32_t trow = (uint32_t)((uint64_t)(32 * (tt0 + tt)) * (uint64_t)a.Y_stride * es);
+        const f16x& am = acc[m][cb];
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+          const int lr = 32 * (kT32WCB * wn + cb) + 8 * vg + 4 * g;
+          // row scales of block cb, run vg (rows 8 vg + 4 g + e)
+          const f4 vr = *reinterpret_cast<const f4*>(&sVR[lr]);
+          const f4 vc = *reinterpret_cast<const f4*>(&sVC[lr]);
+          const f4 vw = *reinterpret_cast<const f4*>(&sVW[lr]);
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * vg + e;
+            y[e] = fmaf(zs, fmaf(vw[e], pw[v], vc[e] * pc[v]), hs * (vr[e] * am[v]));
+          }
+          if (a.y_bf16)
+            __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(y[0], y[1], y[2], y[3]), yrs, yoff[cb],
+                                                  trow + (uint32_t)(16 * vg), 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, f4{y[0], y[1], y[2], y[3]}), yrs,
+                                                   yoff[cb], trow + (uint32_t)(32 * vg), 0);
+        }
+      };
+      static_for<0, kTiles>([&](auto J_) {
+        __builtin_amdgcn_sched_barrier(0);
+        f16x pc, pw;
+        low_rank(J_, pc, pw);
+        finish(J_, pc, pw);
+      });
     };
-    load_z(std::integral_constant<int, 0>{});
-    load_z(std::integral_constant<int, 1>{});
-    load_z(std::integral_constant<int, 2>{});
-    load_z(std::integral_constant<int, 3>{});
-    u2 ac[kT32WCB][kEpiLdsSteps];
+    switch (csteps) {
+      case 0: epilogue(std::integral_constant<int, 0>{}); break;
+      case 2: epilogue(std::integral_constant<int, 2>{}); break;
+      case 4: epilogue(std::integral_constant<int, 4>{}); break;
+      case 6: epilogue(std::integral_constant<int, 6>{}); break;
+      default: epilogue(std::integral_constant<int, 8>{}); break;
+    }
+    return;
+  }
+
+  if (zlds) {
+    __syncthreads();  // every wave's Z copies (complete after the wait above) are visible
+    h8 aun[kT32WCB][kEpiLdsSteps];  // A codes unpacked once for all token tiles
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb)
 #pragma unroll
-      for (int s = 0; s < kEpiLdsSteps; ++s) ac[cb][s] = s < esteps ? a_code(cb, s) : u2{0u, 0u};
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+      for (int s = 0; s < kEpiLdsSteps; ++s) aun[cb][s] = unpack_i8x8(ac[cb][s][0], ac[cb][s][1]);
     // kEpiBlocks vocabulary blocks at a time: with 8 waves per workgroup the
     // registers only hold one block's low-rank accumulators next to the tile's
     constexpr int kEpiBlocks = kT32WCB >= 4 ? 2 : 1;
     auto tile_pair = [&](auto M_, auto P_) {
       constexpr int m = decltype(M_)::value, cp = kEpiBlocks * decltype(P_)::value;
-      if (tt0 + 4 * wm + m >= G.ntiles) return;
-      const int f0 = wm * zper;  // in slot m
+      const int tt = kT32MT * wm + m;
+      if (tt0 + tt >= G.ntiles) return;
+      const int f0 = (tt >> 2) * zper;  // in slot tt % 4 = m % 4
       f16x pc[kEpiBlocks], pw[kEpiBlocks];
 #pragma unroll
       for (int j = 0; j < kEpiBlocks; ++j) {
@@ -571,11 +709,11 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
       for (int s = 0; s < kEpiLdsSteps; ++s) {
         if (s < esteps) {
           const int fh = f0 + 2 * s, fl = fh + 1;
-          const h8 zh = T32_SLOT(m)[fh >> 2][fh & 3][lane];
-          const h8 zl = T32_SLOT(m)[fl >> 2][fl & 3][lane];
+          const h8 zh = T32_SLOT(m & 3)[fh >> 2][fh & 3][lane];
+          const h8 zl = T32_SLOT(m & 3)[fl >> 2][fl & 3][lane];
           h8 av[kEpiBlocks];
 #pragma unroll
-          for (int j = 0; j < kEpiBlocks; ++j) av[j] = unpack_i8x8(ac[cp + j][s][0], ac[cp + j][s][1]);
+          for (int j = 0; j < kEpiBlocks; ++j) av[j] = aun[cp + j][s];
           if (s < csteps) {
 #pragma unroll
             for (int j = 0; j < kEpiBlocks; ++j) pc[j] = mfma32(av[j], zh, pc[j]);
@@ -592,14 +730,9 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < kEpiBlocks; ++j) store(m, cp + j, acc[m][cp + j], pc[j], pw[j]);
     };
-    auto tile_pairs = [&](auto M_) {
-      tile_pair(M_, std::integral_constant<int, 0>{});
-      tile_pair(M_, std::integral_constant<int, 1>{});  // kT32WCB == 2 * kEpiBlocks
-    };
-    tile_pairs(std::integral_constant<int, 0>{});
-    tile_pairs(std::integral_constant<int, 1>{});
-    tile_pairs(std::integral_constant<int, 2>{});
-    tile_pairs(std::integral_constant<int, 3>{});
+    static_for<0, kT32MT>([&](auto M_) {
+      static_for<0, kT32WCB / kEpiBlocks>([&](auto P_) { tile_pair(M_, P_); });
+    });
     return;
   }
 
@@ -636,17 +769,14 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   };
   auto tile = [&](auto M_) {
     constexpr int m = decltype(M_)::value;
-    const int T = tt0 + 4 * wm + m;
+    const int T = tt0 + kT32MT * wm + m;
     if (T >= G.ntiles) return;
     const Acc4 pc = low_rank_part(T, 0, csteps);
     const Acc4 pw = low_rank_part(T, csteps, esteps);
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb) store(m, cb, acc[m][cb], pc.v[cb], pw.v[cb]);
   };
-  tile(std::integral_constant<int, 0>{});
-  tile(std::integral_constant<int, 1>{});
-  tile(std::integral_constant<int, 2>{});
-  tile(std::integral_constant<int, 3>{});
+  static_for<0, kT32MT>(tile);
 }
 
 #undef T32_SLOT
