@@ -76,7 +76,7 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens) {
   w.zf = take(n32 * (uint64_t)w.zsteps * 2 * 32 * 2);
   w.zscale = take(n32 * 4);
   const uint64_t nsmall = n_tokens <= kDecodeLdsTokens ? (uint64_t)std::max<int64_t>(n_tokens, 0) : 0;
-  w.z32 = take(nsmall * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
+  w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
   w.hc = take(nsmall * D * 2);
   w.total = n32 ? off : 0;
   return w;

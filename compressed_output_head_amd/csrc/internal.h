@@ -64,7 +64,7 @@ struct FwdArgs {
   float* hscale;              // [n32]
   _Float16* zf;               // hi/lo pre-projection
   float* zscale;              // [n32]
-  float* z32;                 // [N][r] fp32 pre-projection (small-N decode path only)
+  float* z32;                 // [n32][r] fp32 pre-projection
   _Float16* hc;               // [N][D] scaled fp16 H rows in kernel k-order (small-N decode path only)
 };
 
