@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const FwdArgs a)
 // ring runs across block boundaries, so a wave never drains its pipeline.  H
 // (already scaled fp16 from the pre-projection kernel) and Z (fp32) sit in
 // LDS; LDS reads use the separate lgkm counter and never wait behind the ring.
-// Only lanes that carry a real token read H; the other MFMA rows are zero.
+// MFMA rows past the tokens read a zero row of H in LDS.
 constexpr int kLdsWaves = 4;
 constexpr int kLdsThreads = 64 * kLdsWaves;
 #ifndef ARCHEAD_DECODE_WG_PER_CU
@@ -184,9 +184,10 @@ __device__ __forceinline__ float code_at(const typename CodeVec<G>::T& v, int id
   }
 }
 
-// LDS carve-up of the small-N kernel: H as fp16 [N][D + 8] (8 halves of
-// padding per row spread the rows over the banks), then Z as fp32 [N][r].
-__host__ __device__ inline size_t lds_h_bytes(int64_t N, int64_t D) { return (size_t)N * (D + 8) * 2; }
+// LDS carve-up of the small-N kernel: H as fp16 [N + 1][D + 8] (8 halves of
+// padding per row spread the rows over the banks; row N is zero, read by the
+// MFMA lanes that carry no token), then Z as fp32 [N][r].
+__host__ __device__ inline size_t lds_h_bytes(int64_t N, int64_t D) { return (size_t)(N + 1) * (D + 8) * 2; }
 __host__ __device__ inline size_t lds_bytes(int64_t N, int64_t D, int r) {
   return lds_h_bytes(N, D) + (size_t)N * r * 4;
 }
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kLdsThreads) void decode_lds_kernel(const FwdArgs a
   __shared__ float s_hs[kDecodeLdsTokens];
   __shared__ int s_F[kDecodeLdsTokens];
   _Float16* sH = reinterpret_cast<_Float16*>(smem);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = (int)a.N;
   const int D = (int)a.D;
   const int ldh = D + 8;
@@ -228,62 +229,93 @@ __global__ __launch_bounds__(kLdsThreads) void decode_lds_kernel(const FwdArgs a
     return *reinterpret_cast<const CV*>(
         cbase + ((uint32_t)(blk * 16 + i16) * (uint32_t)ng + (uint32_t)(kt4 * 128 / G)));
   };
+  // epilogue sections: s_R [V16], A scales [V16][nA], A codes [V16][r]
+  const uint32_t v16 = (uint32_t)nb * 16u;
+  const __amdgpu_buffer_rsrc_t rrs = buffer_rsrc(a.r_rowscale, 2u * v16);
+  const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(a.a_scales, 2u * v16 * (uint32_t)a.nA);
+  const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a.a_codes, v16 * (uint32_t)r);
 
   int64_t b = (int64_t)blockIdx.x * kLdsWaves + wave;
   const int64_t b0 = b < nb ? b : nb - 1;  // waves without work load a valid block, store nothing
+  const int per_row = D / 8;
 
-  // the weight stream does not depend on H: start it before staging H and Z
+  // prologue, one round trip: this thread's first pieces of H, Z and the
+  // token scales, then the weight ring, then those pieces into LDS
+  constexpr int kPre = 2;
+  u4 hpre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int c = tid + i * kLdsThreads;
+    hpre[i] = c < N * per_row ? *reinterpret_cast<const u4*>(a.hc + (int64_t)(c / per_row) * D + 8 * (c % per_row))
+                              : u4{0u, 0u, 0u, 0u};
+  }
+  const float zpre = tid < N * r ? a.z32[tid] : 0.0f;
+  const float hspre = tid < N ? a.hscale[tid] : 0.0f;
   u4 wr[P];
   CV cv[NC];
 #pragma unroll
   for (int j = 0; j < P; ++j) wr[j] = tile_at(b0, j);
 #pragma unroll
   for (int c = 0; c < NC; ++c) cv[c] = codes_at(b0, 4 * c);
-
-  // prologue: H rows (scaled fp16), Z rows and per-token scales into LDS
-  const int per_row = D / 8;
-  for (int c = tid; c < N * per_row; c += kLdsThreads) {
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int c = tid + i * kLdsThreads;
+    if (c < N * per_row) *reinterpret_cast<u4*>(sH + (c / per_row) * ldh + 8 * (c % per_row)) = hpre[i];
+  }
+  if (tid < N * r) sZ[tid] = zpre;
+  if (tid < N) s_hs[tid] = hspre;
+  for (int c = tid; c < (D + 8) / 8; c += kLdsThreads)
+    *reinterpret_cast<u4*>(sH + N * ldh + 8 * c) = u4{0u, 0u, 0u, 0u};
+  for (int c = tid + kPre * kLdsThreads; c < N * per_row; c += kLdsThreads) {
     const int n = c / per_row, k8 = c - n * per_row;
     *reinterpret_cast<u4*>(sH + n * ldh + 8 * k8) =
         *reinterpret_cast<const u4*>(a.hc + (int64_t)n * D + 8 * k8);
   }
-  for (int c = tid; c < N * r; c += kLdsThreads) sZ[c] = a.z32[c];
-  for (int n = wave; n < N; n += kLdsWaves) {
-    float m = 0.0f;
-    for (int j = lane; j < r; j += 64) m = fmaxf(m, fabsf(a.z32[n * r + j]));
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (lane == 0) {
-      s_F[n] = row_exponent(m);
-      s_hs[n] = a.hscale[n];
-    }
-  }
+  for (int c = tid + kLdsThreads; c < N * r; c += kLdsThreads) sZ[c] = a.z32[c];
   __syncthreads();
   if (b >= nb) return;
 
   const bool real = i16 < N;
-  const _Float16* hrow = sH + (real ? i16 : 0) * ldh + 8 * q;
-  const int F = real ? s_F[i16] : 0;
+  const _Float16* hrow = sH + (real ? i16 : N) * ldh + 8 * q;
+  // per-token Z exponent from LDS: lanes i16 + 16 q split the ranks of token
+  // i16; every wave writes the same values to s_F
+  int F = 0;
+  {
+    float m = 0.0f;
+    if (real)
+      for (int j = q; j < r; j += 4) m = fmaxf(m, fabsf(sZ[i16 * r + j]));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    F = real ? row_exponent(m) : 0;
+    if (q == 0 && real) s_F[i16] = F;
+  }
 
-  for (; b < nb; b += nwaves) {
-    const int64_t bn = b + nwaves < nb ? b + nwaves : b;  // the ring's next block (or a harmless re-read)
+  int64_t bn = b + nwaves;
+  while (b < nb) {
+    const int64_t bnx = bn < nb ? bn : b;  // the ring's next block (or a harmless re-read)
     const int64_t v = 16 * b + i16;
-    // epilogue operands of this block, loaded now so they arrive long before use
-    const uint16_t sRb = a.r_rowscale[v];
-    const uint16_t sAcb = a.r_c > 0 ? a.a_scales[v * a.nA] : (uint16_t)0;
-    const uint16_t sAwb = a.r_r > 0 ? a.a_scales[v * a.nA + a.nA - 1] : (uint16_t)0;
-    const int8_t* arow = a.a_codes + v * r;
+    // epilogue operands of this block, loaded now so they arrive long before
+    // use: buffer loads with no branches (past a section's end they read zero),
+    // every choice made where the values are used, so nothing here waits
+    const uint32_t vv = (uint32_t)v;
+    const uint16_t sRb = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rrs, 2u * vv, 0, 0);
+    const uint16_t sAcb = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(srs, 2u * vv * (uint32_t)a.nA, 0, 0);
+    const uint16_t sAwb =
+        (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(srs, 2u * (vv * (uint32_t)a.nA + (uint32_t)a.nA - 1u), 0, 0);
     u2 araw[kEpiSteps];
 #pragma unroll
     for (int s = 0; s < kEpiSteps; ++s) {
-      araw[s] = u2{0u, 0u};
       const bool part_c = s < csteps;
       const int col = 32 * (part_c ? s : s - csteps) + 8 * q;
-      const int rank = part_c ? a.r_c : a.r_r;
-      if (s < esteps && col < rank) araw[s] = *reinterpret_cast<const u2*>(arow + (part_c ? 0 : a.r_c) + col);
+      araw[s] = __builtin_bit_cast(
+          u2, __builtin_amdgcn_raw_buffer_load_b64(ars, vv * (uint32_t)r + (uint32_t)((part_c ? 0 : a.r_c) + col), 0, 0));
     }
 
     f4 acc = {0.f, 0.f, 0.f, 0.f}, part = {0.f, 0.f, 0.f, 0.f};
-    for (int kt0 = 0; kt0 < nkt; kt0 += P) {
+    // nkt >= 4: the loop body runs at least once, which lets the compiler
+    // count the loads between the prefetches above and their use
+    int kt0 = 0;
+    do {
 #pragma unroll
       for (int j = 0; j < P; ++j) {
         // keep the scheduler from hoisting work of later ring slots
@@ -294,8 +326,7 @@ __global__ __launch_bounds__(kLdsThreads) void decode_lds_kernel(const FwdArgs a
         for (int s = 0; s < 4; ++s) c[s] = code_at<G>(cv[j / 4], (128 * (j & 3) + 32 * s) / G);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          h8 hv = h8{0, 0, 0, 0, 0, 0, 0, 0};
-          if (real) hv = *reinterpret_cast<const h8*>(hrow + 32 * (4 * kt + s));
+          const h8 hv = *reinterpret_cast<const h8*>(hrow + 32 * (4 * kt + s));
           part = mfma16(hv, unpack_q4(wr[j][s]), part);
           // a group of g columns ends after this 32-column step
           const bool flush = ((128 * (j & 3) + 32 * (s + 1)) % G) == 0;
@@ -307,31 +338,25 @@ __global__ __launch_bounds__(kLdsThreads) void decode_lds_kernel(const FwdArgs a
         {
           // refill the slot with the tile P positions ahead in this wave's sequence
           const bool same = kt + P < nkt;
-          wr[j] = tile_at(same ? b : bn, same ? kt + P : kt + P - nkt);
+          wr[j] = tile_at(same ? b : bnx, same ? kt + P : kt + P - nkt);
           if ((j & 3) == 3) {
             const int k4 = kt - 3 + P;  // first tile of the chunk this code slot serves next
-            cv[j / 4] = codes_at(k4 < nkt ? b : bn, k4 < nkt ? k4 : k4 - nkt);
+            cv[j / 4] = codes_at(k4 < nkt ? b : bnx, k4 < nkt ? k4 : k4 - nkt);
           }
         }
       }
-    }
+      kt0 += P;
+    } while (kt0 < nkt);
 
     // epilogue: row scale, low-rank term (Z hi/lo from LDS against exact INT8
     // A codes, one accumulator per part), store
     f4 pc = {0.f, 0.f, 0.f, 0.f}, pw = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < esteps; ++s) {
+    auto low_rank_step = [&](int s, u2 raw) {
       const bool part_c = s < csteps;
       const int col = 32 * (part_c ? s : s - csteps) + 8 * q;
       const int rank = part_c ? a.r_c : a.r_r;
       const int base = part_c ? 0 : a.r_c;
-      u2 raw = {0u, 0u};
-      if (s < kEpiSteps) {
-#pragma unroll
-        for (int t = 0; t < kEpiSteps; ++t)
-          if (t == s) raw = araw[t];
-      } else if (col < rank) {
-        raw = *reinterpret_cast<const u2*>(arow + base + col);
-      }
+      if (col >= rank) raw = u2{0u, 0u};
       const h8 av = unpack_i8x8(raw[0], raw[1]);
       h8 zh, zl;
 #pragma unroll
@@ -348,9 +373,27 @@ __global__ __launch_bounds__(kLdsThreads) void decode_lds_kernel(const FwdArgs a
         pw = mfma16(zh, av, pw);
         pw = mfma16(zl, av, pw);
       }
+    };
+    if (esteps <= kEpiSteps) {  // every A code was prefetched
+#pragma unroll
+      for (int s = 0; s < kEpiSteps; ++s)
+        if (s < esteps) low_rank_step(s, araw[s]);
+    } else {
+      const int8_t* arow = a.a_codes + v * r;
+#pragma unroll
+      for (int s = 0; s < kEpiSteps; ++s) low_rank_step(s, araw[s]);
+      for (int s = kEpiSteps; s < esteps; ++s) {
+        const bool part_c = s < csteps;
+        const int col = 32 * (part_c ? s : s - csteps) + 8 * q;
+        const int rank = part_c ? a.r_c : a.r_r;
+        u2 raw = {0u, 0u};
+        if (col < rank) raw = *reinterpret_cast<const u2*>(arow + (part_c ? 0 : a.r_c) + col);
+        low_rank_step(s, raw);
+      }
     }
     if (v < a.V) {
-      const float sR = f16_to_f32(sRb), sAc = f16_to_f32(sAcb), sAw = f16_to_f32(sAwb);
+      const float sR = f16_to_f32(sRb);
+      const float sAc = a.r_c > 0 ? f16_to_f32(sAcb) : 0.0f, sAw = a.r_r > 0 ? f16_to_f32(sAwb) : 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int n = 4 * q + e;
@@ -363,6 +406,8 @@ __global__ __launch_bounds__(kLdsThreads) void decode_lds_kernel(const FwdArgs a
           reinterpret_cast<float*>(a.Y)[n * a.Y_stride + v] = y;
       }
     }
+    b = bn;
+    bn = b + nwaves;
   }
 }
 

@@ -115,6 +115,14 @@ __device__ __forceinline__ int row_exponent(float maxabs) {
   return 15 - e;
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+// The size is made wave-uniform explicitly: a resource the compiler believes
+// divergent is used through a loop over lanes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 // 16 x 16 x 32: lane l holds A row l%16 / B column l%16, k 8*(l/16) .. +8;
 // result lane l holds rows 4*(l/16) + e, column l%16.
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {

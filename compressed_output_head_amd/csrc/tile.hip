@@ -215,13 +215,6 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// A buffer resource over [base, base + bytes).  The size is made wave-uniform
-// explicitly: a resource the compiler believes divergent is used through a
-// loop over lanes.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
 
 // f(integral_constant<I>) for I = B .. E-1, unrolled at compile time
 template <int B, int E, class F>
