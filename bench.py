@@ -184,14 +184,19 @@ def run_workload(name, steps, warmup, path=0):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     # dominant-kernel duration: the library records these events on the launch
-    # stream right before and after the main kernel
+    # stream right before and after the main kernel.  Each instrumented call
+    # runs on an idle queue (synchronized before the next one): with calls
+    # queued back to back the start marker waits behind the previous call and
+    # the pre-projection, and the span then includes dispatch gaps that are
+    # not the kernel's
     evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     eve = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for e in evb + eve:
         e.record(stream)  # creates the underlying hipEvent
+    torch.cuda.synchronize()
     for i in range(steps):
         ah.archead_logits_events(H, heads[i % 2], Y, path, evb[i], eve[i])
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     kms = [evb[i].elapsed_time(eve[i]) for i in range(steps)]
     A = algorithmic(cfg, L, N)
     return dict(cfg=cfg, L=L, A=A, ms=ms, kernel=dominant_kernel(N), kernel_ms=float(np.mean(kms)),
