@@ -144,8 +144,6 @@ def dominant_kernel(N):
     """Name of the main kernel the library launches for N tokens (automatic path)."""
     if N <= 16:
         return "decode_lds_kernel"
-    if N <= 64:
-        return "mid_kernel"
     return "tile32_kernel"
 
 
@@ -204,9 +202,9 @@ def run_workload(name, steps, warmup, path=0):
 
 
 def tile_workload(N):
-    """Workloads of more than 64 tokens run the MFMA tile kernel and are
-    reported in TFLOP/s against the MFMA peak; smaller ones in GB/s of packed
-    head bytes against the HBM peak."""
+    """Workloads of more than 64 tokens are bound by the MFMA and reported in
+    TFLOP/s against its peak; up to 64 tokens the head's bytes bound the call,
+    reported in GB/s of packed head bytes against the HBM peak."""
     return N > 64
 
 

@@ -300,11 +300,13 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
-  const bool decode = path == ARCHEAD_PATH_DECODE || (path == ARCHEAD_PATH_AUTO && N <= kDecodeMaxTokens);
-  // decode path: the LDS kernel for a few tokens, else the batched kernel
-  // (the 16-row decode kernel only when offsets exceed 32 bits); tile path: the
+  // auto: the LDS decode kernel for a few tokens, else the tile path.
+  // decode path: the LDS kernel when it applies, else the batched kernel (the
+  // 16-row decode kernel only when offsets exceed 32 bits); tile path: the
   // 32-row kernel unless offsets exceed 32 bits (launch_tile decides the same way)
-  const bool small = decode && decode_lds_eligible(a);
+  const bool small = (path == ARCHEAD_PATH_DECODE || (path == ARCHEAD_PATH_AUTO && N <= kDecodeMaxTokens)) &&
+                     decode_lds_eligible(a);
+  const bool decode = path == ARCHEAD_PATH_DECODE || small;
   const bool mid = decode && !small && mid_eligible(a);
   const bool rows32 = mid || (!decode && tile32_eligible(a));
   if ((small ? launch_prep_z(a, s) : launch_prep(a, rows32, s)) != hipSuccess) return ARCHEAD_E_HIP;

@@ -171,33 +171,22 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const FwdArgs a) {
 // run, and the next stage's first step is fetched right after the barrier
 // that publishes it.  Every global read goes through a buffer resource: a
 // wave-uniform offset plus a small per-lane one.
-constexpr int kT32TT = 8;  // 32-token tiles per workgroup
-constexpr int kT32CB = 8;  // 32-row vocabulary blocks per workgroup
-#ifndef ARCHEAD_T32_WM
-#define ARCHEAD_T32_WM 1
-#endif
-constexpr int kT32Waves = 8;
-constexpr int kT32WM = ARCHEAD_T32_WM;       // waves along the tokens
-constexpr int kT32WN = kT32Waves / kT32WM;   // waves along the vocabulary
+// TT (a template parameter): 32-token tiles per workgroup, 2, 4 or 8
+constexpr int kT32CB = 8;     // 32-row vocabulary blocks per workgroup
+constexpr int kT32Waves = 8;  // one wave per vocabulary block; every wave takes all the tokens
 constexpr int kT32Threads = 64 * kT32Waves;
-constexpr int kT32MT = kT32TT / kT32WM;      // token tiles per wave
-constexpr int kT32WCB = kT32CB / kT32WN;     // vocabulary blocks per wave
-static_assert(kT32MT % 4 == 0, "the epilogue's Z slots assume whole groups of 4 token tiles per wave");
+constexpr int kT32WCB = 1;    // vocabulary blocks per wave
 constexpr int kT32Ahead = 4;  // stages between a load's issue and its stage (H: 4 LDS slots, W: 4 register slots)
-constexpr int kT32HOps = kT32TT * 4 / kT32Waves;  // H copies per wave and stage
-constexpr int kT32WOps = kT32WCB;                // W loads per wave and stage
+constexpr int kT32WOps = kT32WCB;  // W loads per wave and stage
 constexpr int kT32MaxCodes = 64;  // group codes per row the workgroup can hold in LDS
 // LDS row stride of the group codes: an odd number of dwords, so the 32 rows
 // one wave reads at a time fall in 32 different banks
 __host__ __device__ constexpr int t32_code_stride(int ng) { return 4 * (((ng + 3) / 4) | 1); }
 constexpr int kT32Group = 4;  // token tiles that walk the vocabulary together
-constexpr int kEpiChunk = kT32WCB >= 4 ? 4 : 2;  // low-rank rank steps whose loads are issued together
+constexpr int kEpiChunk = 2;  // low-rank rank steps whose loads are issued together
 constexpr int kEpiLdsSteps = 8;  // up to 128 padded ranks: Z of the workgroup fits the H ring
 constexpr int kXcds = 8;
 
-// s_waitcnt immediate: wait until at most n vector-memory operations of this
-// wave are outstanding (expcnt and lgkmcnt not waited on)
-__device__ constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
 
 // Workgroup barrier for the LDS ring: this wave's copies up to the last n
 // vector-memory operations and all its LDS reads are complete, then every
@@ -232,13 +221,20 @@ struct Acc4 {  // low-rank accumulators of one wave's vocabulary blocks
 struct T32Grid {
   int ntiles, ncb, ttiles, vtiles;
 };
-__host__ __device__ inline T32Grid t32_grid(const FwdArgs& a) {
+__host__ __device__ inline T32Grid t32_grid(const FwdArgs& a, int tt) {
   T32Grid t;
   t.ntiles = (int)(a.n32 >> 5);
   t.ncb = (int)((a.nb + 1) >> 1);
-  t.ttiles = (t.ntiles + kT32TT - 1) / kT32TT;
+  t.ttiles = (t.ntiles + tt - 1) / tt;
   t.vtiles = (t.ncb + kT32CB - 1) / kT32CB;
   return t;
+}
+
+// One 16-byte buffer-to-LDS copy per lane.  Kept out of the kernel template:
+// called from inside it directly, the builtin makes the host pass reject the
+// template's instantiation without a diagnostic, and no launch stub is made.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rs, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
 }
 
 // GC: group codes per k-tile and row that one stage needs: 0 -> one (g >= 128),
@@ -249,17 +245,22 @@ __host__ __device__ inline T32Grid t32_grid(const FwdArgs& a) {
 // for all copies in flight.  T32_SLOT(S) names slot S (S a constant).
 #define T32_SLOT(S) (*((S) == 0 ? &sH0 : (S) == 1 ? &sH1 : (S) == 2 ? &sH2 : &sH3))
 
-template <int GC>
-__global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
+// Small TT streams the head with little reuse per weight: ask for registers
+// that let two workgroups (four waves per SIMD) share a CU.
+template <int GC, int TT>
+__global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(const FwdArgs a) {
+  constexpr int kT32TT = TT, kT32MT = TT;     // token tiles per workgroup and per wave
+  constexpr int kT32HOps = TT * 4 / kT32Waves;  // H copies per wave and stage
+  static_assert(kT32HOps >= 1 && TT * 4 == kT32HOps * kT32Waves, "TT must be 2, 4 or 8");
   __shared__ h8 sH0[kT32TT][4][64], sH1[kT32TT][4][64], sH2[kT32TT][4][64], sH3[kT32TT][4][64];
-  __shared__ __align__(16) uint8_t sCode[kT32CB * 32 * t32_code_stride(kT32MaxCodes)];  // [row][stride]
+  extern __shared__ __align__(16) uint8_t sCode[];  // [256 rows][t32_code_stride(ng)], sized at launch
   __shared__ float sTok[kT32TT * 32][2];  // hscale, zscale of the workgroup's tokens
   __shared__ __align__(16) float sVR[kT32CB * 32], sVC[kT32CB * 32], sVW[kT32CB * 32];  // s_R, s_Ac, s_Aw
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kT32WN, wn = wave % kT32WN;
+  const int wm = 0, wn = wave;  // wave row 0: every wave takes all the tokens
   const int g = lane >> 5, c32 = lane & 31;
-  const T32Grid G = t32_grid(a);
+  const T32Grid G = t32_grid(a, TT);
 
   // Workgroups are dealt to the XCDs round robin; renumber them so each XCD
   // owns one contiguous range, and walk it kT32Group token tiles at a time
@@ -306,8 +307,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < kT32HOps; ++i) {
       const int f = kT32Waves * i + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, &T32_SLOT(S)[f >> 2][f & 3][0], 16, lane16,
-                                               hoff[i] + (uint32_t)ks * 4096u, 0, 0);
+      lds_copy16(hrs, &T32_SLOT(S)[f >> 2][f & 3][0], lane16, hoff[i] + (uint32_t)ks * 4096u);
     }
   };
 
@@ -364,11 +364,14 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     for (int s = 0; s < kEpiLdsSteps; ++s) ac[cb][s] = zlds && s < esteps ? a_code(cb, s) : u2{0u, 0u};
   // Entry j of the copy sequence into slot j % 4: H stage j for j < nS; past
   // the last stage, Z of the workgroup (or the last stage again when Z is
-  // read from memory in the epilogue).  Slot S holds the Z fragments of token
-  // tiles S and S + 4, fragment w2 * zper + rem at the position an H fragment
-  // would take; positions past 2 zper repeat the last fragment.  The source
-  // is a uniform select, so every copy has the same form as an H copy.
+  // read from memory in the epilogue).  Token tile tt's Z fragment rem sits
+  // at z = tt * 2^zsh + rem (2^zsh the power of two >= zper, at most 16, so
+  // all TT tiles fit the ring's 16 TT positions): slot z / (4 TT), the
+  // position z % (4 TT) an H fragment would take.  Positions past a tile's
+  // fragments repeat one of them.  The source is a uniform select, so every
+  // copy has the same form as an H copy.
   const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(a.zf, (uint32_t)(a.n32 * (a.rc32 + a.rr32) * 4));
+  const int zsh = zper <= 1 ? 0 : 32 - __builtin_clz((unsigned)(zper - 1));
   auto load_slot = [&](int j, auto S_) {
     constexpr int S = decltype(S_)::value;
     const bool zsrc = j >= nS && zlds;
@@ -376,12 +379,13 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < kT32HOps; ++i) {
       const int f = kT32Waves * i + wave;
-      const int fz = f < 2 * zper ? f : 2 * zper - 1;
-      const int w2 = fz >= zper ? 1 : 0, rem = fz - w2 * zper, tt = S + 4 * w2;
+      const int z = 4 * kT32TT * S + f;
+      int tt = z >> zsh, rem = z & ((1 << zsh) - 1);
+      if (tt > kT32TT - 1) tt = kT32TT - 1;
+      if (rem > zper - 1) rem = zper - 1;  // zper = 0: negative, read past the end as zero
       const int T = tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1;  // padding tiles are never stored
       const uint32_t off = zsrc ? (uint32_t)(T * zper + rem) * 1024u : hoff[i] + (uint32_t)jh * 4096u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(zsrc ? zrs : hrs, &T32_SLOT(S)[f >> 2][f & 3][0], 16, lane16,
-                                               off, 0, 0);
+      lds_copy16(zsrc ? zrs : hrs, &T32_SLOT(S)[f >> 2][f & 3][0], lane16, off);
     }
   };
 
@@ -435,6 +439,9 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
     const int64_t tok = std::min<int64_t>(32 * (int64_t)tt0 + tid, a.n32 - 1);
     sTok[tid][0] = a.hscale[tok];
     sTok[tid][1] = a.zscale[tok];
+  }
+  static_assert(kT32Threads >= kT32CB * 32, "one thread per vocabulary row of the workgroup");
+  if (tid < kT32CB * 32) {
     const int64_t v = std::min<int64_t>(32 * (int64_t)vt * kT32CB + tid, 16 * a.nb - 1);
     sVR[tid] = f16_to_f32(a.r_rowscale[v]);
     sVC[tid] = a.r_c > 0 ? f16_to_f32(a.a_scales[v * a.nA]) : 0.0f;
@@ -594,6 +601,15 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
   // epilogue with the split between the two low-rank parts fixed at compile
   // time (csteps is even), the row scales in registers and buffer stores at
   // uniform offsets.
+  // Z fragment rem of the workgroup's token tile tt from the ring (rem past
+  // the tile's fragments reads a copy or an old H fragment; its A codes are 0)
+  auto zfrag = [&](int tt, int rem) {
+    int z = (tt << zsh) + rem;
+    if (z > 16 * kT32TT - 1) z = 16 * kT32TT - 1;
+    const int slot = z / (4 * kT32TT), pos = z - slot * 4 * kT32TT;
+    const h8* base = slot == 0 ? &sH0[0][0][0] : slot == 1 ? &sH1[0][0][0] : slot == 2 ? &sH2[0][0][0] : &sH3[0][0][0];
+    return base[pos * 64 + lane];
+  };
   const uint64_t es = a.y_bf16 ? 2 : 4;
   const bool fast = zlds && vec && 32 * (int64_t)(tt0 + kT32TT) <= a.N &&
                     32 * ((int64_t)vt * kT32CB + kT32CB) <= a.V &&
@@ -615,14 +631,12 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
       auto low_rank = [&](auto J_, f16x& pc, f16x& pw) {
         constexpr int m = decltype(J_)::value / kT32WCB, cb = decltype(J_)::value % kT32WCB;
         const int tt = kT32MT * wm + m;
-        const int f0 = (tt >> 2) * zper;  // Z of token tile tt: slot tt % 4 = m % 4
         pc = f16x{};
         pw = f16x{};
         static_for<0, kEpiLdsSteps>([&](auto S_) {
           constexpr int s = decltype(S_)::value;
-          const int fh = f0 + 2 * s, fl = fh + 1;  // within the slot (past 2 zper: copies, A codes are 0)
-          const h8 zh = T32_SLOT(m & 3)[fh >> 2][fh & 3][lane];
-          const h8 zl = T32_SLOT(m & 3)[fl >> 2][fl & 3][lane];
+          const h8 zh = zfrag(tt, 2 * s);  // past the tile's zper: its A codes are 0
+          const h8 zl = zfrag(tt, 2 * s + 1);
           const h8 av = unpack_i8x8(ac[cb][s][0], ac[cb][s][1]);
           if constexpr (s < CS) {
             pc = mfma32(av, zh, pc);
@@ -691,7 +705,7 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
       constexpr int m = decltype(M_)::value, cp = kEpiBlocks * decltype(P_)::value;
       const int tt = kT32MT * wm + m;
       if (tt0 + tt >= G.ntiles) return;
-      const int f0 = (tt >> 2) * zper;  // in slot tt % 4 = m % 4
+
       f16x pc[kEpiBlocks], pw[kEpiBlocks];
 #pragma unroll
       for (int j = 0; j < kEpiBlocks; ++j) {
@@ -701,9 +715,8 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 #pragma unroll
       for (int s = 0; s < kEpiLdsSteps; ++s) {
         if (s < esteps) {
-          const int fh = f0 + 2 * s, fl = fh + 1;
-          const h8 zh = T32_SLOT(m & 3)[fh >> 2][fh & 3][lane];
-          const h8 zl = T32_SLOT(m & 3)[fl >> 2][fl & 3][lane];
+          const h8 zh = zfrag(tt, 2 * s);
+          const h8 zl = zfrag(tt, 2 * s + 1);
           h8 av[kEpiBlocks];
 #pragma unroll
           for (int j = 0; j < kEpiBlocks; ++j) av[j] = aun[cp + j][s];
@@ -778,27 +791,41 @@ __global__ __launch_bounds__(kT32Threads) void tile32_kernel(const FwdArgs a) {
 
 // The 32 x 32 x 16 kernel serves N > 128 when every section it reads fits
 // 32-bit buffer offsets.
+// Token tiles per workgroup: 64 tokens for N <= 64, 128 for N <= 128, else 256.
+static int t32_tt(int64_t N) { return N <= 64 ? 2 : N <= 128 ? 4 : 8; }
+
+// The 32 x 32 x 16 kernel serves any N whose sections fit 32-bit buffer
+// offsets and whose group codes fit the workgroup's LDS table.
 bool tile32_eligible(const FwdArgs& a) {
-  if (a.N <= 128) return false;
   if ((uint64_t)a.nb * 16 * (uint64_t)a.D / 2 >= (1ull << 32)) return false;
   if (a.ng > kT32MaxCodes) return false;
   if (((uint64_t)a.nb * 16 + kT32CB * 32) * (uint64_t)a.ng >= (1ull << 32)) return false;
   if ((uint64_t)a.n32 * (uint64_t)a.D * 2 >= (1ull << 32)) return false;
-  const T32Grid G = t32_grid(a);
+  const T32Grid G = t32_grid(a, t32_tt(a.N));
   return (int64_t)G.ttiles * G.vtiles < (1ll << 31);
+}
+
+template <int TT>
+static hipError_t launch_t32(const FwdArgs& a, hipStream_t s) {
+  const T32Grid G = t32_grid(a, TT);
+  const dim3 grid((unsigned)(G.ttiles * G.vtiles)), block(kT32Threads);
+  const size_t codes = (size_t)kT32CB * 32 * t32_code_stride(a.ng);  // dynamic LDS: the group-code table
+  if (a.g == 32)
+    hipLaunchKernelGGL((tile32_kernel<2, TT>), grid, block, codes, s, a);
+  else if (a.g == 64)
+    hipLaunchKernelGGL((tile32_kernel<1, TT>), grid, block, codes, s, a);
+  else
+    hipLaunchKernelGGL((tile32_kernel<0, TT>), grid, block, codes, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_tile(const FwdArgs& a, hipStream_t s) {
   if (tile32_eligible(a)) {
-    const T32Grid G = t32_grid(a);
-    const dim3 grid((unsigned)(G.ttiles * G.vtiles)), block(kT32Threads);
-    if (a.g == 32)
-      hipLaunchKernelGGL(tile32_kernel<2>, grid, block, 0, s, a);
-    else if (a.g == 64)
-      hipLaunchKernelGGL(tile32_kernel<1>, grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL(tile32_kernel<0>, grid, block, 0, s, a);
-    return hipGetLastError();
+    switch (t32_tt(a.N)) {
+      case 2: return launch_t32<2>(a, s);
+      case 4: return launch_t32<4>(a, s);
+      default: return launch_t32<8>(a, s);
+    }
   }
   constexpr int TM = 64, TN = 64, WM = 2, WN = 2;
   using C = TileCfg<TM, TN, WM, WN>;

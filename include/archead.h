@@ -59,7 +59,7 @@ typedef enum {
 typedef enum { ARCHEAD_BF16 = 1, ARCHEAD_F32 = 2 } archead_dtype;
 
 typedef enum {
-  ARCHEAD_PATH_AUTO = 0,   /* N <= 64: decode path; N > 64: tile path            */
+  ARCHEAD_PATH_AUTO = 0,   /* up to 16 tokens whose H and Z fit LDS: decode path; else tile path */
   ARCHEAD_PATH_DECODE = 1, /* skinny path (streams the head once for all N <= 64 tokens) */
   ARCHEAD_PATH_TILE = 2    /* LDS-tiled MFMA path (any N)                          */
 } archead_path;
