@@ -78,6 +78,8 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens) {
   const uint64_t nsmall = n_tokens <= kDecodeLdsTokens ? (uint64_t)std::max<int64_t>(n_tokens, 0) : 0;
   w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
   w.hc = take(nsmall * D * 2);
+  w.split_bytes = n_tokens > kDecodeLdsTokens ? kSplitBytes : 0;
+  w.split = take(w.split_bytes);
   w.total = n32 ? off : 0;
   return w;
 }
@@ -297,6 +299,8 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   a.zscale = reinterpret_cast<float*>(ws + W.zscale);
   a.z32 = reinterpret_cast<float*>(ws + W.z32);
   a.hc = reinterpret_cast<_Float16*>(ws + W.hc);
+  a.part = W.split_bytes ? reinterpret_cast<float*>(ws + W.split) : nullptr;
+  a.part_bytes = W.split_bytes;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state

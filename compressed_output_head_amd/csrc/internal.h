@@ -16,6 +16,10 @@ constexpr int kDecodeMaxTokens = 64;
 constexpr int kDecodeLdsTokens = 16;
 // LDS budget of that kernel: N*(D+8)*2 bytes of H plus N*r*4 bytes of Z.
 constexpr uint64_t kDecodeLdsBytes = 48 * 1024;
+// Workspace for the fp32 partial sums of tiles whose hidden dimension the
+// tile kernel splits over several workgroups (calls of more than
+// kDecodeLdsTokens tokens).
+constexpr uint64_t kSplitBytes = 64ull << 20;
 
 inline uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -31,7 +35,7 @@ struct WorkspaceLayout {
   int64_t n32;          // tokens rounded up to 32 (rows of every per-token workspace section)
   int rc32, rr32;       // ranks rounded up to 32
   int zsteps;           // (rc32 + rr32) / 32
-  uint64_t hf, hscale, zf, zscale, z32, hc, total;
+  uint64_t hf, hscale, zf, zscale, z32, hc, split, split_bytes, total;
 };
 WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens);
 
@@ -66,6 +70,8 @@ struct FwdArgs {
   float* zscale;              // [n32]
   float* z32;                 // [n32][r] fp32 pre-projection
   _Float16* hc;               // [N][D] scaled fp16 H rows in kernel k-order (small-N decode path only)
+  float* part;                // fp32 partial sums of split tiles (null: no room, tiles are not split)
+  uint64_t part_bytes;
 };
 
 hipError_t launch_prep(const FwdArgs& a, bool rows32, hipStream_t s);

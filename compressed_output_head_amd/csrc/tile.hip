@@ -177,11 +177,14 @@ constexpr int kT32Waves = 8;  // one wave per vocabulary block; every wave takes
 constexpr int kT32Threads = 64 * kT32Waves;
 constexpr int kT32WCB = 1;    // vocabulary blocks per wave
 constexpr int kT32Ahead = 4;  // stages between a load's issue and its stage (H: 4 LDS slots, W: 4 register slots)
-constexpr int kT32WOps = kT32WCB;  // W loads per wave and stage
 constexpr int kT32MaxCodes = 64;  // group codes per row the workgroup can hold in LDS
 // LDS row stride of the group codes: an odd number of dwords, so the 32 rows
 // one wave reads at a time fall in 32 different banks
 __host__ __device__ constexpr int t32_code_stride(int ng) { return 4 * (((ng + 3) / 4) | 1); }
+// MFMA steps (of 16 columns) per stage: the LDS ring holds 4 stages of TT KS
+// 1 KB H fragments, so smaller token tiles take longer stages and keep more
+// of the head in flight
+__host__ __device__ constexpr int t32_ks(int tt) { return tt <= 4 ? 8 : 4; }
 constexpr int kT32Group = 4;  // token tiles that walk the vocabulary together
 constexpr int kEpiChunk = 2;  // low-rank rank steps whose loads are issued together
 constexpr int kEpiLdsSteps = 8;  // up to 128 padded ranks: Z of the workgroup fits the H ring
@@ -230,6 +233,29 @@ __host__ __device__ inline T32Grid t32_grid(const FwdArgs& a, int tt) {
   return t;
 }
 
+// Tile L of the walk order: groups of kT32Group token tiles walk the
+// vocabulary together (the last group may be narrower).
+__host__ __device__ inline void t32_tile(const T32Grid& G, int L, int& vt, int& ttile) {
+  const int groups = G.ttiles / kT32Group, span = kT32Group * G.vtiles;
+  if (L < groups * span) {
+    const int rr = L % span;
+    vt = rr / kT32Group;
+    ttile = (L / span) * kT32Group + rr % kT32Group;
+  } else {
+    const int w = G.ttiles - groups * kT32Group, rr = L - groups * span;
+    vt = rr / w;
+    ttile = groups * kT32Group + rr % w;
+  }
+}
+
+// Tiles full .. (all tiles - 1) of the walk order (the last, partly filled
+// round of workgroups) are each split into s parts of the hidden dimension:
+// workgroup full + s j + p computes part p of tile full + j and writes fp32
+// partial sums, which t32_reduce_kernel adds up in part order.
+struct T32Split {
+  int full, s;
+};
+
 // One 16-byte buffer-to-LDS copy per lane.  Kept out of the kernel template:
 // called from inside it directly, the builtin makes the host pass reject the
 // template's instantiation without a diagnostic, and no launch stub is made.
@@ -245,14 +271,16 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rs, void* dst,
 // for all copies in flight.  T32_SLOT(S) names slot S (S a constant).
 #define T32_SLOT(S) (*((S) == 0 ? &sH0 : (S) == 1 ? &sH1 : (S) == 2 ? &sH2 : &sH3))
 
-// Small TT streams the head with little reuse per weight: ask for registers
-// that let two workgroups (four waves per SIMD) share a CU.
 template <int GC, int TT>
-__global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(kT32Threads, 1) void tile32_kernel(const FwdArgs a, const T32Split sp) {
   constexpr int kT32TT = TT, kT32MT = TT;     // token tiles per workgroup and per wave
-  constexpr int kT32HOps = TT * 4 / kT32Waves;  // H copies per wave and stage
-  static_assert(kT32HOps >= 1 && TT * 4 == kT32HOps * kT32Waves, "TT must be 2, 4 or 8");
-  __shared__ h8 sH0[kT32TT][4][64], sH1[kT32TT][4][64], sH2[kT32TT][4][64], sH3[kT32TT][4][64];
+  constexpr int KS = t32_ks(TT);              // MFMA steps per stage
+  constexpr int kLK = KS == 8 ? 3 : 2;        // log2(KS)
+  constexpr int kSPT = 8 / KS;                // stages per 128-column k-tile
+  constexpr int kT32HOps = TT * KS / kT32Waves;  // H copies per wave and stage
+  constexpr int kWOps = kT32WCB * KS / 4;        // W loads per wave and stage
+  static_assert(kT32HOps >= 1 && TT * KS == kT32HOps * kT32Waves, "TT must be 2, 4 or 8");
+  __shared__ h8 sH0[kT32TT][KS][64], sH1[kT32TT][KS][64], sH2[kT32TT][KS][64], sH3[kT32TT][KS][64];
   extern __shared__ __align__(16) uint8_t sCode[];  // [256 rows][t32_code_stride(ng)], sized at launch
   __shared__ float sTok[kT32TT * 32][2];  // hscale, zscale of the workgroup's tokens
   __shared__ __align__(16) float sVR[kT32CB * 32], sVC[kT32CB * 32], sVW[kT32CB * 32];  // s_R, s_Ac, s_Aw
@@ -262,59 +290,64 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
   const int g = lane >> 5, c32 = lane & 31;
   const T32Grid G = t32_grid(a, TT);
 
-  // Workgroups are dealt to the XCDs round robin; renumber them so each XCD
-  // owns one contiguous range, and walk it kT32Group token tiles at a time
-  // across the vocabulary, so the workgroups resident on one XCD share a few
-  // H row sets and packed vocabulary tiles in its L2.
-  int L;
-  {
-    const int grid = G.ttiles * G.vtiles, b = blockIdx.x;
-    const int per = grid / kXcds, rem = grid % kXcds, x = b % kXcds;
+  // Workgroups are dealt to the XCDs round robin.  Those that take whole
+  // tiles are renumbered so each XCD owns one contiguous range of the walk
+  // order, so the workgroups resident on one XCD share a few H row sets and
+  // packed vocabulary tiles in its L2.  The rest take one part of the hidden
+  // dimension of a split tile.
+  const int b = blockIdx.x;
+  const bool split = b >= sp.full;
+  int L, part = 0;
+  if (!split) {
+    const int per = sp.full / kXcds, rem = sp.full % kXcds, x = b % kXcds;
     L = x * per + (x < rem ? x : rem) + b / kXcds;
+  } else {
+    const int q = b - sp.full, j = q / sp.s;
+    L = sp.full + j;
+    part = q - j * sp.s;
   }
   int vt, ttile;
-  {
-    const int full = G.ttiles / kT32Group, span = kT32Group * G.vtiles;
-    if (L < full * span) {
-      const int rr = L % span;
-      vt = rr / kT32Group;
-      ttile = (L / span) * kT32Group + rr % kT32Group;
-    } else {
-      const int w = G.ttiles - full * kT32Group, rr = L - full * span;
-      vt = rr / w;
-      ttile = full * kT32Group + rr % w;
-    }
-  }
+  t32_tile(G, L, vt, ttile);
   const int tt0 = ttile * kT32TT;           // first 32-token tile
   const int cb0 = vt * kT32CB + wn * kT32WCB;  // first vocabulary block of this wave
-  const int nS = (int)(a.D / 64);           // stages (even, at least 2)
+  // stages of 16 KS columns: all of them (at least 2), or this part's share
+  // of whole k-tiles (at least 4 stages: the host splits a tile in at most a
+  // quarter as many parts as it has stages)
+  int kb = 0, nS = (int)(a.D / (16 * KS));
+  if (split) {
+    const int nu = nS / kSPT;
+    kb = kSPT * (part * nu / sp.s);
+    nS = kSPT * ((part + 1) * nu / sp.s) - kb;
+  }
 
-  // H: the 32 fragments of a stage (8 token tiles x 4 MFMA steps) are spread
-  // over the waves, fragment f = kT32Waves i + wave being token tile f / 4,
-  // step f % 4.  Token tiles past the last re-read the last one: their rows
-  // are never stored.
+  // H: the TT KS fragments of a stage (TT token tiles x KS MFMA steps) are
+  // spread over the waves, fragment f = kT32Waves i + wave being token tile
+  // f / KS, step f % KS.  Token tiles past the last re-read the last one:
+  // their rows are never stored.
   const __amdgpu_buffer_rsrc_t hrs = buffer_rsrc(a.hf, (uint32_t)(a.n32 * a.D * 2));
   const uint32_t lane16 = (uint32_t)lane * 16u;
   const uint32_t hT = (uint32_t)a.nkt * 8192u;  // bytes per token tile
   uint32_t hoff[kT32HOps];
 #pragma unroll
   for (int i = 0; i < kT32HOps; ++i) {
-    const int f = kT32Waves * i + wave, tt = f >> 2;
-    hoff[i] = (uint32_t)(tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1) * hT + (uint32_t)(f & 3) * 1024u;
+    const int f = kT32Waves * i + wave, tt = f >> kLK;
+    hoff[i] = (uint32_t)(tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1) * hT + (uint32_t)(f & (KS - 1)) * 1024u +
+              (uint32_t)kb * (KS * 1024u);
   }
   auto load_h = [&](int ks, auto S_) {
     constexpr int S = decltype(S_)::value;
 #pragma unroll
     for (int i = 0; i < kT32HOps; ++i) {
       const int f = kT32Waves * i + wave;
-      lds_copy16(hrs, &T32_SLOT(S)[f >> 2][f & 3][0], lane16, hoff[i] + (uint32_t)ks * 4096u);
+      lds_copy16(hrs, &T32_SLOT(S)[f >> kLK][f & (KS - 1)][0], lane16, hoff[i] + (uint32_t)ks * (KS * 1024u));
     }
   };
 
   // W: per-lane byte offsets of this lane's row in each of its blocks (a
   // block past the end re-reads the last one; its results are never stored)
-  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(a.r_codes, (uint32_t)(a.nb * 16 * (a.D / 2)));
-  const uint32_t tstride = (uint32_t)a.nb * 1024u;
+  const uint32_t tstride = (uint32_t)a.nb * 1024u;  // bytes per k-tile
+  const uint32_t wkb = (uint32_t)(kb / kSPT) * tstride;  // the part's first k-tile
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(a.r_codes + wkb, (uint32_t)(a.nb * 16 * (a.D / 2)) - wkb);
   uint32_t wvoff[kT32WCB];
 #pragma unroll
   for (int cb = 0; cb < kT32WCB; ++cb) {
@@ -323,13 +356,18 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
     if (b >= a.nb) b = (int)a.nb - 1;
     wvoff[cb] = (uint32_t)b * 1024u + (uint32_t)(lane & 15) * 16u + (uint32_t)g * 256u;
   }
-  u4 wr[kT32Ahead][kT32WCB];
+  // one 16-byte load per half k-tile (4 MFMA steps): one per stage of 64
+  // columns, two per stage of 128
+  u4 wr[kT32Ahead][kT32WCB][KS / 4];
   auto load_w = [&](int ks, auto S_) {
     constexpr int S = decltype(S_)::value;
-    const uint32_t soff = (uint32_t)(ks >> 1) * tstride + 512u * (uint32_t)(ks & 1);
 #pragma unroll
-    for (int cb = 0; cb < kT32WCB; ++cb)
-      wr[S][cb] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff[cb], soff, 0));
+    for (int h = 0; h < KS / 4; ++h) {
+      const uint32_t soff = (uint32_t)(ks / kSPT) * tstride + 512u * (uint32_t)(kSPT == 2 ? (ks & 1) : h);
+#pragma unroll
+      for (int cb = 0; cb < kT32WCB; ++cb)
+        wr[S][cb][h] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff[cb], soff, 0));
+    }
   };
 
   // Low-rank operands.  With at most kEpiLdsSteps rank steps (the common
@@ -366,8 +404,8 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
   // the last stage, Z of the workgroup (or the last stage again when Z is
   // read from memory in the epilogue).  Token tile tt's Z fragment rem sits
   // at z = tt * 2^zsh + rem (2^zsh the power of two >= zper, at most 16, so
-  // all TT tiles fit the ring's 16 TT positions): slot z / (4 TT), the
-  // position z % (4 TT) an H fragment would take.  Positions past a tile's
+  // all TT tiles fit the ring's 4 KS TT >= 16 TT positions): slot
+  // z / (KS TT), the position z % (KS TT) an H fragment would take.  Positions past a tile's
   // fragments repeat one of them.  The source is a uniform select, so every
   // copy has the same form as an H copy.
   const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(a.zf, (uint32_t)(a.n32 * (a.rc32 + a.rr32) * 4));
@@ -379,13 +417,13 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
 #pragma unroll
     for (int i = 0; i < kT32HOps; ++i) {
       const int f = kT32Waves * i + wave;
-      const int z = 4 * kT32TT * S + f;
+      const int z = KS * kT32TT * S + f;
       int tt = z >> zsh, rem = z & ((1 << zsh) - 1);
       if (tt > kT32TT - 1) tt = kT32TT - 1;
       if (rem > zper - 1) rem = zper - 1;  // zper = 0: negative, read past the end as zero
       const int T = tt0 + tt < G.ntiles ? tt0 + tt : G.ntiles - 1;  // padding tiles are never stored
-      const uint32_t off = zsrc ? (uint32_t)(T * zper + rem) * 1024u : hoff[i] + (uint32_t)jh * 4096u;
-      lds_copy16(zsrc ? zrs : hrs, &T32_SLOT(S)[f >> 2][f & 3][0], lane16, off);
+      const uint32_t off = zsrc ? (uint32_t)(T * zper + rem) * 1024u : hoff[i] + (uint32_t)jh * (KS * 1024u);
+      lds_copy16(zsrc ? zrs : hrs, &T32_SLOT(S)[f >> kLK][f & (KS - 1)][0], lane16, off);
     }
   };
 
@@ -438,7 +476,7 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
   if (tid < kT32TT * 32) {
     const int64_t tok = std::min<int64_t>(32 * (int64_t)tt0 + tid, a.n32 - 1);
     sTok[tid][0] = a.hscale[tok];
-    sTok[tid][1] = a.zscale[tok];
+    sTok[tid][1] = part == 0 ? a.zscale[tok] : 0.0f;  // the low-rank term goes with part 0 only
   }
   static_assert(kT32Threads >= kT32CB * 32, "one thread per vocabulary row of the workgroup");
   if (tid < kT32CB * 32) {
@@ -448,8 +486,8 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
     sVW[tid] = a.r_r > 0 ? f16_to_f32(a.a_scales[v * a.nA + a.nA - 1]) : 0.0f;
   }
 
-  // group codes of this lane's rows for one stage: the code of each of the
-  // stage's 4 MFMA steps is byte (GC == 2 ? t : GC == 1 ? t / 2 : 0)
+  // group codes of this lane's rows for one stage: the code of MFMA step t
+  // of a half k-tile is byte (GC == 2 ? t : GC == 1 ? t / 2 : 0)
   const int lg = __builtin_ctz((unsigned)a.g);
   uint32_t crow[kT32WCB];
 #pragma unroll
@@ -457,7 +495,7 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
     crow[cb] = (uint32_t)(32 * (wn * kT32WCB + cb) + 16 * ((lane >> 4) & 1) + (lane & 15)) * (uint32_t)cstride;
   uint32_t cd[2][kT32WCB];
   auto read_codes = [&](int ks, uint32_t(&dst)[kT32WCB]) {
-    const int kt = ks >> 1;
+    const int kt = (kb + ks) / kSPT;
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb) {
       if constexpr (GC == 2)
@@ -484,8 +522,9 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb) {
       const uint32_t c = cd[S & 1][cb];
-      const uint32_t code = GC == 2 ? (c >> (8 * T)) & 0xffu : GC == 1 ? (c >> (8 * (T >> 1))) & 0xffu : c;
-      bw[P][cb] = unpack_q4_scaled(wr[S][cb][T], (_Float16)(float)code);
+      constexpr int t = T & 3;  // step of the half k-tile
+      const uint32_t code = GC == 2 ? (c >> (8 * t)) & 0xffu : GC == 1 ? (c >> (8 * (t >> 1))) & 0xffu : c;
+      bw[P][cb] = unpack_q4_scaled(wr[S][cb][T >> 2][t], (_Float16)(float)code);
     }
   };
   auto mma = [&](auto P_) {
@@ -502,7 +541,7 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
 
   // stage 0 complete: wait past the loads of stages 1..3, then publish every
   // wave's copies and the codes
-  stage_barrier<3 * (kT32WOps + kT32HOps)>();
+  stage_barrier<3 * (kWOps + kT32HOps)>();
   read_codes(0, cd[0]);
   fetch(I0{}, I0{}, I0{});
 
@@ -518,24 +557,22 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
     constexpr std::integral_constant<int, (S + 1) & 3> Sn{};
     const int kn = ks + kT32Ahead < nS ? ks + kT32Ahead : nS - 1;
     // each MFMA step is its own scheduling region, so that no unpacking of
-    // registers still being loaded is hoisted into it
-    fetch(Sc, I1{}, I1{});
-    read_codes(ks + 1 < nS ? ks + 1 : ks, cd[(S + 1) & 1]);
-    mma(I0{});
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(Sc, I2{}, I0{});
-    mma(I1{});
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(Sc, I3{}, I1{});
-    load_w(kn, Sc);
-    mma(I0{});
-    __builtin_amdgcn_sched_barrier(0);
+    // registers still being loaded is hoisted into it; step t's operands are
+    // fetched while step t - 1 runs
+    static_for<1, KS>([&](auto T_) {
+      constexpr int T = decltype(T_)::value;
+      fetch(Sc, T_, std::integral_constant<int, T & 1>{});
+      if constexpr (T == 1) read_codes(ks + 1 < nS ? ks + 1 : ks, cd[(S + 1) & 1]);
+      if constexpr (T == KS - 1) load_w(kn, Sc);  // the slot's last step is unpacked
+      mma(std::integral_constant<int, (T - 1) & 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
     // stage ks + 1 is complete once this wave has at most the loads of the
     // three stages after it (W of ks + 4 included) in flight
-    stage_barrier<3 * kT32WOps + 2 * kT32HOps>();
+    stage_barrier<3 * kWOps + 2 * kT32HOps>();
     load_slot(ks + kT32Ahead, Sc);
     fetch(Sn, I0{}, I0{});  // past the last stage: harmless reads, never used
-    mma(I1{});
+    mma(std::integral_constant<int, (KS - 1) & 1>{});
     __builtin_amdgcn_sched_barrier(0);
   };
   int ks = 0;
@@ -545,9 +582,15 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
     stage(ks + 2, I2{});
     stage(ks + 3, I3{});
   }
-  if (ks < nS) {  // nS is even: two stages remain
-    stage(ks, I0{});
-    stage(ks + 1, I1{});
+  if constexpr (KS == 4) {
+    if (ks < nS) {  // nS is even: two stages remain
+      stage(ks, I0{});
+      stage(ks + 1, I1{});
+    }
+  } else {  // one to three stages remain
+    if (ks < nS) stage(ks, I0{});
+    if (ks + 1 < nS) stage(ks + 1, I1{});
+    if (ks + 2 < nS) stage(ks + 2, I2{});
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -557,6 +600,8 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
   // against exact INT8 A codes, 16 ranks per MFMA step, one accumulator per
   // part) is added with the scales, and each run is stored at once.
   const bool vec = ((uintptr_t)a.Y & 15) == 0 && (a.Y_stride & 3) == 0;
+  // a split tile's partial sums: [32 TT tokens][kT32CB * 32 rows] fp32
+  float* const ypart = a.part + (size_t)(split ? b - sp.full : 0) * (kT32TT * 32 * kT32CB * 32);
   auto store = [&](int m, int cb, const f16x& am, const f16x& pc, const f16x& pw) {
     const int tl = 32 * (kT32MT * wm + m) + c32;  // token within the workgroup
     const int64_t tok = 32 * (int64_t)tt0 + tl;
@@ -577,7 +622,9 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
         y[e] = hs * (sr[e] * am[v]);
         if (r > 0) y[e] = fmaf(zs, fmaf(sw[e], pw[v], sc[e] * pc[v]), y[e]);
       }
-      if (vec && voc0 + 3 < a.V) {
+      if (split) {  // tile-local fp32 partial sums
+        *reinterpret_cast<f4*>(ypart + tl * (kT32CB * 32) + lr) = f4{y[0], y[1], y[2], y[3]};
+      } else if (vec && voc0 + 3 < a.V) {
         if (a.y_bf16)
           *reinterpret_cast<u2*>(reinterpret_cast<uint16_t*>(a.Y) + row + voc0) = pack_bf16x4(y[0], y[1], y[2], y[3]);
         else
@@ -605,24 +652,31 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
   // the tile's fragments reads a copy or an old H fragment; its A codes are 0)
   auto zfrag = [&](int tt, int rem) {
     int z = (tt << zsh) + rem;
-    if (z > 16 * kT32TT - 1) z = 16 * kT32TT - 1;
-    const int slot = z / (4 * kT32TT), pos = z - slot * 4 * kT32TT;
+    if (z > 4 * KS * kT32TT - 1) z = 4 * KS * kT32TT - 1;
+    const int slot = z / (KS * kT32TT), pos = z - slot * KS * kT32TT;
     const h8* base = slot == 0 ? &sH0[0][0][0] : slot == 1 ? &sH1[0][0][0] : slot == 2 ? &sH2[0][0][0] : &sH3[0][0][0];
     return base[pos * 64 + lane];
   };
-  const uint64_t es = a.y_bf16 ? 2 : 4;
-  const bool fast = zlds && vec && 32 * (int64_t)(tt0 + kT32TT) <= a.N &&
-                    32 * ((int64_t)vt * kT32CB + kT32CB) <= a.V &&
-                    (uint64_t)a.N * (uint64_t)a.Y_stride * es < (1ull << 32);
+  // output of the straight-line epilogue: Y, or for a split tile its partial
+  // sums (every row of the tile, whole or not)
+  const bool ybf = !split && a.y_bf16;
+  const uint64_t es = ybf ? 2 : 4;
+  const uint64_t ys = split ? kT32CB * 32 : (uint64_t)a.Y_stride;  // row stride
+  const bool fast = zlds && (split || (vec && 32 * (int64_t)(tt0 + kT32TT) <= a.N &&
+                                       32 * ((int64_t)vt * kT32CB + kT32CB) <= a.V &&
+                                       (uint64_t)a.N * (uint64_t)a.Y_stride * es < (1ull << 32)));
   if (fast) {
     __syncthreads();  // every wave's Z copies (complete after the wait above) are visible
-    const __amdgpu_buffer_rsrc_t yrs = buffer_rsrc(a.Y, (uint32_t)((uint64_t)a.N * (uint64_t)a.Y_stride * es));
+    const __amdgpu_buffer_rsrc_t yrs =
+        split ? buffer_rsrc(ypart, (uint32_t)(kT32TT * 32 * kT32CB * 32 * 4))
+              : buffer_rsrc(a.Y, (uint32_t)((uint64_t)a.N * (uint64_t)a.Y_stride * es));
+    const int ytt0 = split ? 0 : tt0;                        // first token tile of the output
+    const uint64_t ycb0 = split ? 0 : (uint64_t)vt * kT32CB;  // first vocabulary block of the output
     // lane part of the output offset: token c32 of the tile, the lane's run of block cb
     uint32_t yoff[kT32WCB];
 #pragma unroll
     for (int cb = 0; cb < kT32WCB; ++cb)
-      yoff[cb] = (uint32_t)(((uint64_t)c32 * (uint64_t)a.Y_stride +
-                             32 * ((uint64_t)vt * kT32CB + kT32WCB * wn + cb) + 4 * g) * es);
+      yoff[cb] = (uint32_t)(((uint64_t)c32 * ys + 32 * (ycb0 + kT32WCB * wn + cb) + 4 * g) * es);
     // The wave's tiles (m, cb) one at a time, each its own scheduling region
     // (the two waves of a SIMD overlap one's scaling with the other's MFMAs).
     auto epilogue = [&](auto CS_) {
@@ -651,7 +705,7 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
         constexpr int m = decltype(J_)::value / kT32WCB, cb = decltype(J_)::value % kT32WCB;
         const int tt = kT32MT * wm + m;
         const float hs = sTok[32 * tt + c32][0], zs = sTok[32 * tt + c32][1];
-        const uint32_t trow = (uint32_t)((uint64_t)(32 * (tt0 + tt)) * (uint64_t)a.Y_stride * es);
+        const uint32_t trow = (uint32_t)((uint64_t)(32 * (ytt0 + tt)) * ys * es);
         const f16x& am = acc[m][cb];
 #pragma unroll
         for (int vg = 0; vg < 4; ++vg) {
@@ -666,7 +720,7 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
             const int v = 4 * vg + e;
             y[e] = fmaf(zs, fmaf(vw[e], pw[v], vc[e] * pc[v]), hs * (vr[e] * am[v]));
           }
-          if (a.y_bf16)
+          if (ybf)
             __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(y[0], y[1], y[2], y[3]), yrs, yoff[cb],
                                                   trow + (uint32_t)(16 * vg), 0);
           else
@@ -787,12 +841,65 @@ __global__ __launch_bounds__(kT32Threads, TT == 2 ? 4 : 1) void tile32_kernel(co
 
 #undef T32_SLOT
 
+// Y of the split tiles: the sum of each tile's sp.s partial tiles in part
+// order, in the output format.  Workgroup w takes token rows 4 (w % (8 TT))
+// .. + 3 of split tile w / (8 TT); thread t takes 4 consecutive vocabulary
+// rows of one of them, and issues the loads of up to 8 parts at once.
+template <int TT>
+__global__ __launch_bounds__(256) void t32_reduce_kernel(const FwdArgs a, const T32Split sp) {
+  constexpr int kRows = kT32CB * 32;       // vocabulary rows per tile
+  constexpr int kTileF = TT * 32 * kRows;  // floats per partial tile
+  constexpr int kBatch = 8;                // parts loaded together
+  const T32Grid G = t32_grid(a, TT);
+  const int j = blockIdx.x / (8 * TT), t = 4 * (blockIdx.x % (8 * TT)) + (threadIdx.x >> 6);
+  int vt, ttile;
+  t32_tile(G, sp.full + j, vt, ttile);
+  const int c = 4 * (threadIdx.x & 63);
+  const int64_t voc = (int64_t)vt * kRows + c, tok = 32 * (int64_t)ttile * TT + t;
+  if (voc >= a.V || tok >= a.N) return;
+  const float* src = a.part + (size_t)j * sp.s * kTileF + t * kRows + c;
+  f4 y = f4{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < sp.s; p0 += kBatch) {
+    f4 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = p0 + i < sp.s ? p0 + i : sp.s - 1;
+      v[i] = *reinterpret_cast<const f4*>(src + (size_t)p * kTileF);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (p0 + i < sp.s) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] += v[i][e];
+      }
+  }
+  const int64_t o = tok * a.Y_stride + voc;
+  if (((uintptr_t)a.Y & 15) == 0 && (a.Y_stride & 3) == 0 && voc + 3 < a.V) {
+    if (a.y_bf16)
+      *reinterpret_cast<u2*>(reinterpret_cast<uint16_t*>(a.Y) + o) = pack_bf16x4(y[0], y[1], y[2], y[3]);
+    else
+      *reinterpret_cast<f4*>(reinterpret_cast<float*>(a.Y) + o) = y;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (voc + e < a.V) {
+        if (a.y_bf16)
+          reinterpret_cast<uint16_t*>(a.Y)[o + e] = f32_to_bf16(y[e]);
+        else
+          reinterpret_cast<float*>(a.Y)[o + e] = y[e];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // The 32 x 32 x 16 kernel serves N > 128 when every section it reads fits
 // 32-bit buffer offsets.
-// Token tiles per workgroup: 64 tokens for N <= 64, 128 for N <= 128, else 256.
-static int t32_tt(int64_t N) { return N <= 64 ? 2 : N <= 128 ? 4 : 8; }
+// Token tiles per workgroup: 64 tokens for N <= 64, 128 for N <= 128, else
+// 256.  The two smaller sizes run 128-column stages, which need at least two
+// k-tiles (D >= 256).
+static int t32_tt(const FwdArgs& a) { return a.D < 256 ? 8 : a.N <= 64 ? 2 : a.N <= 128 ? 4 : 8; }
 
 // The 32 x 32 x 16 kernel serves any N whose sections fit 32-bit buffer
 // offsets and whose group codes fit the workgroup's LDS table.
@@ -801,27 +908,61 @@ bool tile32_eligible(const FwdArgs& a) {
   if (a.ng > kT32MaxCodes) return false;
   if (((uint64_t)a.nb * 16 + kT32CB * 32) * (uint64_t)a.ng >= (1ull << 32)) return false;
   if ((uint64_t)a.n32 * (uint64_t)a.D * 2 >= (1ull << 32)) return false;
-  const T32Grid G = t32_grid(a, t32_tt(a.N));
+  const T32Grid G = t32_grid(a, t32_tt(a));
   return (int64_t)G.ttiles * G.vtiles < (1ll << 31);
+}
+
+// Workgroups of one kernel instance resident at once on the current device
+// (0 if unknown).
+static int t32_slots(const void* kernel, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kT32Threads, lds) != hipSuccess)
+    return 0;
+  return cus > 0 && per_cu > 0 ? cus * per_cu : 0;
+}
+
+// Whole tiles fill whole rounds of resident workgroups; the tiles of a last,
+// partly filled round are split over the hidden dimension into as many parts
+// as that round has room for (at most a quarter of the stages, so every part
+// has at least four, and as many as the workspace holds).
+template <int TT>
+static T32Split t32_split(const FwdArgs& a, int tiles, int slots) {
+  const int rem = slots > 0 ? tiles % slots : 0;
+  if (rem == 0 || !a.part) return T32Split{tiles, 1};
+  const uint64_t tile_bytes = (uint64_t)TT * 32 * kT32CB * 32 * 4;
+  int64_t s = slots / rem;
+  s = std::min<int64_t>(s, a.D / (16 * t32_ks(TT)) / 4);
+  s = std::min<int64_t>(s, (int64_t)(a.part_bytes / tile_bytes / (uint64_t)rem));
+  if (s < 2) return T32Split{tiles, 1};
+  return T32Split{tiles - rem, (int)s};
+}
+
+template <int GC, int TT>
+static hipError_t launch_t32_g(const FwdArgs& a, hipStream_t s) {
+  const T32Grid G = t32_grid(a, TT);
+  const int tiles = G.ttiles * G.vtiles;
+  const size_t codes = (size_t)kT32CB * 32 * t32_code_stride(a.ng);  // dynamic LDS: the group-code table
+  const T32Split sp = t32_split<TT>(a, tiles, t32_slots((const void*)&tile32_kernel<GC, TT>, codes));
+  const int nsplit = tiles - sp.full;
+  const dim3 grid((unsigned)(sp.full + nsplit * sp.s)), block(kT32Threads);
+  hipLaunchKernelGGL((tile32_kernel<GC, TT>), grid, block, codes, s, a, sp);
+  if (nsplit > 0 && sp.s > 1)
+    hipLaunchKernelGGL((t32_reduce_kernel<TT>), dim3(nsplit * 8 * TT), dim3(256), 0, s, a, sp);
+  return hipGetLastError();
 }
 
 template <int TT>
 static hipError_t launch_t32(const FwdArgs& a, hipStream_t s) {
-  const T32Grid G = t32_grid(a, TT);
-  const dim3 grid((unsigned)(G.ttiles * G.vtiles)), block(kT32Threads);
-  const size_t codes = (size_t)kT32CB * 32 * t32_code_stride(a.ng);  // dynamic LDS: the group-code table
-  if (a.g == 32)
-    hipLaunchKernelGGL((tile32_kernel<2, TT>), grid, block, codes, s, a);
-  else if (a.g == 64)
-    hipLaunchKernelGGL((tile32_kernel<1, TT>), grid, block, codes, s, a);
-  else
-    hipLaunchKernelGGL((tile32_kernel<0, TT>), grid, block, codes, s, a);
-  return hipGetLastError();
+  if (a.g == 32) return launch_t32_g<2, TT>(a, s);
+  if (a.g == 64) return launch_t32_g<1, TT>(a, s);
+  return launch_t32_g<0, TT>(a, s);
 }
 
 hipError_t launch_tile(const FwdArgs& a, hipStream_t s) {
   if (tile32_eligible(a)) {
-    switch (t32_tt(a.N)) {
+    switch (t32_tt(a)) {
       case 2: return launch_t32<2>(a, s);
       case 4: return launch_t32<4>(a, s);
       default: return launch_t32<8>(a, s);

@@ -145,7 +145,9 @@ typedef struct {
 ARCHEAD_API int archead_pack_layout(const archead_dims* d, archead_layout* out);
 
 /* Device workspace one archead_logits call with n_tokens rows of H needs
- * (converted hidden states, the low-rank pre-projection and per-token scales).
+ * (converted hidden states, the low-rank pre-projection and per-token scales;
+ * above 16 tokens also 64 MiB for partial sums of output tiles whose hidden
+ * dimension is split over several workgroups).
  * Pure host arithmetic.  E_NULL, E_DIMS. */
 ARCHEAD_API int archead_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes);
 

@@ -105,14 +105,15 @@ def test_layout_dims_errors(ah):
 
 def test_workspace_bytes(ah):
     # hf (N32*D*2) | hscale (N32*4) | zf (N32*2*(rc32+rr32)*2) | zscale (N32*4) |
-    # z32 (N32*r*4) | hc (N*D*2), the last only for N <= 16; each 256-aligned
+    # z32 (N32*r*4) | hc (N*D*2), only for N <= 16 | split-tile partial sums
+    # (64 MiB), only for N > 16; each 256-aligned
     up = lambda x: (x + 255) // 256 * 256
     for (V, D, r_c, r_r, g), N in [((1024, 256, 16, 8, 64), 4), ((151936, 4096, 32, 32, 128), 1),
                                    ((151936, 4096, 64, 64, 128), 4096), ((64, 128, 0, 0, 32), 17)]:
         n32 = (N + 31) // 32 * 32
         rc32, rr32 = (r_c + 31) // 32 * 32, (r_r + 31) // 32 * 32
         want = (up(n32 * D * 2) + up(n32 * 4) + up(n32 * 2 * (rc32 + rr32) * 2) + up(n32 * 4) +
-                up(n32 * (r_c + r_r) * 4) + up(N * D * 2 if N <= 16 else 0))
+                up(n32 * (r_c + r_r) * 4) + up(N * D * 2 if N <= 16 else 0) + (64 << 20 if N > 16 else 0))
         assert ah.archead_workspace_bytes(V, D, r_c, r_r, g, N) == want
     assert ah.archead_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
 
