@@ -314,3 +314,27 @@ def top2_gap(Y):
     """Per-row gap between the largest and second-largest logit."""
     part = np.partition(Y, Y.shape[1] - 2, axis=1)
     return part[:, -1] - part[:, -2]
+
+
+def row_stats(Y, targets=None):
+    """Per-row statistics that the logits' consumers need, in fp64.
+
+    The pages judge a head by what the vocabulary distribution softmax(Y[n])
+    gives downstream: perplexity and added cross-entropy (ARCHead, Abstract)
+    and agreement of the top-ranked token (ARCHead, results discussion of
+    Table 8).  Per row n of Y:
+      max[n]    = max_v Y[n, v]
+      argmax[n] = the smallest v with Y[n, v] = max[n]
+      lse[n]    = log sum_v exp(Y[n, v])           (log of softmax's normaliser)
+      ce[n]     = lse[n] - Y[n, targets[n]]        (-log softmax(Y[n])[target])
+    lse is evaluated as max + log sum_v exp(Y - max), so rows with large
+    logits do not overflow.
+    """
+    Y = np.asarray(Y, np.float64)
+    m = Y.max(axis=1)
+    out = {"max": m, "argmax": np.argmax(Y, axis=1),
+           "lse": m + np.log(np.exp(Y - m[:, None]).sum(axis=1))}
+    if targets is not None:
+        t = np.asarray(targets, np.int64)
+        out["ce"] = out["lse"] - Y[np.arange(Y.shape[0]), t]
+    return out

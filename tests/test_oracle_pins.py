@@ -452,3 +452,64 @@ def test_argmax_ties_and_gap():
     Y = np.array([[1.0, 3.0, 3.0, -1.0], [0.0, 0.0, 0.0, 0.0], [-5.0, -4.0, -4.5, -9.0]])
     assert oracle.row_argmax(Y).tolist() == [1, 0, 1]
     assert oracle.top2_gap(Y).tolist() == [0.0, 0.0, 0.5]
+
+
+# ------------------------------------------------------------ row statistics ---
+
+
+def test_row_stats_closed_forms():
+    """Constant rows: every logit ties, so argmax is 0, lse = c + log V and the
+    cross-entropy of any target is log V; a row with one dominant logit has
+    lse equal to it up to exp(-gap)."""
+    V = 37
+    Y = np.full((3, V), 2.5)
+    Y[1] = -1e4
+    Y[2, :] = 0.0
+    Y[2, 11] = 800.0
+    st = oracle.row_stats(Y, targets=[5, 0, 11])
+    assert st["argmax"].tolist() == [0, 0, 11]
+    assert st["max"].tolist() == [2.5, -1e4, 800.0]
+    assert abs(st["lse"][0] - (2.5 + np.log(V))) < 1e-14
+    assert abs(st["lse"][1] - (-1e4 + np.log(V))) < 1e-11
+    assert st["lse"][2] == 800.0  # exp(-800) * 36 is far below one ulp of 800
+    assert abs(st["ce"][0] - np.log(V)) < 1e-14 and abs(st["ce"][1] - np.log(V)) < 1e-11
+    assert st["ce"][2] == 0.0
+
+
+def test_row_stats_brute_force_and_library():
+    """Small rows against a pure-Python loop (math.fsum of math.exp), and
+    larger ones against scipy's log-sum-exp and softmax, which are written
+    independently of the oracle."""
+    import math
+    from scipy.special import logsumexp, softmax
+    rng = np.random.default_rng(7)
+    Y = rng.normal(0.0, 3.0, size=(5, 50))
+    t = rng.integers(0, 50, size=5)
+    st = oracle.row_stats(Y, targets=t)
+    for n in range(5):
+        row = [float(x) for x in Y[n]]
+        lse = math.log(math.fsum(math.exp(x) for x in row))
+        assert abs(st["lse"][n] - lse) < 1e-12
+        assert st["argmax"][n] == max(range(50), key=lambda v: (row[v], -v))
+        assert abs(st["ce"][n] - (lse - row[t[n]])) < 1e-12
+    Z = rng.normal(0.0, 400.0, size=(4, 20000))  # logits of the size the synthetic heads give
+    tz = rng.integers(0, 20000, size=4)
+    sz = oracle.row_stats(Z, targets=tz)
+    assert np.allclose(sz["lse"], logsumexp(Z, axis=1), rtol=1e-15, atol=1e-12)
+    p = softmax(Z, axis=1)[np.arange(4), tz]
+    assert np.allclose(np.exp(-sz["ce"]), p, rtol=1e-12, atol=0)
+
+
+def test_row_stats_invariants():
+    """Shift: lse(Y + c) = lse(Y) + c and the cross-entropy is unchanged;
+    bounds: max <= lse <= max + log V and ce >= 0; ties go to the lowest index."""
+    rng = np.random.default_rng(8)
+    Y = rng.normal(0.0, 50.0, size=(6, 300))
+    t = rng.integers(0, 300, size=6)
+    a, b = oracle.row_stats(Y, t), oracle.row_stats(Y + 1234.5, t)
+    assert np.allclose(b["lse"], a["lse"] + 1234.5, rtol=0, atol=1e-9)
+    assert np.allclose(b["ce"], a["ce"], rtol=0, atol=1e-9)
+    assert (a["lse"] >= a["max"]).all() and (a["lse"] <= a["max"] + np.log(300) + 1e-12).all()
+    assert (a["ce"] >= 0).all()
+    T = np.array([[1.0, 3.0, 3.0, -1.0], [0.0, 0.0, 0.0, 0.0]])
+    assert oracle.row_stats(T)["argmax"].tolist() == [1, 0]
