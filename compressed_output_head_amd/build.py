@@ -34,8 +34,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libarchead.so)")
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,6 +44,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to its own object in parallel, then link."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run([hipcc(), *compile_flags, "-c", os.path.join(CSRC, so[0]), "-o", so[1]],
+                                    verbose), zip(SOURCES, objs)))
+    _run([hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 
