@@ -23,8 +23,8 @@ ARCHEAD_PATH_AUTO, ARCHEAD_PATH_DECODE, ARCHEAD_PATH_TILE = 0, 1, 2
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5: "E_SHAPE",
           6: "E_ALIGN", 7: "E_WORKSPACE", 8: "E_HIP", 9: "E_VALUE", 10: "E_SIZE"}
 EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_pack", "archead_logits",
-           "archead_logits_path", "archead_logits_events", "archead_status_string",
-           "archead_format_version")
+           "archead_logits_path", "archead_logits_events", "archead_stats_workspace_bytes",
+           "archead_logits_stats", "archead_status_string", "archead_format_version")
 
 
 class ArcheadError(RuntimeError):
@@ -68,6 +68,11 @@ class ArcheadPackedHead(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
 
 
+class ArcheadRowStats(ctypes.Structure):
+    _fields_ = [("row_max", ctypes.c_void_p), ("row_argmax", ctypes.c_void_p), ("row_lse", ctypes.c_void_p),
+                ("row_ce", ctypes.c_void_p), ("targets", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python compressed_output_head_amd/build.py`")
@@ -88,6 +93,9 @@ def _load():
                                         ctypes.c_int, ctypes.c_void_p]
     lib.archead_logits_events.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor),
                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.archead_stats_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int64, P(ctypes.c_uint64)]
+    lib.archead_logits_stats.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadRowStats),
+                                         ctypes.c_void_p]
     lib.archead_status_string.argtypes = [ctypes.c_int]
     lib.archead_status_string.restype = ctypes.c_char_p
     lib.archead_format_version.argtypes = []
@@ -134,6 +142,13 @@ def archead_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
     b = ctypes.c_uint64()
     _check(lib.archead_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
                                        ctypes.byref(b)), "archead_workspace_bytes")
+    return b.value
+
+
+def archead_stats_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
+    b = ctypes.c_uint64()
+    _check(lib.archead_stats_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
+                                             ctypes.byref(b)), "archead_stats_workspace_bytes")
     return b.value
 
 
@@ -192,9 +207,10 @@ class PackedHead:
     def dims(self):
         return dict(V=self.V, D=self.D, r_c=self.r_c, r_r=self.r_r, g=self.g)
 
-    def ensure_workspace(self, n_tokens: int):
+    def ensure_workspace(self, n_tokens: int, stats: bool = False):
         torch = _torch()
-        need = archead_workspace_bytes(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens)
+        size = archead_stats_workspace_bytes if stats else archead_workspace_bytes
+        need = size(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens)
         if self.workspace is None or self.workspace.numel() < need:
             self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.buffer.device)
         return self.workspace
@@ -252,3 +268,30 @@ def logits(H, head: PackedHead, out_dtype=None, path: int = ARCHEAD_PATH_AUTO):
     torch = _torch()
     Y = torch.empty((H.shape[0], head.V), dtype=out_dtype or torch.float32, device=H.device)
     return archead_logits_path(H, head, Y, path)
+
+
+def archead_logits_stats(H, head: PackedHead, targets=None, stream=None, outputs=("max", "argmax", "lse", "ce")):
+    """Per-row statistics of Y = H W_hat^T without writing Y: returns a dict of
+    device tensors of N elements -- "max" and "lse" (fp32), "argmax" (int32),
+    and "ce" (fp32, cross-entropy of ``targets``, an int32 device tensor of N
+    elements) when targets are given."""
+    torch = _torch()
+    N = H.shape[0]
+    head.ensure_workspace(N, stats=True)
+    if stream is None:
+        stream = torch.cuda.current_stream(H.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    out = {}
+    for k in outputs:
+        if k == "ce" and targets is None:
+            continue
+        out[k] = torch.empty(N, dtype=torch.int32 if k == "argmax" else torch.float32, device=H.device)
+    if targets is not None and (targets.dtype != torch.int32 or targets.numel() != N or not targets.is_contiguous()):
+        raise ValueError("targets must be a contiguous int32 tensor of N elements")
+    st = ArcheadRowStats(*(out[k].data_ptr() if k in out else None for k in ("max", "argmax", "lse", "ce")),
+                         targets.data_ptr() if targets is not None else None)
+    h, p = _tensor(H), head.struct()
+    _check(lib.archead_logits_stats(ctypes.byref(h), ctypes.byref(p), ctypes.byref(st), ctypes.c_void_p(stream)),
+           "archead_logits_stats")
+    return out

@@ -57,7 +57,7 @@ void compute_layout(const archead_dims* d, archead_layout* L) {
   L->payload_bytes = payload;
 }
 
-WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens) {
+WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool stats) {
   WorkspaceLayout w{};
   w.n16 = (int64_t)round_up((uint64_t)std::max<int64_t>(n_tokens, 0), 16);
   w.rc32 = (int)round_up((uint64_t)d->r_c, 32);
@@ -80,6 +80,12 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens) {
   w.hc = take(nsmall * D * 2);
   w.split_bytes = n_tokens > kDecodeLdsTokens ? kSplitBytes : 0;
   w.split = take(w.split_bytes);
+  if (stats) {  // statistics pieces, and Y of a few-token call
+    const uint64_t n = (uint64_t)std::max<int64_t>(n_tokens, 0);
+    w.st_nparts = std::max<int64_t>(kStatChunks, (int64_t)(round_up((uint64_t)d->V, 16) + 255) / 256);
+    w.st_part = take(n * (uint64_t)w.st_nparts * 16);
+    w.st_y = take(n <= (uint64_t)kDecodeLdsTokens ? n * (uint64_t)d->V * 4 : 0);
+  }
   w.total = n32 ? off : 0;
   return w;
 }
@@ -235,36 +241,37 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
   return ARCHEAD_OK;
 }
 
-int archead_logits_events(const archead_tensor* H, const archead_packed_head* head,
-                          archead_tensor* Y, int path, void* stream, void* ev_begin, void* ev_end) {
-  if (!H || !head || !Y) return ARCHEAD_E_NULL;
+}  // extern "C"
+
+namespace archead {
+namespace {
+
+// Checks shared by the entry points that run kernels, then every field of
+// `a` except the output's.
+int setup_args(const archead_tensor* H, const archead_packed_head* head, bool stats, FwdArgs& a,
+               WorkspaceLayout& W) {
+  if (!H || !head) return ARCHEAD_E_NULL;
   const archead_dims* d = &head->dims;
   int rc = check_kernel_dims(d);
   if (rc) return rc;
-  if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
   if (H->dtype != ARCHEAD_BF16) return ARCHEAD_E_DTYPE;
-  if (Y->dtype != ARCHEAD_F32 && Y->dtype != ARCHEAD_BF16) return ARCHEAD_E_DTYPE;
   const int64_t N = H->rows;
-  if (N < 0 || H->cols != d->D || Y->cols != d->V || Y->rows != N) return ARCHEAD_E_SHAPE;
-  if (H->row_stride < d->D || Y->row_stride < d->V) return ARCHEAD_E_SHAPE;
-  if (path == ARCHEAD_PATH_DECODE && N > kDecodeMaxTokens) return ARCHEAD_E_UNSUPPORTED;
+  if (N < 0 || H->cols != d->D || H->row_stride < d->D) return ARCHEAD_E_SHAPE;
   if (N > (int64_t(1) << 22)) return ARCHEAD_E_UNSUPPORTED;
   if (N == 0) return ARCHEAD_OK;
-  if (!H->data || !Y->data || !head->buffer || !head->workspace) return ARCHEAD_E_NULL;
-  const int ysz = Y->dtype == ARCHEAD_F32 ? 4 : 2;
+  if (!H->data || !head->buffer || !head->workspace) return ARCHEAD_E_NULL;
   if ((uintptr_t)head->buffer % ARCHEAD_ALIGNMENT || (uintptr_t)head->workspace % ARCHEAD_ALIGNMENT)
     return ARCHEAD_E_ALIGN;
   if ((uintptr_t)H->data % 16 || (H->row_stride * 2) % 16) return ARCHEAD_E_ALIGN;
-  if ((uintptr_t)Y->data % ysz) return ARCHEAD_E_ALIGN;
   archead_layout L;
   compute_layout(d, &L);
   if (head->buffer_bytes < L.total_bytes) return ARCHEAD_E_SIZE;
-  const WorkspaceLayout W = workspace_layout(d, N);
+  W = workspace_layout(d, N, stats);
   if (head->workspace_bytes < W.total) return ARCHEAD_E_WORKSPACE;
 
   const uint8_t* buf = static_cast<const uint8_t*>(head->buffer);
   uint8_t* ws = static_cast<uint8_t*>(head->workspace);
-  FwdArgs a;
+  a = FwdArgs{};
   a.V = d->V;
   a.D = d->D;
   a.N = N;
@@ -283,9 +290,6 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   a.nA = (d->r_c > 0) + (d->r_r > 0);
   a.H = static_cast<const uint16_t*>(H->data);
   a.H_stride = H->row_stride;
-  a.Y = Y->data;
-  a.Y_stride = Y->row_stride;
-  a.y_bf16 = Y->dtype == ARCHEAD_BF16;
   a.r_codes = buf + L.r_codes.offset;
   a.r_gcodes = buf + L.r_gcodes.offset;
   a.r_rowscale = reinterpret_cast<const uint16_t*>(buf + L.r_rowscale.offset);
@@ -301,6 +305,38 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   a.hc = reinterpret_cast<_Float16*>(ws + W.hc);
   a.part = W.split_bytes ? reinterpret_cast<float*>(ws + W.split) : nullptr;
   a.part_bytes = W.split_bytes;
+  if (stats) {
+    a.st_part = reinterpret_cast<float*>(ws + W.st_part);
+    a.st_nparts = W.st_nparts;
+  }
+  return ARCHEAD_OK;
+}
+
+}  // namespace
+}  // namespace archead
+
+extern "C" {
+
+int archead_logits_events(const archead_tensor* H, const archead_packed_head* head,
+                          archead_tensor* Y, int path, void* stream, void* ev_begin, void* ev_end) {
+  if (!H || !head || !Y) return ARCHEAD_E_NULL;
+  if (int rc0 = check_kernel_dims(&head->dims)) return rc0;
+  if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
+  if (H->dtype != ARCHEAD_BF16) return ARCHEAD_E_DTYPE;
+  if (Y->dtype != ARCHEAD_F32 && Y->dtype != ARCHEAD_BF16) return ARCHEAD_E_DTYPE;
+  const int64_t N = H->rows;
+  if (Y->cols != head->dims.V || Y->rows != N || Y->row_stride < head->dims.V) return ARCHEAD_E_SHAPE;
+  if (path == ARCHEAD_PATH_DECODE && N > kDecodeMaxTokens) return ARCHEAD_E_UNSUPPORTED;
+  FwdArgs a;
+  WorkspaceLayout W;
+  int rc = setup_args(H, head, false, a, W);
+  if (rc || N == 0) return rc;
+  const int ysz = Y->dtype == ARCHEAD_F32 ? 4 : 2;
+  if (!Y->data) return ARCHEAD_E_NULL;
+  if ((uintptr_t)Y->data % ysz) return ARCHEAD_E_ALIGN;
+  a.Y = Y->data;
+  a.Y_stride = Y->row_stride;
+  a.y_bf16 = Y->dtype == ARCHEAD_BF16;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
@@ -332,6 +368,51 @@ int archead_logits_path(const archead_tensor* H, const archead_packed_head* head
 int archead_logits(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y,
                    void* stream) {
   return archead_logits_path(H, head, Y, ARCHEAD_PATH_AUTO, stream);
+}
+
+int archead_stats_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes) {
+  if (!d || !bytes) return ARCHEAD_E_NULL;
+  const int rc = check_dims(d);
+  if (rc) return rc;
+  if (n_tokens < 0) return ARCHEAD_E_SHAPE;
+  *bytes = workspace_layout(d, n_tokens, true).total;
+  return ARCHEAD_OK;
+}
+
+int archead_logits_stats(const archead_tensor* H, const archead_packed_head* head, const archead_row_stats* out,
+                         void* stream) {
+  if (!H || !head || !out) return ARCHEAD_E_NULL;
+  if (out->row_ce && !out->targets) return ARCHEAD_E_NULL;
+  for (const void* p : {(const void*)out->row_max, (const void*)out->row_argmax, (const void*)out->row_lse,
+                        (const void*)out->row_ce, (const void*)out->targets})
+    if ((uintptr_t)p % 4) return ARCHEAD_E_ALIGN;
+  FwdArgs a;
+  WorkspaceLayout W;
+  int rc = setup_args(H, head, true, a, W);
+  if (rc || H->rows == 0) return rc;
+  a.targets = out->targets;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // start from a clean error state
+  hipError_t e;
+  if (decode_lds_eligible(a)) {
+    // a few tokens: Y (at most 16 rows) into the workspace, then its pieces
+    float* Yw = reinterpret_cast<float*>(static_cast<uint8_t*>(head->workspace) + W.st_y);
+    a.Y = Yw;
+    a.Y_stride = a.V;
+    a.y_bf16 = 0;
+    a.st_nparts = kStatChunks;
+    e = launch_prep_z(a, s);
+    if (e == hipSuccess) e = launch_decode_lds(a, s);
+    if (e == hipSuccess) e = launch_rowstats_y(a, Yw, a.V, s);
+  } else if (tile32_eligible(a)) {
+    a.st_nparts = tile_stat_parts(a);
+    e = launch_prep(a, true, s);
+    if (e == hipSuccess) e = launch_tile_stats(a, s);
+  } else {
+    return ARCHEAD_E_UNSUPPORTED;
+  }
+  if (e == hipSuccess) e = launch_stats_reduce(a, out->row_max, out->row_argmax, out->row_lse, out->row_ce, s);
+  return e == hipSuccess ? ARCHEAD_OK : ARCHEAD_E_HIP;
 }
 
 }  // extern "C"

@@ -35,9 +35,12 @@ struct WorkspaceLayout {
   int64_t n32;          // tokens rounded up to 32 (rows of every per-token workspace section)
   int rc32, rr32;       // ranks rounded up to 32
   int zsteps;           // (rc32 + rr32) / 32
-  uint64_t hf, hscale, zf, zscale, z32, hc, split, split_bytes, total;
+  uint64_t hf, hscale, zf, zscale, z32, hc, split, split_bytes;
+  uint64_t st_part, st_y;  // row statistics only: pieces [N][st_nparts], Y [N][V] fp32 for N <= 16
+  int64_t st_nparts;
+  uint64_t total;
 };
-WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens);
+WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool stats = false);
 
 // Everything a kernel needs, resolved to raw device pointers.
 struct FwdArgs {
@@ -72,6 +75,10 @@ struct FwdArgs {
   _Float16* hc;               // [N][D] scaled fp16 H rows in kernel k-order (small-N decode path only)
   float* part;                // fp32 partial sums of split tiles (null: no room, tiles are not split)
   uint64_t part_bytes;
+  // row statistics (archead_logits_stats): pieces [N][st_nparts] of 16 bytes
+  float* st_part;
+  int64_t st_nparts;
+  const int32_t* targets;     // [N] or null
 };
 
 hipError_t launch_prep(const FwdArgs& a, bool rows32, hipStream_t s);
@@ -83,5 +90,13 @@ hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
 bool mid_eligible(const FwdArgs& a);
 hipError_t launch_mid(const FwdArgs& a, hipStream_t s);
 hipError_t launch_tile(const FwdArgs& a, hipStream_t s);
+int tile_stat_parts(const FwdArgs& a);
+hipError_t launch_tile_stats(const FwdArgs& a, hipStream_t s);
+// statistics pieces of a fp32 Y already in memory, kStatChunks per token
+constexpr int kStatChunks = 64;
+hipError_t launch_rowstats_y(const FwdArgs& a, const float* Y, int64_t y_stride, hipStream_t s);
+// merge a.st_nparts pieces per token into the outputs (null: not written)
+hipError_t launch_stats_reduce(const FwdArgs& a, float* row_max, int32_t* row_argmax, float* row_lse,
+                               float* row_ce, hipStream_t s);
 
 }  // namespace archead

@@ -162,8 +162,9 @@ ARCHEAD_API int archead_pack(const archead_dims* d, const archead_host_component
  *   Y: fp32 or bf16 [N][V] device tensor, written completely (every element
  *      once); bf16 output is rounded to nearest even from the fp32 result.
  *   stream: a hipStream_t (NULL = the default stream).
- * Enqueues the pre-projection kernels and then the decode path (N <= 64) or
- * the tile path (N > 64) on `stream` and returns without synchronising.
+ * Enqueues the pre-projection kernels and then the decode path (up to 16
+ * tokens whose H and Z fit LDS) or the tile path on `stream` and returns
+ * without synchronising.
  * N = 0 is a no-op that returns ARCHEAD_OK.  Faults inside kernels surface at
  * the caller's next synchronisation with the stream. */
 ARCHEAD_API int archead_logits(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y,
@@ -181,6 +182,41 @@ ARCHEAD_API int archead_logits_path(const archead_tensor* H, const archead_packe
 ARCHEAD_API int archead_logits_events(const archead_tensor* H, const archead_packed_head* head,
                                       archead_tensor* Y, int path, void* stream, void* ev_begin,
                                       void* ev_end);
+
+/* Per-row statistics of Y = H W_hat^T (the fp32 logits archead_logits
+ * computes), without writing Y: what the pages' quality metrics are built
+ * from (ARCHead, Abstract: perplexity and cross-entropy; results discussion
+ * of Table 8: top-1 agreement).  Each output is a device array of N elements,
+ * 4-byte aligned, or NULL (not written):
+ *   row_max[n]    = max_v Y[n, v]                          fp32
+ *   row_argmax[n] = the lowest v with Y[n, v] = row_max[n]  int32
+ *   row_lse[n]    = log sum_v exp(Y[n, v])                  fp32
+ *   row_ce[n]     = row_lse[n] - Y[n, targets[n]]           fp32; NaN where
+ *                   targets[n] is outside [0, V); needs targets
+ *   targets       = device int32 [N], or NULL when row_ce is NULL. */
+typedef struct {
+  float* row_max;
+  int32_t* row_argmax;
+  float* row_lse;
+  float* row_ce;
+  const int32_t* targets;
+} archead_row_stats;
+
+/* Device workspace one archead_logits_stats call with n_tokens rows needs:
+ * archead_workspace_bytes plus 16 bytes per token and statistics piece
+ * (max(64, ceil(V16 / 256)) pieces), plus Y in fp32 when n_tokens <= 16.
+ * Pure host arithmetic.  E_NULL, E_DIMS. */
+ARCHEAD_API int archead_stats_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes);
+
+/* Enqueue the statistics of `out` for the N rows of H on `stream`; the same
+ * argument rules as archead_logits for H and head (the workspace must hold
+ * archead_stats_workspace_bytes).  The tile path reduces each 256-row
+ * vocabulary tile of every token in its epilogue and never writes Y; up to
+ * 16 tokens whose H and Z fit LDS run the decode kernel into the workspace
+ * first.  Shapes neither path takes (section offsets past 32 bits) give
+ * E_UNSUPPORTED.  E_NULL also when row_ce is set without targets. */
+ARCHEAD_API int archead_logits_stats(const archead_tensor* H, const archead_packed_head* head,
+                                     const archead_row_stats* out, void* stream);
 
 /* Static string naming a status code. */
 ARCHEAD_API const char* archead_status_string(int status);

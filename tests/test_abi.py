@@ -175,6 +175,42 @@ def test_logits_error_paths(ah):
         assert _call(ah, H, P, Y, path) == want, i
 
 
+def test_stats_workspace_bytes(ah):
+    # the logits workspace, then statistics pieces (N * max(64, ceil(V16/256)) * 16 B)
+    # and, for N <= 16, Y in fp32 (N * V * 4 B); each 256-aligned
+    up = lambda x: (x + 255) // 256 * 256
+    for (V, D, r_c, r_r, g), N in [((1024, 256, 16, 8, 64), 4), ((151936, 4096, 32, 32, 128), 1),
+                                   ((151936, 4096, 64, 64, 128), 4096), ((64, 128, 0, 0, 32), 17)]:
+        pieces = max(64, ((V + 15) // 16 * 16 + 255) // 256)
+        want = (ah.archead_workspace_bytes(V, D, r_c, r_r, g, N) + up(N * pieces * 16) +
+                up(N * V * 4 if N <= 16 else 0))
+        assert ah.archead_stats_workspace_bytes(V, D, r_c, r_r, g, N) == want
+    assert ah.archead_stats_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
+
+
+def test_stats_error_paths(ah):
+    def call(H, P, st):
+        return ah.lib.archead_logits_stats(ctypes.byref(H), ctypes.byref(P), st and ctypes.byref(st), None)
+
+    def args(**kw):
+        H, P, Y, need, total = _args(ah, **kw)
+        P.workspace_bytes = ah.archead_stats_workspace_bytes(1024, 256, 16, 8, 64, H.rows) if H.rows >= 0 else 0
+        return H, P, ah.ArcheadRowStats(FAKE + (4 << 30), FAKE + (5 << 30), FAKE + (6 << 30), None, None)
+
+    H, P, st = args()
+    assert call(H, P, None) == 1
+    assert ah.lib.archead_logits_stats(None, ctypes.byref(P), ctypes.byref(st), None) == 1
+    H, P, st = args(); st.row_ce = FAKE + (7 << 30); assert call(H, P, st) == 1         # ce without targets
+    H, P, st = args(); st.row_lse = FAKE + 2; assert call(H, P, st) == 6                # misaligned output
+    H, P, st = args(); st.row_ce = FAKE + (7 << 30); st.targets = FAKE + 1; assert call(H, P, st) == 6
+    H, P, st = args(hdt=2); assert call(H, P, st) == 4
+    H, P, st = args(); H.cols = 255; assert call(H, P, st) == 5
+    H, P, st = args(g=16); assert call(H, P, st) == 3
+    H, P, st = args(); P.workspace_bytes = ah.archead_workspace_bytes(1024, 256, 16, 8, 64, 4)
+    assert call(H, P, st) == 7                                                          # logits-sized workspace
+    H, P, st = args(N=0); H.data = None; P.workspace = None; assert call(H, P, st) == 0
+
+
 def test_logits_zero_tokens_is_a_noop(ah):
     H, P, Y, need, total = _args(ah, N=0)
     H.data = Y.data = None
