@@ -38,7 +38,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ["decode.hip", "device_common.h", "internal.h"],
     "mid_kernel": ["mid.hip", "device_common.h", "internal.h"],
     "tile_kernel": ["tile.hip", "device_common.h", "internal.h"],
-    "tile32_kernel": ["tile.hip", "device_common.h", "internal.h"],
+    "tile32_kernel": ["tile.hip", "tile32.h", "rowstat.h", "device_common.h", "internal.h"],
 }
 
 
@@ -201,6 +201,39 @@ def run_workload(name, steps, warmup, path=0):
                 kernel_ms_min=float(np.min(kms)), kernel_ms_max=float(np.max(kms)))
 
 
+def run_stats(name, steps, warmup):
+    """archead_logits_stats (row max, argmax, log-sum-exp, cross-entropy; no
+    logits written) on one workload, K timed calls."""
+    import torch
+    import synth
+    import compressed_output_head_amd as ah
+
+    cfg = synth.config(name)
+    inp = synth.make(name)
+    packed = ah.archead_pack(inp.head)
+    heads = [ah.PackedHead(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], packed)]
+    heads.append(ah.PackedHead(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], heads[0].buffer.clone()))
+    N = cfg["N"]
+    H = torch.from_numpy(inp.H_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    targets = torch.as_tensor(np.random.default_rng(0).integers(0, cfg["V"], size=N).astype(np.int32), device="cuda")
+    del inp
+    for i in range(warmup):
+        ah.archead_logits_stats(H, heads[i % 2], targets)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        ah.archead_logits_stats(H, heads[i % 2], targets)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = 2 * N * cfg["V"] * (cfg["D"] + cfg["r_c"] + cfg["r_r"]) + 2 * N * cfg["D"] * (cfg["r_c"] + cfg["r_r"])
+    return {"workload": name, "ms_per_call": round(ms, 4), "steps": steps,
+            "what": "row max, argmax, log-sum-exp and cross-entropy of given targets; the logits are never written",
+            "tflops": round(flops / (ms / 1e3) / 1e12, 2)}
+
+
 def tile_workload(N):
     """Workloads of more than 64 tokens are bound by the MFMA and reported in
     TFLOP/s against its peak; up to 64 tokens the head's bytes bound the call,
@@ -280,6 +313,8 @@ def main():
     ap.add_argument("--cpu-sample-rows", type=int, default=None,
                     help="vocabulary rows the CPU oracle is timed on (default: all for decode-type "
                          "workloads, 4096 for tile-type ones)")
+    ap.add_argument("--stats", default="prefill",
+                    help="workload timed through archead_logits_stats ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run the device copies that calibrate HBM byte counters")
@@ -342,6 +377,10 @@ def main():
             "config": {k: s["cfg"][k] for k in ("V", "D", "N", "r_c", "r_r", "g")} | {"logits": s["cfg"]["y_dtype"]},
             "roofline": roof2,
         }
+    if args.stats:
+        st = run_stats(args.stats, max(5, args.steps // 5), max(2, args.warmup // 5))
+        log(f"[bench] stats on {args.stats}: {st['ms_per_call']:.3f} ms/call")
+        out["stats"] = st
     out["kernel_sources"] = kernel_hash()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")

@@ -36,6 +36,34 @@ __device__ __forceinline__ void stat_add(RowStat& r, float y, int v, int tgt) {
   }
 }
 
+// The 16 logits one lane holds in a 32 x 32 result tile: y[4 j + e] at
+// vocabulary index v0 + 8 j + e.  One maximum per block; the index of the
+// maximum and the target's logit are looked for only in the rare blocks that
+// can change them.
+__device__ __forceinline__ void stat_add16(RowStat& r, const float (&y)[16], int v0, int tgt) {
+  float bm = y[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) bm = fmaxf(bm, y[i]);
+  if (bm >= r.m) {
+    int bi = INT32_MAX;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) bi = y[i] == bm ? v0 + 8 * (i >> 2) + (i & 3) : bi;
+    r.idx = bm > r.m ? bi : (bi < r.idx ? bi : r.idx);
+  }
+  const float M = fmaxf(r.m, bm);
+  float s = r.m == -INFINITY ? 0.0f : r.s * __expf(r.m - M);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += __expf(y[i] - M);
+  r.m = M;
+  r.s = s;
+  const unsigned d = (unsigned)(tgt - v0);
+  if (d < 28u && (d & 4u) == 0u) {
+    const int ti = (int)(d >> 3) * 4 + (int)(d & 3u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r.yt = i == ti ? y[i] : r.yt;
+  }
+}
+
 __device__ __forceinline__ RowStat stat_merge(const RowStat& a, const RowStat& b) {
   RowStat r;
   r.m = fmaxf(a.m, b.m);

@@ -477,6 +477,7 @@ __global__ __launch_bounds__(kT32Threads, 1) void tile32_kernel(const FwdArgs a,
   // once every wave is done with the Z it holds.
   auto finish_stats = [&]() {
     if constexpr (ST) {
+      if (split) return;
 #pragma unroll
       for (int m = 0; m < kT32MT; ++m) st[m] = stat_merge(st[m], stat_shfl_xor(st[m], 32));
       __syncthreads();
@@ -517,10 +518,12 @@ __global__ __launch_bounds__(kT32Threads, 1) void tile32_kernel(const FwdArgs a,
         y[e] = hs * (sr[e] * am[v]);
         if (r > 0) y[e] = fmaf(zs, fmaf(sw[e], pw[v], sc[e] * pc[v]), y[e]);
       }
-      if constexpr (ST) {
+      if (ST && !split) {
+        if constexpr (ST) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (voc0 + e < a.V) stat_add(st[m], y[e], (int)(voc0 + e), sTgt[tl]);
+          for (int e = 0; e < 4; ++e)
+            if (voc0 + e < a.V) stat_add(st[m], y[e], (int)(voc0 + e), sTgt[tl]);
+        }
       } else if (split) {  // tile-local fp32 partial sums
         *reinterpret_cast<f4*>(ypart + tl * (kT32CB * 32) + lr) = f4{y[0], y[1], y[2], y[3]};
       } else if (vec && voc0 + 3 < a.V) {
@@ -562,8 +565,7 @@ __global__ __launch_bounds__(kT32Threads, 1) void tile32_kernel(const FwdArgs a,
   const uint64_t es = ybf ? 2 : 4;
   const uint64_t ys = split ? kT32CB * 32 : (uint64_t)a.Y_stride;  // row stride
   const bool whole = 32 * (int64_t)(tt0 + kT32TT) <= a.N && 32 * ((int64_t)vt * kT32CB + kT32CB) <= a.V;
-  const bool fast = zlds && (ST ? whole
-                                : split || (vec && whole && (uint64_t)a.N * (uint64_t)a.Y_stride * es < (1ull << 32)));
+  const bool fast = zlds && (split || (ST ? whole : vec && whole && (uint64_t)a.N * (uint64_t)a.Y_stride * es < (1ull << 32)));
   if (fast) {
     __syncthreads();  // every wave's Z copies (complete after the wait above) are visible
     const __amdgpu_buffer_rsrc_t yrs =
@@ -606,6 +608,7 @@ __global__ __launch_bounds__(kT32Threads, 1) void tile32_kernel(const FwdArgs a,
         const float hs = sTok[32 * tt + c32][0], zs = sTok[32 * tt + c32][1];
         const uint32_t trow = (uint32_t)((uint64_t)(32 * (ytt0 + tt)) * ys * es);
         const f16x& am = acc[m][cb];
+        float y16[ST ? 16 : 1];  // statistics: the tile's 16 logits of this lane
 #pragma unroll
         for (int vg = 0; vg < 4; ++vg) {
           const int lr = 32 * (kT32WCB * wn + cb) + 8 * vg + 4 * g;
@@ -619,10 +622,11 @@ __global__ __launch_bounds__(kT32Threads, 1) void tile32_kernel(const FwdArgs a,
             const int v = 4 * vg + e;
             y[e] = fmaf(zs, fmaf(vw[e], pw[v], vc[e] * pc[v]), hs * (vr[e] * am[v]));
           }
-          if constexpr (ST) {
-            const int voc = 32 * (vt * kT32CB + kT32WCB * wn + cb) + 8 * vg + 4 * g;
+          if (ST && !split) {
+            if constexpr (ST) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) stat_add(st[m], y[e], voc + e, sTgt[32 * tt + c32]);
+              for (int e = 0; e < 4; ++e) y16[4 * vg + e] = y[e];
+            }
           } else if (ybf) {
             __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(y[0], y[1], y[2], y[3]), yrs, yoff[cb],
                                                   trow + (uint32_t)(16 * vg), 0);
@@ -630,6 +634,9 @@ __global__ __launch_bounds__(kT32Threads, 1) void tile32_kernel(const FwdArgs a,
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, f4{y[0], y[1], y[2], y[3]}), yrs,
                                                    yoff[cb], trow + (uint32_t)(32 * vg), 0);
           }
+        }
+        if constexpr (ST) {
+          if (!split) stat_add16(st[m], y16, 32 * (vt * kT32CB + kT32WCB * wn + cb) + 4 * g, sTgt[32 * tt + c32]);
         }
       };
       static_for<0, kTiles>([&](auto J_) {
@@ -752,7 +759,9 @@ __global__ __launch_bounds__(kT32Threads, 1) void tile32_kernel(const FwdArgs a,
 // order, in the output format.  Workgroup w takes token rows 4 (w % (8 TT))
 // .. + 3 of split tile w / (8 TT); thread t takes 4 consecutive vocabulary
 // rows of one of them, and issues the loads of up to 8 parts at once.
-template <int TT>
+// ST: statistics pieces instead (each wave takes one token row, so its 64
+// lanes hold the tile's 256 logits of that token).
+template <int TT, bool ST>
 __global__ __launch_bounds__(256) void t32_reduce_kernel(const FwdArgs a, const T32Split sp) {
   constexpr int kRows = kT32CB * 32;       // vocabulary rows per tile
   constexpr int kTileF = TT * 32 * kRows;  // floats per partial tile
@@ -763,7 +772,11 @@ __global__ __launch_bounds__(256) void t32_reduce_kernel(const FwdArgs a, const 
   t32_tile(G, sp.full + j, vt, ttile);
   const int c = 4 * (threadIdx.x & 63);
   const int64_t voc = (int64_t)vt * kRows + c, tok = 32 * (int64_t)ttile * TT + t;
-  if (voc >= a.V || tok >= a.N) return;
+  if constexpr (!ST) {
+    if (voc >= a.V || tok >= a.N) return;
+  } else {
+    if (tok >= a.N) return;  // a whole wave: the token is uniform
+  }
   const float* src = a.part + (size_t)j * sp.s * kTileF + t * kRows + c;
   f4 y = f4{0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < sp.s; p0 += kBatch) {
@@ -779,6 +792,17 @@ __global__ __launch_bounds__(256) void t32_reduce_kernel(const FwdArgs a, const 
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] += v[i][e];
       }
+  }
+  if constexpr (ST) {
+    RowStat r = stat_empty();
+    const int tgt = a.targets ? a.targets[tok] : -1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (voc + e < a.V) stat_add(r, y[e], (int)(voc + e), tgt);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) r = stat_merge(r, stat_shfl_xor(r, off));
+    if ((threadIdx.x & 63) == 0) reinterpret_cast<f4*>(a.st_part)[tok * a.st_nparts + vt] = stat_pack(r);
+    return;
   }
   const int64_t o = tok * a.Y_stride + voc;
   if (((uintptr_t)a.Y & 15) == 0 && (a.Y_stride & 3) == 0 && voc + 3 < a.V) {
@@ -836,14 +860,12 @@ static hipError_t launch_t32_g(const FwdArgs& a, hipStream_t s) {
   const T32Grid G = t32_grid(a, TT);
   const int tiles = G.ttiles * G.vtiles;
   const size_t codes = (size_t)kT32CB * 32 * t32_code_stride(a.ng);  // dynamic LDS: the group-code table
-  // statistics pieces are whole tiles: no split
-  const T32Split sp =
-      ST ? T32Split{tiles, 1} : t32_split<TT>(a, tiles, t32_slots((const void*)&tile32_kernel<GC, TT, ST>, codes));
+  const T32Split sp = t32_split<TT>(a, tiles, t32_slots((const void*)&tile32_kernel<GC, TT, ST>, codes));
   const int nsplit = tiles - sp.full;
   const dim3 grid((unsigned)(sp.full + nsplit * sp.s)), block(kT32Threads);
   hipLaunchKernelGGL((tile32_kernel<GC, TT, ST>), grid, block, codes, s, a, sp);
   if (nsplit > 0 && sp.s > 1)
-    hipLaunchKernelGGL((t32_reduce_kernel<TT>), dim3(nsplit * 8 * TT), dim3(256), 0, s, a, sp);
+    hipLaunchKernelGGL((t32_reduce_kernel<TT, ST>), dim3(nsplit * 8 * TT), dim3(256), 0, s, a, sp);
   return hipGetLastError();
 }
 
