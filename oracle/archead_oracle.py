@@ -319,7 +319,7 @@ def top2_gap(Y):
 def row_stats(Y, targets=None):
     """Per-row statistics that the logits' consumers need, in fp64.
 
-    The pages judge a head by what the vocabulary distribution softmax(Y[n])
+    The pages assess a head by what the vocabulary distribution softmax(Y[n])
     gives downstream: perplexity and added cross-entropy (ARCHead, Abstract)
     and agreement of the top-ranked token (ARCHead, results discussion of
     Table 8).  Per row n of Y:

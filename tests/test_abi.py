@@ -230,7 +230,7 @@ def test_status_strings(ah):
 
 def test_every_kernel_has_its_host_launch_stub(ah):
     """A kernel whose host-side instantiation is dropped leaves an undefined
-    launch stub behind, and the library then fails to load on a GPU machine."""
+    launch stub behind, and the library then fails to load on a machine with a GPU."""
     import shutil
     import subprocess
     nm = shutil.which("nm")
