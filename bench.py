@@ -198,7 +198,8 @@ def run_workload(name, steps, warmup, path=0):
     kms = [evb[i].elapsed_time(eve[i]) for i in range(steps)]
     A = algorithmic(cfg, L, N)
     return dict(cfg=cfg, L=L, A=A, ms=ms, kernel=dominant_kernel(N), kernel_ms=float(np.mean(kms)),
-                kernel_ms_min=float(np.min(kms)), kernel_ms_max=float(np.max(kms)))
+                kernel_ms_min=float(np.min(kms)), kernel_ms_max=float(np.max(kms)),
+                kernel_ms_pct=[round(float(np.percentile(kms, q)), 5) for q in (10, 50, 90)])
 
 
 def run_stats(name, steps, warmup):
@@ -232,6 +233,47 @@ def run_stats(name, steps, warmup):
     return {"workload": name, "ms_per_call": round(ms, 4), "steps": steps,
             "what": "row max, argmax, log-sum-exp and cross-entropy of given targets; the logits are never written",
             "tflops": round(flops / (ms / 1e3) / 1e12, 2)}
+
+
+def dense_context(name, steps=10):
+    """Measured ceilings for context (not the target): a dense bf16
+    torch.matmul of the workload's shapes (H [N x D] times a dense [D x V]
+    head, what the packed format avoids storing), and a device-to-device copy
+    of the packed head's size (read + write)."""
+    import torch
+    import synth
+    cfg = synth.config(name)
+    N, V, D = cfg["N"], cfg["V"], cfg["D"]
+    H = torch.randn(N, D, device="cuda", dtype=torch.bfloat16)
+    W = torch.randn(D, V, device="cuda", dtype=torch.bfloat16)
+    out = {}
+    for _ in range(2):
+        torch.matmul(H, W)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        torch.matmul(H, W)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    out["dense_bf16_matmul"] = {"shape": [N, D, V], "ms": round(ms, 4),
+                                "tflops": round(2 * N * V * D / (ms / 1e3) / 1e12, 1),
+                                "dense_head_bytes": 2 * V * D}
+    del H, W
+    src = torch.empty(336 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    out["device_copy"] = {"bytes": src.numel(), "ms": round(ms, 4),
+                          "gbs_read_plus_write": round(2 * src.numel() / (ms / 1e3) / 1e9, 1)}
+    return out
 
 
 def tile_workload(N):
@@ -316,6 +358,7 @@ def main():
     ap.add_argument("--stats", default="prefill",
                     help="workload timed through archead_logits_stats ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run the device copies that calibrate HBM byte counters")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV"),
@@ -381,6 +424,10 @@ def main():
         st = run_stats(args.stats, max(5, args.steps // 5), max(2, args.warmup // 5))
         log(f"[bench] stats on {args.stats}: {st['ms_per_call']:.3f} ms/call")
         out["stats"] = st
+    out["roofline"]["kernel_ms_p10_p50_p90"] = r["kernel_ms_pct"]
+    if not args.no_context and args.secondary:
+        out["context"] = dense_context(args.secondary)
+        log(f"[bench] context: {out['context']}")
     out["kernel_sources"] = kernel_hash()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
