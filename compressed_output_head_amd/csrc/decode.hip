@@ -416,16 +416,13 @@ __global__ __launch_bounds__(kLdsThreads) void decode_lds_kernel(const FwdArgs a
 #endif
 constexpr int kRingDepth = ARCHEAD_RING_DEPTH;  // largest packed-tile ring per wave
 
+// CUs of the current device (256 if the runtime cannot tell)
 int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 template <int P, int G>

@@ -344,17 +344,13 @@ hipError_t launch_mid_nt(const FwdArgs& a, hipStream_t s, int grid) {
   return hipGetLastError();
 }
 
+// CUs of the current device (256 if the runtime cannot tell)
 int mid_cu_count() {
-  static int cached = 0;
-  if (cached == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      cached = cus;
-    else
-      return 256;
-  }
-  return cached;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
 }
 
 }  // namespace
