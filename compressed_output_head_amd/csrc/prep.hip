@@ -388,24 +388,39 @@ __global__ __launch_bounds__(kPrepZThreads) void prep_z_kernel(const FwdArgs a) 
   const uint16_t* hrow = a.H + n * a.H_stride;
   const int nchunk = (int)(a.D / 8);
   if ((int)blockIdx.y == nJ) {
+    // the row's first kPrepZKeep * 256 chunks stay in registers between the
+    // maximum and the conversion (one read of H for D <= 8192)
+    constexpr int kPrepZKeep = 4;
     __shared__ float red[kPrepZThreads / 64];
+    u4 keep[kPrepZKeep];
+#pragma unroll
+    for (int i = 0; i < kPrepZKeep; ++i) {
+      const int c = tid + i * kPrepZThreads;
+      keep[i] = c < nchunk ? *reinterpret_cast<const u4*>(hrow + 8 * c) : u4{0u, 0u, 0u, 0u};
+    }
+    // f(chunk index, its 8 bf16 values) for every chunk of this thread
+    auto each_chunk = [&](auto f) {
+#pragma unroll
+      for (int i = 0; i < kPrepZKeep; ++i)
+        if (tid + i * kPrepZThreads < nchunk) f(tid + i * kPrepZThreads, keep[i]);
+      for (int c = tid + kPrepZKeep * kPrepZThreads; c < nchunk; c += kPrepZThreads)
+        f(c, *reinterpret_cast<const u4*>(hrow + 8 * c));
+    };
     float m = 0.0f;
-    for (int c = tid; c < nchunk; c += kPrepZThreads) {
-      const u4 raw = *reinterpret_cast<const u4*>(hrow + 8 * c);
+    each_chunk([&](int, const u4& raw) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] & 0xffffu))));
         m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(raw[w] >> 16))));
       }
-    }
+    });
     m = wave_max(m);
     if (lane == 0) red[wave] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const int S = row_exponent(m);
     if (tid == 0) a.hscale[n] = ldexpf(1.0f, -S);
-    for (int c = tid; c < nchunk; c += kPrepZThreads) {
-      const u4 raw = *reinterpret_cast<const u4*>(hrow + 8 * c);
+    each_chunk([&](int c, const u4& raw) {
       float v[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -416,7 +431,7 @@ __global__ __launch_bounds__(kPrepZThreads) void prep_z_kernel(const FwdArgs a) 
 #pragma unroll
       for (int j = 0; j < 8; ++j) out[j] = (_Float16)ldexpf(v[k_order_h(j)], S);
       *reinterpret_cast<h8*>(a.hc + n * a.D + 8 * c) = out;
-    }
+    });
     return;
   }
   const int j = blockIdx.y * (kPrepZThreads / 64) + wave;
