@@ -1,9 +1,11 @@
-// Tile path (any N, used for N > 64): LDS-tiled fp16 MFMA contraction.
+// Tile path (any N the few-token decode kernel does not take): the 32-row
+// tile kernel (tile32.h) when every section fits 32-bit buffer offsets, else
+// the 16-row LDS-tiled kernel below.
 //
 // Y = [H | Z] [R | A_c ; A_w]^T, i.e. Algorithm 1's inference step with the
 // quantised core evaluated through the same (H B^T) A^T association.
 //
-// A workgroup owns a TM x TN (tokens x vocabulary) output tile and walks the
+// 16-row kernel: a workgroup owns a TM x TN (tokens x vocabulary) output tile and walks the
 // hidden dimension in 128-column steps.  Per step it copies the TM token rows
 // of hf (already fp16 operand fragments) into LDS, and unpacks the TN/16
 // residual tiles from their packed INT4 form into LDS as exact fp16 integers

@@ -15,14 +15,15 @@ namespace archead {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Large-N kernel on the 32 x 32 x 16 MFMA: 256 tokens x 256 vocabulary rows
-// per workgroup, eight waves in a 2 x 4 grid (two per SIMD), 128 x 64 per
-// wave (8 result tiles of 32 x 32, 128 fp32 accumulators per lane).  The
-// hidden dimension advances 64 columns (4 MFMA steps) per stage.
+// Tile kernel on the 32 x 32 x 16 MFMA: 32 TT tokens x 256 vocabulary rows
+// per workgroup (TT = 2, 4 or 8 token tiles), eight waves (two per SIMD).
+// Each wave takes all the workgroup's tokens and one 32-row vocabulary block
+// (TT result tiles of 32 x 32, 16 TT fp32 accumulators per lane).  The hidden
+// dimension advances 16 KS columns (KS MFMA steps) per stage.
 //
 //   H (32-row layout, written by the prep kernel): an LDS ring of 4 stages of
-//     8 token tiles x 4 steps x 1 KB fragments, filled by buffer loads straight
-//     into LDS three stages ahead; one barrier per stage.
+//     TT token tiles x KS steps x 1 KB fragments, filled by buffer loads
+//     straight into LDS four stages ahead; one barrier per stage.
 //   W: lane l of a wave reads, for 32-row vocabulary block CB, row l%16 of
 //     packed block 2 CB + (l/16)%2 at packed lane (l%16) + 16 q, q = l/32 in
 //     the first half of a k-tile and l/32 + 2 in the second; the 16 bytes give
@@ -30,7 +31,7 @@ namespace {
 //     four stages ahead in a register ring.  Step t of half h thus covers runs
 //     R = 4 t + 2 h + l/32, the order the prep kernel gives H.
 //   Group codes: the workgroup's 256 rows of codes are copied to LDS once.
-// Each MFMA step's operands (4 H fragments from LDS, the W fragments unpacked
+// Each MFMA step's operands (TT H fragments from LDS, the W fragment unpacked
 // to exact fp16 integers q4 * c8) are fetched while the previous step's MFMAs
 // run, and the next stage's first step is fetched right after the barrier
 // that publishes it.  Every global read goes through a buffer resource: a
