@@ -188,3 +188,30 @@ def test_row_strides_and_offsets():
         torch.cuda.synchronize()
         check_parity(Y.cpu().numpy().astype(np.float64), Yr, f"strided path={path}")
         assert torch.isnan(Ybig[:, :100]).all() and torch.isnan(Ybig[:, 600:]).all()
+
+
+@pytest.mark.parametrize("N", [40, 200])
+def test_split_tiles_with_unaligned_outputs(N):
+    """Few vocabulary tiles on a deep hidden dimension: the tile path splits
+    every tile's hidden dimension over several workgroups and adds the parts
+    in a second kernel; here into fp32 and bf16 outputs whose rows are
+    neither 16-byte aligned nor a multiple of 4 elements apart."""
+    torch = torch_mod()
+    ah = ah_mod()
+    V, D = 1000, 2048
+    inp = synth.make("tiny", seed=N, V=V, D=D, N=N, r_c=16, r_r=8, g=64, n_outlier=4)
+    head = _head(inp)
+    H = device_H(inp.H_bits)
+    Yr = oracle.logits(inp.H_bits, inp.head)
+    for dt in (torch.float32, torch.bfloat16):
+        Ybig = torch.full((N, V + 7), float("nan"), dtype=dt, device="cuda")
+        Y = Ybig[:, 3:3 + V]  # row stride V + 7, start 3 elements in
+        ah.archead_logits_path(H, head, Y, TILE)
+        torch.cuda.synchronize()
+        assert torch.isnan(Ybig[:, :3]).all() and torch.isnan(Ybig[:, 3 + V:]).all()
+        Yg = Y.float().cpu().numpy().astype(np.float64)
+        if dt == torch.float32:
+            check_parity(Yg, Yr, f"split N={N} fp32")
+            y32 = Y.clone()
+        else:
+            assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), Y.contiguous().view(torch.int16))
