@@ -338,3 +338,101 @@ def row_stats(Y, targets=None):
         t = np.asarray(targets, np.int64)
         out["ce"] = out["lse"] - Y[np.arange(Y.shape[0]), t]
     return out
+
+
+# ------------------------------------------------------------- quantizers ---
+#
+# The packing step of Algorithm 1 (ARCHead, Algorithm 1 and the Sec. 3
+# quantized-core sentence): the core factors are quantised (Q_b), the residual
+# the quantised core leaves, R = W - Q(A_c) Q(B_c), goes to SC4, and the
+# correction factors are stored with row-wise (A_w) and group-wise (B_w) INT8.
+# The page fixes no rounding rule, scale formula or range; the readings here
+# are symmetric absmax scaling with round-half-to-even:
+#   INT8 (rows of A, or g-column groups of rows of B): s = fp16(amax / 127),
+#     code = clamp(rint(x / s), -127, 127), 0 where s = 0;
+#   SC4 (rows of R in g-column groups): with m_t the group's amax,
+#     s_R = fp16(max_t m_t / (7 * 255)),
+#     c8_t = clamp(ceil(m_t / (7 s_R)), 1, 255) (the smallest step that keeps
+#     the group within [-7, 7], up to the fp16 rounding of s_R),
+#     q4 = clamp(rint(r / (c8_t s_R)), -8, 7); s_R = 0 gives c8 = 0, q4 = 0.
+# Every decision (the division and the rounding to an integer, the fp16
+# rounding of a scale) is taken in fp32 from fp32 operands, the precision the
+# GPU kernels use; the residual itself is accumulated in fp64 over the core
+# rank in index order (each product is exact in fp64) and then rounded once
+# to fp32.  E = W - W_d, the error the correction is fitted to, is returned as
+# fp32(R) - fp32(SC4 dequantised R).
+
+def quant_int8_rows(M32):
+    """Row-wise symmetric INT8 of a float32 matrix: (codes int8, scales fp16)."""
+    M32 = np.asarray(M32, np.float32)
+    if M32.shape[1] == 0:
+        return np.zeros(M32.shape, np.int8), np.zeros(M32.shape[0], np.float16)
+    amax = np.abs(M32).max(axis=1)
+    s = (amax / np.float32(127)).astype(np.float16)
+    s32 = s.astype(np.float32)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s32 > 0, np.rint(M32 / np.where(s32 > 0, s32, np.float32(1))), 0)
+    return np.clip(q, -127, 127).astype(np.int8), s
+
+
+def quant_int8_groups(M32, g):
+    """Group-wise (g columns) symmetric INT8 of a float32 matrix:
+    (codes int8 [n, D], scales fp16 [n, D/g])."""
+    M32 = np.asarray(M32, np.float32)
+    n, D = M32.shape
+    q, s = quant_int8_rows(M32.reshape(n * (D // g), g))
+    return q.reshape(n, D), s.reshape(n, D // g)
+
+
+def quant_sc4(R32, g):
+    """SC4 of a float32 residual: (q4 int8 in [-8, 7], c8 uint8 [V, D/g], s_R fp16)."""
+    R32 = np.asarray(R32, np.float32)
+    V, D = R32.shape
+    ng = D // g
+    m = np.abs(R32).reshape(V, ng, g).max(axis=2)                     # [V, ng]
+    s_R = (m.max(axis=1) / np.float32(7 * 255)).astype(np.float16)
+    sR32 = s_R.astype(np.float32)
+    den = np.float32(7) * sR32                                         # exact
+    ok = (sR32 > 0)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c8 = np.where(ok, np.clip(np.ceil(m / np.where(ok, den[:, None], np.float32(1))), 1, 255), 0)
+    c8 = c8.astype(np.uint8)
+    scale = np.repeat(c8.astype(np.float32) * sR32[:, None], g, axis=1)   # exact
+    okk = scale > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q4 = np.where(okk, np.clip(np.rint(R32 / np.where(okk, scale, np.float32(1))), -8, 7), 0)
+    return q4.astype(np.int8), c8, s_R
+
+
+def core_residual(W64, qa, sa, qb, sb, g):
+    """R = W - Q(A_c) Q(B_c) in fp64, the core rank accumulated in index order."""
+    acc = np.zeros_like(W64)
+    a = qa.astype(np.float64) * f16_to_f64(sa)[:, None]                # [V, r_c], exact
+    b = qb.astype(np.float64) * np.repeat(f16_to_f64(sb), g, axis=1)   # [r_c, D], exact
+    for j in range(qa.shape[1]):
+        acc = acc + a[:, j:j + 1] * b[j:j + 1, :]                      # exact products
+    return W64 - acc
+
+
+def quantize(W, A_c, B_c, A_w, B_w, g):
+    """Quantise a dense head and its factors into the packed components.
+
+    W: [V, D] as bf16 bit patterns (uint16) or float32; A_c [V, r_c], B_c
+    [r_c, D], A_w [V, r_r], B_w [r_r, D]: float32.  Returns (head, E) where
+    head has the attributes ``pack`` reads and E is float32 [V, D]."""
+    from types import SimpleNamespace
+    W = np.asarray(W)
+    W64 = bf16_bits_to_f64(W) if W.dtype == np.uint16 else W.astype(np.float32).astype(np.float64)
+    V, D = W64.shape
+    r_c, r_r = A_c.shape[1], A_w.shape[1]
+    qa, sa = quant_int8_rows(A_c)
+    qb, sb = quant_int8_groups(B_c, g) if r_c else (np.zeros((0, D), np.int8), np.zeros((0, D // g), np.float16))
+    R32 = core_residual(W64, qa, sa, qb, sb, g).astype(np.float32)
+    q4, c8, s_R = quant_sc4(R32, g)
+    deq = (q4.astype(np.float32) * np.repeat(c8.astype(np.float32) * s_R.astype(np.float32)[:, None], g, axis=1))
+    E = R32 - deq
+    qaw, saw = quant_int8_rows(A_w)
+    qbw, sbw = quant_int8_groups(B_w, g) if r_r else (np.zeros((0, D), np.int8), np.zeros((0, D // g), np.float16))
+    head = SimpleNamespace(V=V, D=D, r_c=r_c, r_r=r_r, g=g, q4=q4, c8=c8, s_R=s_R,
+                           A_c=qa, s_Ac=sa, B_c=qb, s_Bc=sb, A_w=qaw, s_Aw=saw, B_w=qbw, s_Bw=sbw)
+    return head, E

@@ -513,3 +513,111 @@ def test_row_stats_invariants():
     assert (a["ce"] >= 0).all()
     T = np.array([[1.0, 3.0, 3.0, -1.0], [0.0, 0.0, 0.0, 0.0]])
     assert oracle.row_stats(T)["argmax"].tolist() == [1, 0]
+
+
+# -------------------------------------------------------------- quantizers ---
+
+
+def test_int8_quantizers_recover_exact_codes():
+    """Matrices built as code x fp16 scale, each row (group) holding a code of
+    magnitude 127, quantise back to the same codes and scales; an all-zero
+    row gets scale 0 and codes 0."""
+    rng = np.random.default_rng(21)
+    codes = rng.integers(-127, 128, size=(6, 40)).astype(np.int8)
+    codes[np.arange(6), rng.integers(0, 40, size=6)] = rng.choice([-127, 127], size=6)
+    codes[5] = 0
+    s = np.abs(rng.normal(0, 1e-2, size=6)).astype(np.float16)
+    s[5] = 0
+    M = codes.astype(np.float32) * s.astype(np.float32)[:, None]      # exact in fp32
+    q, sq = oracle.quant_int8_rows(M)
+    assert np.array_equal(q, codes) and np.array_equal(sq.view(np.uint16), s.view(np.uint16))
+    g = 8
+    cg = rng.integers(-127, 128, size=(3, 32)).astype(np.int8)
+    cg[:, ::g] = 127
+    sg = np.abs(rng.normal(0, 1e-3, size=(3, 4))).astype(np.float16)
+    Mg = cg.astype(np.float32) * np.repeat(sg.astype(np.float32), g, axis=1)
+    qg, sqg = oracle.quant_int8_groups(Mg, g)
+    assert np.array_equal(qg, cg) and np.array_equal(sqg.view(np.uint16), sg.view(np.uint16))
+
+
+def test_int8_rounding_and_bounds():
+    """Ties round to even; every unclamped code is within half a step; the
+    largest magnitude of a row lands on 127 (or 126 after the scale's fp16
+    rounding)."""
+    s = np.float32(np.float16(0.25))
+    M = np.array([[127 * s, 0.5 * s, 1.5 * s, -2.5 * s, 2.5 * s, -0.5 * s]], np.float32)
+    q, sq = oracle.quant_int8_rows(M)
+    assert q.tolist() == [[127, 0, 2, -2, 2, 0]] and float(sq[0]) == 0.25
+    rng = np.random.default_rng(22)
+    X = rng.normal(0, 3.0, size=(50, 33)).astype(np.float32)
+    q, sq = oracle.quant_int8_rows(X)
+    step = sq.astype(np.float64)[:, None]
+    assert (np.abs(X - q * step) <= step / 2 + 1e-12 * np.abs(X)).all()
+    top = np.abs(q[np.arange(50), np.abs(X).argmax(axis=1)])
+    assert ((top == 127) | (top == 126)).all()
+
+
+def test_sc4_recovers_exact_codes_and_zero_groups():
+    """R built as q4 x c8 x s_R with a code of magnitude 7 in every group and
+    a group code of 255 in every row quantises back to the same components;
+    an all-zero group gets group code 1, an all-zero row group codes 0."""
+    rng = np.random.default_rng(23)
+    V, D, g = 5, 64, 16
+    q4 = rng.integers(-7, 8, size=(V, D)).astype(np.int8)
+    q4[:, ::g] = 7
+    c8 = rng.integers(1, 256, size=(V, D // g)).astype(np.uint8)
+    c8[:, 1] = 255
+    s_R = np.abs(rng.normal(0, 1e-3, size=V)).astype(np.float16)
+    q4[1, 2 * g:3 * g] = 0                      # a zero group
+    q4[4] = 0                                   # a zero row
+    R = q4.astype(np.float32) * np.repeat(c8.astype(np.float32) * s_R.astype(np.float32)[:, None], g, axis=1)
+    q, c, s = oracle.quant_sc4(R, g)
+    want_c8 = c8.copy()
+    want_c8[1, 2] = 1
+    want_c8[4] = 0
+    want_s = s_R.copy()
+    want_s[4] = 0
+    assert np.array_equal(q, q4) and np.array_equal(c, want_c8)
+    assert np.array_equal(s.view(np.uint16), want_s.view(np.uint16))
+
+
+def test_core_residual_brute_force():
+    """R = W - Q(A_c) Q(B_c) against exact rational arithmetic."""
+    rng = np.random.default_rng(24)
+    V, D, r, g = 3, 8, 3, 4
+    W = rng.normal(0, 1, size=(V, D))
+    qa = rng.integers(-127, 128, size=(V, r)).astype(np.int8)
+    sa = np.abs(rng.normal(0, 1e-2, size=V)).astype(np.float16)
+    qb = rng.integers(-127, 128, size=(r, D)).astype(np.int8)
+    sb = np.abs(rng.normal(0, 1e-2, size=(r, D // g))).astype(np.float16)
+    R = oracle.core_residual(W, qa, sa, qb, sb, g)
+    for v in range(V):
+        for k in range(D):
+            core = sum(Fraction(int(qa[v, j])) * Fraction(float(sa[v])) * Fraction(int(qb[j, k])) *
+                       Fraction(float(sb[j, k // g])) for j in range(r))
+            exact = Fraction(float(W[v, k])) - core
+            assert abs(float(exact) - R[v, k]) <= 1e-15 * max(1.0, abs(float(exact)))
+
+
+def test_quantize_end_to_end_reconstructs_w():
+    """The packed head's dequantised weights plus the returned error E give
+    back W (to the fp32 rounding of the residual); the packed bytes decode to
+    the same components."""
+    rng = np.random.default_rng(25)
+    V, D, r_c, g = 37, 256, 8, 64
+    W = rng.normal(0, 0.02, size=(V, D)).astype(np.float32)
+    A = rng.normal(0, 1, size=(V, r_c)).astype(np.float32)
+    B = rng.normal(0, 0.01, size=(r_c, D)).astype(np.float32)
+    head, E = oracle.quantize(W, A, B, np.zeros((V, 0), np.float32), np.zeros((0, D), np.float32), g)
+    back = oracle.w_hat(head) + E.astype(np.float64)
+    assert np.allclose(back, W, rtol=0, atol=2.0 ** -23 * np.abs(W).max())
+    u = oracle.unpack(oracle.pack(head), V, D, r_c, 0, g)
+    assert np.array_equal(u["q4"], head.q4) and np.array_equal(u["c8"], head.c8)
+    # the error is what SC4 cannot represent: half a group step (the group
+    # code rounds up, so no code clamps beyond the fp16 rounding of s_R)
+    step = np.repeat(head.c8.astype(np.float64) * head.s_R.astype(np.float64)[:, None], g, axis=1)
+    assert (np.abs(E) <= step * (0.5 + 7 * 2.0 ** -10)).all()
+    # a group whose amax is 1.3 steps of the row's unit needs group code 2
+    # (rounding to 1 would clamp its largest code from 9 to 7)
+    small = oracle.quant_sc4(np.array([[1.0, 0.0, 0.0051, -0.002]], np.float32), 2)
+    assert small[1].tolist() == [[255, 2]] and small[0].tolist() == [[7, 0, 5, -2]]
