@@ -24,7 +24,7 @@ STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5
           6: "E_ALIGN", 7: "E_WORKSPACE", 8: "E_HIP", 9: "E_VALUE", 10: "E_SIZE"}
 EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_pack", "archead_logits",
            "archead_logits_path", "archead_logits_events", "archead_stats_workspace_bytes",
-           "archead_logits_stats", "archead_status_string", "archead_format_version")
+           "archead_logits_stats", "archead_quantize", "archead_status_string", "archead_format_version")
 
 
 class ArcheadError(RuntimeError):
@@ -73,6 +73,12 @@ class ArcheadRowStats(ctypes.Structure):
                 ("row_ce", ctypes.c_void_p), ("targets", ctypes.c_void_p)]
 
 
+class ArcheadDenseHead(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("W_stride", ctypes.c_int64), ("W_dtype", ctypes.c_int32),
+                ("A_c", ctypes.c_void_p), ("B_c", ctypes.c_void_p), ("A_w", ctypes.c_void_p),
+                ("B_w", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python compressed_output_head_amd/build.py`")
@@ -96,6 +102,8 @@ def _load():
     lib.archead_stats_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int64, P(ctypes.c_uint64)]
     lib.archead_logits_stats.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadRowStats),
                                          ctypes.c_void_p]
+    lib.archead_quantize.argtypes = [P(ArcheadDims), P(ArcheadDenseHead), ctypes.c_void_p, ctypes.c_uint64,
+                                     P(ArcheadTensor), ctypes.c_void_p]
     lib.archead_status_string.argtypes = [ctypes.c_int]
     lib.archead_status_string.restype = ctypes.c_char_p
     lib.archead_format_version.argtypes = []
@@ -295,3 +303,34 @@ def archead_logits_stats(H, head: PackedHead, targets=None, stream=None, outputs
     _check(lib.archead_logits_stats(ctypes.byref(h), ctypes.byref(p), ctypes.byref(st), ctypes.c_void_p(stream)),
            "archead_logits_stats")
     return out
+
+
+def archead_quantize(W, A_c, B_c, A_w, B_w, g: int, with_error: bool = False, stream=None):
+    """Quantise a dense head on the GPU into a packed head (the packing step:
+    INT8 factors, SC4 residual of the quantised core).  W: bf16 or fp32 [V, D]
+    device tensor; A_c [V, r_c], B_c [r_c, D], A_w [V, r_r], B_w [r_r, D]:
+    fp32 device tensors.  Returns (PackedHead, E) where E is the fp32 [V, D]
+    error left after the residual codes when ``with_error``, else None."""
+    torch = _torch()
+    V, D = W.shape
+    r_c, r_r = A_c.shape[1], A_w.shape[1]
+    for name, t, shape in (("A_c", A_c, (V, r_c)), ("B_c", B_c, (r_c, D)), ("A_w", A_w, (V, r_r)),
+                           ("B_w", B_w, (r_r, D))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {shape}")
+    L = archead_pack_layout(V, D, r_c, r_r, g)
+    buf = torch.empty(L["total_bytes"], dtype=torch.uint8, device=W.device)
+    E = torch.empty((V, D), dtype=torch.float32, device=W.device) if with_error else None
+    if stream is None:
+        stream = torch.cuda.current_stream(W.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    w = _tensor(W)
+    src = ArcheadDenseHead(w.data, w.row_stride, w.dtype,
+                           *(t.data_ptr() if t.numel() else None for t in (A_c, B_c, A_w, B_w)))
+    e = _tensor(E) if E is not None else None
+    _check(lib.archead_quantize(ctypes.byref(_dims(V, D, r_c, r_r, g)), ctypes.byref(src),
+                                ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                ctypes.byref(e) if e is not None else None, ctypes.c_void_p(stream)),
+           "archead_quantize")
+    return PackedHead(V, D, r_c, r_r, g, buf), E

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libarchead.so")
-SOURCES = ["archead.hip", "prep.hip", "decode.hip", "mid.hip", "tile.hip", "tile_stats.hip", "stats.hip"]
+SOURCES = ["archead.hip", "prep.hip", "decode.hip", "mid.hip", "tile.hip", "tile_stats.hip", "stats.hip",
+           "quantize.hip"]
 ARCH = os.environ.get("ARCHEAD_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

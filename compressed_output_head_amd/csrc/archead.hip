@@ -187,7 +187,7 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
   memset(out, 0, L.total_bytes);
   // header
   {
-    uint32_t u32[2] = {0x48435241u, ARCHEAD_FORMAT_VERSION};
+    uint32_t u32[2] = {ARCHEAD_MAGIC, ARCHEAD_FORMAT_VERSION};
     uint64_t u64[2] = {(uint64_t)V, (uint64_t)D};
     uint32_t u32b[4] = {(uint32_t)r_c, (uint32_t)r_r, (uint32_t)g, 0u};
     memcpy(out, u32, 8);

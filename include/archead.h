@@ -38,6 +38,7 @@ extern "C" {
 #endif
 
 #define ARCHEAD_FORMAT_VERSION 1
+#define ARCHEAD_MAGIC 0x48435241u /* "ARCH" little-endian, first word of a packed buffer */
 #define ARCHEAD_ALIGNMENT 256
 
 typedef enum {
@@ -156,6 +157,45 @@ ARCHEAD_API int archead_workspace_bytes(const archead_dims* d, int64_t n_tokens,
  * Host only; multithreaded.  E_NULL, E_DIMS, E_SIZE, E_VALUE. */
 ARCHEAD_API int archead_pack(const archead_dims* d, const archead_host_components* src, void* dst,
                  uint64_t dst_bytes);
+
+/* Dense inputs of the packing step (Algorithm 1 and the Sec. 3 quantized-core
+ * sentence): the head W and the factor matrices, all device memory, row-major.
+ *   W    [V][D]   bf16 or fp32 (W_dtype), row stride W_stride elements; W and
+ *                 every row 16-byte aligned
+ *   A_c  [V][r_c] fp32, B_c [r_c][D] fp32   the low-rank core (e.g. a truncated SVD of W)
+ *   A_w  [V][r_r] fp32, B_w [r_r][D] fp32   the activation-metric correction
+ * Factors of a part of rank 0 may be NULL. */
+typedef struct {
+  const void* W;
+  int64_t W_stride;
+  int32_t W_dtype; /* archead_dtype */
+  const float* A_c;
+  const float* B_c;
+  const float* A_w;
+  const float* B_w;
+} archead_dense_head;
+
+/* Quantise a dense head into a packed buffer on the GPU (the packing step of
+ * Algorithm 1; ARCHead Sec. 3, quantized-core equation and packed-variant
+ * paragraph).  The pages fix no rounding rule or scale formula; this uses
+ * symmetric absmax scaling with round half to even, every decision in fp32:
+ *   INT8 (rows of A_c and A_w; g-column groups of the rows of B_c and B_w):
+ *     s = fp16(amax / 127), code = clamp(rint(x / s), -127, 127), 0 where s = 0;
+ *   R = W - Q(A_c) Q(B_c), accumulated in fp64 over the core rank in index
+ *     order and rounded once to fp32;
+ *   SC4 of R (g-column groups t of row v, m_t = the group's amax):
+ *     s_R = fp16(max_t m_t / 1785), c8_t = clamp(ceil(m_t / (7 s_R)), 1, 255),
+ *     q4 = clamp(rint(R / (c8_t s_R)), -8, 7); a zero row gives s_R = c8 = q4 = 0.
+ * packed: device, 256-byte aligned, packed_bytes >= archead_layout.total_bytes;
+ *   every byte of the layout is written (padding rows and gaps are zero).
+ * E: optional fp32 [V][D] device tensor (NULL: not written), rows 16-byte
+ *   aligned; receives fp32(R) - SC4(R), the error left after the residual
+ *   codes (what the correction A_w B_w is meant to absorb).
+ * Enqueued on `stream` without synchronising; allocates nothing.
+ * E_NULL, E_DIMS, E_UNSUPPORTED (g not in {32, 64, 128, 256}, D > 8192, a
+ * rank above 65536), E_DTYPE, E_SHAPE, E_ALIGN, E_SIZE, E_HIP. */
+ARCHEAD_API int archead_quantize(const archead_dims* d, const archead_dense_head* src, void* packed,
+                                 uint64_t packed_bytes, archead_tensor* E, void* stream);
 
 /* Y = H W_hat^T  (Algorithm 1, inference step).
  *   H: bf16 [N][D] device tensor; rows 16-byte aligned.

@@ -136,6 +136,34 @@ def draw_head(rng, V, D, r_c, r_r, g) -> Head:
     return Head(V, D, r_c, r_r, g, q4, c8, s_R, A_c, A_w, s_Ac, s_Aw, B_c, B_w, s_Bc, s_Bw)
 
 
+@dataclass
+class Dense:
+    """Dense inputs of the packing step: the head W and the factor matrices."""
+    W: np.ndarray      # [V, D] bf16 bit patterns (uint16) or float32
+    A_c: np.ndarray    # [V, r_c] float32
+    B_c: np.ndarray    # [r_c, D] float32
+    A_w: np.ndarray    # [V, r_r] float32
+    B_w: np.ndarray    # [r_r, D] float32
+
+
+def draw_dense(rng, V, D, r_c, r_r, w_dtype="bf16", n_heavy_rows=4) -> Dense:
+    """Dense head and factors, drawn independently.
+
+    W      N(0, 0.02) in fp32; n_heavy_rows rows (chosen uniformly) x 30, so that
+           row scales differ by orders of magnitude; bf16 (rounded once) or fp32.
+    A_c    N(0, 0.1) fp32;  B_c N(0, 0.1) fp32.
+    A_w    N(0, 0.05) fp32; B_w N(0, 0.05) fp32.
+    Draw order: W, heavy rows, A_c, B_c, A_w, B_w."""
+    W = rng.normal(0.0, 0.02, size=(V, D)).astype(np.float32)
+    heavy = rng.choice(V, size=min(n_heavy_rows, V), replace=False)
+    W[heavy] *= np.float32(30.0)
+    A_c = rng.normal(0.0, 0.1, size=(V, r_c)).astype(np.float32)
+    B_c = rng.normal(0.0, 0.1, size=(r_c, D)).astype(np.float32)
+    A_w = rng.normal(0.0, 0.05, size=(V, r_r)).astype(np.float32)
+    B_w = rng.normal(0.0, 0.05, size=(r_r, D)).astype(np.float32)
+    return Dense(f32_to_bf16_bits(W) if w_dtype == "bf16" else W, A_c, B_c, A_w, B_w)
+
+
 def make(cfg, seed: Optional[int] = None, N: Optional[int] = None, **overrides) -> Inputs:
     """Draw one workload.  ``cfg`` is a CONFIGS entry, its name or its index.
 

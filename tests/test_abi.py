@@ -211,6 +211,45 @@ def test_stats_error_paths(ah):
     H, P, st = args(N=0); H.data = None; P.workspace = None; assert call(H, P, st) == 0
 
 
+def test_quantize_error_paths(ah):
+    """archead_quantize rejects bad arguments on the host, before any HIP call."""
+    V, D, r_c, r_r, g = 1000, 512, 16, 8, 64
+    total = ah.archead_pack_layout(V, D, r_c, r_r, g)["total_bytes"]
+
+    def call(dims=(V, D, r_c, r_r, g), W=FAKE, ws=D, wdt=1, A_c=FAKE + (1 << 30), B_c=FAKE + (2 << 30),
+             A_w=FAKE + (3 << 30), B_w=FAKE + (4 << 30), buf=FAKE + (8 << 30), nbytes=total, E=None):
+        src = ah.ArcheadDenseHead(W, ws, wdt, A_c, B_c, A_w, B_w)
+        return ah.lib.archead_quantize(ctypes.byref(ah._dims(*dims)), ctypes.byref(src), buf, nbytes,
+                                       ctypes.byref(E) if E is not None else None, None)
+
+    def E(**kw):
+        f = dict(data=FAKE + (16 << 30), rows=V, cols=D, row_stride=D, dtype=2)
+        f.update(kw)
+        return ah.ArcheadTensor(f["data"], f["rows"], f["cols"], f["row_stride"], f["dtype"])
+
+    assert ah.lib.archead_quantize(None, None, None, 0, None, None) == 1
+    assert call(W=None) == 1
+    assert call(buf=None) == 1
+    assert call(A_c=None) == 1
+    assert call(B_w=None) == 1
+    assert call(dims=(V, D, 0, 8, g), A_c=None, B_c=None, nbytes=0) == 10        # rank-0 part may be NULL
+    assert call(dims=(V, 500, r_c, r_r, g)) == 2                                 # D not a multiple of 128
+    assert call(dims=(V, D, r_c, r_r, 16)) == 3                                  # group size
+    assert call(dims=(V, 8192 + 128, r_c, r_r, g)) == 3                          # D above the register limit
+    assert call(wdt=3) == 4
+    assert call(ws=D - 1) == 5
+    assert call(W=FAKE + 8) == 6                                                  # W not 16-byte aligned
+    assert call(ws=D + 4, wdt=1) == 6                                             # bf16 rows of 1032 bytes
+    assert call(A_w=FAKE + 2) == 6
+    assert call(buf=FAKE + 128) == 6
+    assert call(nbytes=total - 1) == 10
+    assert call(E=E(data=None)) == 1
+    assert call(E=E(dtype=1)) == 4
+    assert call(E=E(rows=V - 1)) == 5
+    assert call(E=E(row_stride=D - 4)) == 5
+    assert call(E=E(row_stride=D + 2)) == 6
+
+
 def test_logits_zero_tokens_is_a_noop(ah):
     H, P, Y, need, total = _args(ah, N=0)
     H.data = Y.data = None
