@@ -235,6 +235,48 @@ def run_stats(name, steps, warmup):
             "tflops": round(flops / (ms / 1e3) / 1e12, 2)}
 
 
+FP64_PEAK_TFLOPS = 78.6  # MI355X vector fp64
+
+
+def run_quantize(name, steps, warmup):
+    """archead_quantize (the packing step) on one workload's head shape: dense
+    bf16 W and fp32 factors resident in HBM, K timed calls of the whole step
+    (zero fill, header, four INT8 passes, the residual/SC4 kernel), without
+    the optional error output.  The residual kernel is fp64-bound: 2 V D r_c
+    flops of core products; the HBM bytes are W read once plus the packed
+    buffer written once."""
+    import torch
+    import synth
+    import compressed_output_head_amd as ah
+
+    cfg = synth.config(name)
+    V, D, r_c, r_r, g = cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"]
+    dense = synth.draw_dense(np.random.default_rng(2024), V, D, r_c, r_r, "bf16")
+    W = torch.from_numpy(dense.W.view(np.int16)).view(torch.bfloat16).cuda()
+    F = [torch.from_numpy(x).cuda() for x in (dense.A_c, dense.B_c, dense.A_w, dense.B_w)]
+    del dense
+    for _ in range(warmup):
+        ah.archead_quantize(W, *F, g)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        ah.archead_quantize(W, *F, g)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = 2 * V * D * r_c
+    nbytes = 2 * V * D + ah.archead_pack_layout(V, D, r_c, r_r, g)["total_bytes"]
+    tf = flops / (ms / 1e3) / 1e12
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": name, "V": V, "D": D, "r_c": r_c, "r_r": r_r, "g": g, "W": "bf16",
+            "ms_per_call": round(ms, 4), "steps": steps, "timed": "whole call",
+            "fp64_tflops": round(tf, 2), "fp64_frac": round(tf / FP64_PEAK_TFLOPS, 4),
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic": {"fp64_flops": flops, "bytes": nbytes}}
+
+
 def dense_context(name, steps=10):
     """Measured ceilings for context (not the target): a dense bf16
     torch.matmul of the workload's shapes (H [N x D] times a dense [D x V]
@@ -357,6 +399,8 @@ def main():
                          "workloads, 4096 for tile-type ones)")
     ap.add_argument("--stats", default="prefill",
                     help="workload timed through archead_logits_stats ('' to skip)")
+    ap.add_argument("--quantize", default="decode",
+                    help="head shape timed through archead_quantize, the packing step ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -424,6 +468,10 @@ def main():
         st = run_stats(args.stats, max(5, args.steps // 5), max(2, args.warmup // 5))
         log(f"[bench] stats on {args.stats}: {st['ms_per_call']:.3f} ms/call")
         out["stats"] = st
+    if args.quantize:
+        q = run_quantize(args.quantize, max(3, args.steps // 10), 2)
+        log(f"[bench] quantize on {args.quantize}: {q['ms_per_call']:.3f} ms/call")
+        out["quantize"] = q
     out["roofline"]["kernel_ms_p10_p50_p90"] = r["kernel_ms_pct"]
     if not args.no_context and args.secondary:
         out["context"] = dense_context(args.secondary)

@@ -31,8 +31,10 @@ struct QuantArgs {
   int64_t E_stride;
 };
 
-// The largest hidden size the residual kernel holds in registers.
+// The largest hidden size the residual kernel holds in registers, and the
+// largest core rank whose dequantised factor rows it keeps in LDS.
 constexpr int64_t kQuantMaxD = 8192;
+constexpr int kQuantMaxCoreRank = 1024;
 
 // Enqueue the whole packing step on `s`: zero the buffer (total_bytes, a
 // multiple of 256), write the header, quantise A_c, B_c, compute the SC4

@@ -29,7 +29,8 @@ namespace {
 
 constexpr int kQThreads = 256;
 constexpr int kQWaves = kQThreads / 64;
-constexpr int kQMaxRunsPerLane = kQuantMaxD / (64 * 8);  // 8-column runs per lane
+constexpr int kQMaxRunsPerThread = kQuantMaxD / (8 * kQThreads);  // 8-column runs per thread
+constexpr int kQTermBatch = 4;                                     // core terms loaded together
 
 __device__ __forceinline__ float wave_max_f(float v) {
 #pragma unroll
@@ -62,104 +63,164 @@ __global__ __launch_bounds__(kQThreads) void quant_i8_kernel(const float* M, int
   if (lane == 0) scales[i * s_ld + t] = __builtin_bit_cast(uint16_t, s);
 }
 
-// One wave per vocabulary row v: R = W - Q(A_c) Q(B_c) for the row's D
-// columns, held as fp32 in registers (lane l takes the 8-column runs
-// l, l + 64, ...), then SC4 and the packed residual tile bytes (4 bytes =
-// one run), the group codes, the row scale and E = fp32(R) - SC4(R).
+// RB vocabulary rows per workgroup: R = W - Q(A_c) Q(B_c), then SC4 and the
+// packed residual tile bytes (4 bytes = one 8-column run), the group codes,
+// the row scale and E = fp32(R) - SC4(R).  Thread t takes the 8-column runs
+// t, t + 256, ... of all RB rows, so each dequantised B_c value (converted
+// once) feeds RB fp64 multiply-adds; the dequantised A_c values of the RB rows
+// sit in LDS as [j][RB].  Per element the core rank is accumulated in index
+// order with one fma per term (each product is exact, so the fma rounds as
+// the sum acc + a b does).
+template <int RB, int NR>
 __global__ __launch_bounds__(kQThreads) void core_sc4_kernel(const QuantArgs q) {
-  const int lane = threadIdx.x & 63;
-  const int64_t v = (int64_t)blockIdx.x * kQWaves + (threadIdx.x >> 6);
-  if (v >= q.V) return;
-  const int D = q.D, g = q.g, ng = D / g, nruns = D / 8, gr = g / 8;  // runs per group: 4 .. 32
-  const int8_t* acode = q.a_codes + v * q.r;
-  const double sa = q.r_c > 0 ? (double)half_bits_to_f32(q.a_scales[v * q.nA]) : 0.0;
-  float R[kQMaxRunsPerLane][8];
-  float rmax = 0.0f;
+  extern __shared__ double sA[];  // [r_c][RB]
+  __shared__ float sMax[kQWaves][RB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t v0 = (int64_t)blockIdx.x * RB;
+  const int D = (int)q.D, g = q.g, ng = D / g, nruns = D / 8, gr = g / 8;  // runs per group: 4 .. 32
+  for (int idx = tid; idx < q.r_c * RB; idx += kQThreads) {
+    const int j = idx / RB, rr = idx % RB;
+    const int64_t v = v0 + rr;
+    sA[idx] = v < q.V ? (double)q.a_codes[v * q.r + j] * (double)half_bits_to_f32(q.a_scales[v * q.nA]) : 0.0;
+  }
+  __syncthreads();
+  float R[RB][NR][8];
+  float rmax[RB];
 #pragma unroll
-  for (int i = 0; i < kQMaxRunsPerLane; ++i) {
-    const int run = lane + 64 * i;
+  for (int rr = 0; rr < RB; ++rr) rmax[rr] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) R[i][e] = 0.0f;  // runs past D take part in the group shuffles as zeros
+  for (int i = 0; i < NR; ++i) {
+    const int run = tid + kQThreads * i;
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) R[rr][i][e] = 0.0f;  // runs past D and rows past V stay zero
     if (run < nruns) {
-      const int k0 = 8 * run;
-      double w[8];
-      if (q.w_bf16) {
-        const u4 raw = *reinterpret_cast<const u4*>(reinterpret_cast<const uint16_t*>(q.W) + v * q.W_stride + k0);
+      const int k0 = 8 * run, t = k0 / g;
+      double acc[RB][8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[2 * e] = (double)bf16_to_f32((uint16_t)(raw[e] & 0xffffu));
-          w[2 * e + 1] = (double)bf16_to_f32((uint16_t)(raw[e] >> 16));
-        }
-      } else {
-        const float* wf = reinterpret_cast<const float*>(q.W) + v * q.W_stride + k0;
-        const f4 lo = *reinterpret_cast<const f4*>(wf), hi = *reinterpret_cast<const f4*>(wf + 4);
+      for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[e] = (double)lo[e];
-          w[4 + e] = (double)hi[e];
+        for (int e = 0; e < 8; ++e) acc[rr][e] = 0.0;
+      // one term j of the core: codes c as unsigned bytes u = c + 128, and
+      // u sb - 128 sb = c sb is exact in fp32 (an 8-bit code times an 11-bit
+      // significand), so the fma returns it
+      auto term = [&](const u2 braw, const uint16_t sbits, const int j) {
+        const float sb = half_bits_to_f32(sbits);
+        const float nsb = -128.0f * sb;
+        const uint32_t x[2] = {braw[0] ^ 0x80808080u, braw[1] ^ 0x80808080u};
+        double b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = (double)fmaf((float)((x[e >> 2] >> (8 * (e & 3))) & 0xffu), sb, nsb);
+        double a[RB];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) a[rr] = sA[j * RB + rr];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[rr][e] = fma(a[rr], b[e], acc[rr][e]);
+      };
+      const int8_t* bp = q.b_codes + k0;
+      const uint16_t* sp = q.b_scales + t;
+      int j = 0;
+      for (; j + kQTermBatch <= q.r_c; j += kQTermBatch) {  // the batch's loads are in flight together
+        u2 br[kQTermBatch];
+        uint16_t sh[kQTermBatch];
+#pragma unroll
+        for (int u = 0; u < kQTermBatch; ++u) {
+          br[u] = *reinterpret_cast<const u2*>(bp + (int64_t)(j + u) * D);
+          sh[u] = sp[(int64_t)(j + u) * ng];
         }
+#pragma unroll
+        for (int u = 0; u < kQTermBatch; ++u) term(br[u], sh[u], j + u);
       }
-      double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      const int t = k0 / g;
-      for (int j = 0; j < q.r_c; ++j) {
-        const double a = (double)acode[j] * sa;  // exact
-        const u2 braw = *reinterpret_cast<const u2*>(q.b_codes + (int64_t)j * D + k0);
-        const double sb = (double)half_bits_to_f32(q.b_scales[(int64_t)j * ng + t]);
+      for (; j < q.r_c; ++j) term(*reinterpret_cast<const u2*>(bp + (int64_t)j * D), sp[(int64_t)j * ng], j);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int8_t bc = (int8_t)((braw[e >> 2] >> (8 * (e & 3))) & 0xffu);
-          acc[e] = fma(a, (double)bc * sb, acc[e]);  // the product is exact: one rounding, as acc + a b
+      for (int rr = 0; rr < RB; ++rr) {
+        const int64_t v = v0 + rr;
+        if (v < q.V) {
+          double w[8];
+          if (q.w_bf16) {
+            const u4 raw =
+                *reinterpret_cast<const u4*>(reinterpret_cast<const uint16_t*>(q.W) + v * q.W_stride + k0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w[2 * e] = (double)bf16_to_f32((uint16_t)(raw[e] & 0xffffu));
+              w[2 * e + 1] = (double)bf16_to_f32((uint16_t)(raw[e] >> 16));
+            }
+          } else {
+            const float* wf = reinterpret_cast<const float*>(q.W) + v * q.W_stride + k0;
+            const f4 lo = *reinterpret_cast<const f4*>(wf), hi = *reinterpret_cast<const f4*>(wf + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w[e] = (double)lo[e];
+              w[4 + e] = (double)hi[e];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            R[rr][i][e] = (float)(w[e] - acc[rr][e]);
+            rmax[rr] = fmaxf(rmax[rr], fabsf(R[rr][i][e]));
+          }
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        R[i][e] = (float)(w[e] - acc[e]);
-        rmax = fmaxf(rmax, fabsf(R[i][e]));
       }
     }
   }
-  // group maxima (a group is gr consecutive runs, held by gr consecutive lanes)
-  float gmax[kQMaxRunsPerLane];
+  // row maxima over the workgroup
 #pragma unroll
-  for (int i = 0; i < kQMaxRunsPerLane; ++i) {
-    float m = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(R[i][e]));
-    for (int off = 1; off < gr; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-    gmax[i] = m;
+  for (int rr = 0; rr < RB; ++rr) {
+    const float m = wave_max_f(rmax[rr]);
+    if (lane == 0) sMax[wave][rr] = m;
   }
-  rmax = wave_max_f(rmax);
-  const _Float16 sR = (_Float16)(rmax / (7.0f * 255.0f));
-  const float sR32 = (float)sR;
-  const float den = 7.0f * sR32;  // exact
-  if (lane == 0) q.r_rowscale[v] = __builtin_bit_cast(uint16_t, sR);
-  const int64_t b = v / 16;
-  const int i16 = (int)(v % 16);
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kQMaxRunsPerLane; ++i) {
-    const int run = lane + 64 * i;
-    if (run < nruns) {
-      const int k0 = 8 * run;
-      const float c8 = sR32 > 0.0f ? fminf(fmaxf(ceilf(gmax[i] / den), 1.0f), 255.0f) : 0.0f;
-      if (run % gr == 0) q.r_gcodes[v * ng + k0 / g] = (uint8_t)c8;
-      const float scale = c8 * sR32;  // exact
-      uint32_t word = 0u;
-      float deq[8];
+  for (int rr = 0; rr < RB; ++rr) {
+    float m = sMax[0][rr];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float c = scale > 0.0f ? fminf(fmaxf(rintf(R[i][e] / scale), -8.0f), 7.0f) : 0.0f;
-        deq[e] = c * scale;  // exact
-        word |= ((uint32_t)(int)c & 0xFu) << (4 * e);
-      }
-      // tile (b, kt) of the packed residual; lane row i16 + 16 (k mod 32) / 8,
-      // dword (k mod 128) / 32 holds these 8 codes, low nibble first
-      const int kt = k0 / 128, kk = k0 % 128;
-      const int64_t off = ((int64_t)kt * q.nb + b) * 1024 + 16 * (i16 + 16 * ((kk % 32) / 8)) + 4 * (kk / 32);
-      *reinterpret_cast<uint32_t*>(q.r_codes + off) = word;
-      if (q.E) {
-        float* er = q.E + v * q.E_stride + k0;
-        *reinterpret_cast<f4*>(er) = f4{R[i][0] - deq[0], R[i][1] - deq[1], R[i][2] - deq[2], R[i][3] - deq[3]};
-        *reinterpret_cast<f4*>(er + 4) = f4{R[i][4] - deq[4], R[i][5] - deq[5], R[i][6] - deq[6], R[i][7] - deq[7]};
+    for (int w = 1; w < kQWaves; ++w) m = fmaxf(m, sMax[w][rr]);
+    rmax[rr] = m;
+  }
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    const int64_t v = v0 + rr;
+    const _Float16 sR = (_Float16)(rmax[rr] / (7.0f * 255.0f));
+    const float sR32 = (float)sR;
+    const float den = 7.0f * sR32;  // exact
+    if (tid == 0 && v < q.V) q.r_rowscale[v] = __builtin_bit_cast(uint16_t, sR);
+    const int64_t b = v / 16;
+    const int i16 = (int)(v % 16);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int run = tid + kQThreads * i;
+      // group maximum: a group is gr consecutive runs, held by gr consecutive lanes
+      float gm = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gm = fmaxf(gm, fabsf(R[rr][i][e]));
+      for (int off = 1; off < gr; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+      if (run < nruns && v < q.V) {
+        const int k0 = 8 * run;
+        const float c8 = sR32 > 0.0f ? fminf(fmaxf(ceilf(gm / den), 1.0f), 255.0f) : 0.0f;
+        if (run % gr == 0) q.r_gcodes[v * ng + k0 / g] = (uint8_t)c8;
+        const float scale = c8 * sR32;  // exact
+        uint32_t word = 0u;
+        float deq[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = scale > 0.0f ? fminf(fmaxf(rintf(R[rr][i][e] / scale), -8.0f), 7.0f) : 0.0f;
+          deq[e] = c * scale;  // exact
+          word |= ((uint32_t)(int)c & 0xFu) << (4 * e);
+        }
+        // tile (b, kt) of the packed residual; lane row i16 + 16 (k mod 32) / 8,
+        // dword (k mod 128) / 32 holds these 8 codes, low nibble first
+        const int kt = k0 / 128, kk = k0 % 128;
+        const int64_t off = ((int64_t)kt * q.nb + b) * 1024 + 16 * (i16 + 16 * ((kk % 32) / 8)) + 4 * (kk / 32);
+        *reinterpret_cast<uint32_t*>(q.r_codes + off) = word;
+        if (q.E) {
+          float* er = q.E + v * q.E_stride + k0;
+          const float(&x)[8] = R[rr][i];
+          *reinterpret_cast<f4*>(er) = f4{x[0] - deq[0], x[1] - deq[1], x[2] - deq[2], x[3] - deq[3]};
+          *reinterpret_cast<f4*>(er + 4) = f4{x[4] - deq[4], x[5] - deq[5], x[6] - deq[6], x[7] - deq[7]};
+        }
       }
     }
   }
@@ -213,8 +274,20 @@ hipError_t launch_quantize(const QuantArgs& q, const float* A_c, const float* B_
     if ((e = quant_i8(B_c, q.D, ng, q.g, (int64_t)q.r_c * ng, q.b_codes, q.D, q.b_scales, ng, s)) != hipSuccess)
       return e;
   }
-  hipLaunchKernelGGL(core_sc4_kernel, dim3((unsigned)((q.V + kQWaves - 1) / kQWaves)), dim3(kQThreads), 0, s, q);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    // rows per workgroup x runs per thread: at most 16 register runs of 8 fp32
+    const int nr = (int)((q.D / 8 + kQThreads - 1) / kQThreads);  // runs per thread
+    const int rb = nr <= 2 ? 8 : 4;
+    const dim3 grid((unsigned)((q.V + rb - 1) / rb));
+    const size_t lds = (size_t)q.r_c * rb * sizeof(double);
+    if (nr <= 1)
+      hipLaunchKernelGGL((core_sc4_kernel<8, 1>), grid, dim3(kQThreads), lds, s, q);
+    else if (nr <= 2)
+      hipLaunchKernelGGL((core_sc4_kernel<8, 2>), grid, dim3(kQThreads), lds, s, q);
+    else
+      hipLaunchKernelGGL((core_sc4_kernel<4, kQMaxRunsPerThread>), grid, dim3(kQThreads), lds, s, q);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (r_r > 0) {
     if ((e = quant_i8(A_w, r_r, 1, r_r, q.V, q.a_codes + q.r_c, q.r, q.a_scales + (q.nA - 1), q.nA, s)) !=
         hipSuccess)
@@ -239,7 +312,7 @@ int archead_quantize(const archead_dims* d, const archead_dense_head* src, void*
   int rc = archead_pack_layout(d, &L);
   if (rc) return rc;
   if (d->g != 32 && d->g != 64 && d->g != 128 && d->g != 256) return ARCHEAD_E_UNSUPPORTED;
-  if (d->D > kQuantMaxD || d->r_c > (1 << 16) || d->r_r > (1 << 16)) return ARCHEAD_E_UNSUPPORTED;
+  if (d->D > kQuantMaxD || d->r_c > kQuantMaxCoreRank || d->r_r > (1 << 16)) return ARCHEAD_E_UNSUPPORTED;
   if ((d->r_c > 0 && (!src->A_c || !src->B_c)) || (d->r_r > 0 && (!src->A_w || !src->B_w))) return ARCHEAD_E_NULL;
   if (src->W_dtype != ARCHEAD_BF16 && src->W_dtype != ARCHEAD_F32) return ARCHEAD_E_DTYPE;
   if (src->W_stride < d->D) return ARCHEAD_E_SHAPE;

@@ -192,8 +192,8 @@ typedef struct {
  *   aligned; receives fp32(R) - SC4(R), the error left after the residual
  *   codes (what the correction A_w B_w is meant to absorb).
  * Enqueued on `stream` without synchronising; allocates nothing.
- * E_NULL, E_DIMS, E_UNSUPPORTED (g not in {32, 64, 128, 256}, D > 8192, a
- * rank above 65536), E_DTYPE, E_SHAPE, E_ALIGN, E_SIZE, E_HIP. */
+ * E_NULL, E_DIMS, E_UNSUPPORTED (g not in {32, 64, 128, 256}, D > 8192,
+ * r_c > 1024, r_r > 65536), E_DTYPE, E_SHAPE, E_ALIGN, E_SIZE, E_HIP. */
 ARCHEAD_API int archead_quantize(const archead_dims* d, const archead_dense_head* src, void* packed,
                                  uint64_t packed_bytes, archead_tensor* E, void* stream);
 

@@ -236,6 +236,7 @@ def test_quantize_error_paths(ah):
     assert call(dims=(V, 500, r_c, r_r, g)) == 2                                 # D not a multiple of 128
     assert call(dims=(V, D, r_c, r_r, 16)) == 3                                  # group size
     assert call(dims=(V, 8192 + 128, r_c, r_r, g)) == 3                          # D above the register limit
+    assert call(dims=(V, D, 1032, r_r, g)) == 3                                  # core rank above the LDS limit
     assert call(wdt=3) == 4
     assert call(ws=D - 1) == 5
     assert call(W=FAKE + 8) == 6                                                  # W not 16-byte aligned
