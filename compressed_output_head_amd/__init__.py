@@ -24,7 +24,8 @@ STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5
           6: "E_ALIGN", 7: "E_WORKSPACE", 8: "E_HIP", 9: "E_VALUE", 10: "E_SIZE"}
 EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_pack", "archead_logits",
            "archead_logits_path", "archead_logits_events", "archead_stats_workspace_bytes",
-           "archead_logits_stats", "archead_quantize", "archead_status_string", "archead_format_version")
+           "archead_logits_stats", "archead_quantize", "archead_topk_workspace_bytes", "archead_logits_topk",
+           "archead_status_string", "archead_format_version")
 
 
 class ArcheadError(RuntimeError):
@@ -104,6 +105,9 @@ def _load():
                                          ctypes.c_void_p]
     lib.archead_quantize.argtypes = [P(ArcheadDims), P(ArcheadDenseHead), ctypes.c_void_p, ctypes.c_uint64,
                                      P(ArcheadTensor), ctypes.c_void_p]
+    lib.archead_topk_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int64, P(ctypes.c_uint64)]
+    lib.archead_logits_topk.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.archead_status_string.argtypes = [ctypes.c_int]
     lib.archead_status_string.restype = ctypes.c_char_p
     lib.archead_format_version.argtypes = []
@@ -158,6 +162,13 @@ def archead_stats_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
     _check(lib.archead_stats_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
                                              ctypes.byref(b)), "archead_stats_workspace_bytes")
     return b.value
+
+
+def archead_topk_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
+    out = ctypes.c_uint64(0)
+    _check(lib.archead_topk_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
+                                            ctypes.byref(out)), "archead_topk_workspace_bytes")
+    return out.value
 
 
 def _ptr(a: Optional[np.ndarray], dtype):
@@ -215,9 +226,10 @@ class PackedHead:
     def dims(self):
         return dict(V=self.V, D=self.D, r_c=self.r_c, r_r=self.r_r, g=self.g)
 
-    def ensure_workspace(self, n_tokens: int, stats: bool = False):
+    def ensure_workspace(self, n_tokens: int, stats: bool = False, topk: bool = False):
         torch = _torch()
-        size = archead_stats_workspace_bytes if stats else archead_workspace_bytes
+        size = archead_topk_workspace_bytes if topk else archead_stats_workspace_bytes if stats \
+            else archead_workspace_bytes
         need = size(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens)
         if self.workspace is None or self.workspace.numel() < need:
             self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.buffer.device)
@@ -334,3 +346,22 @@ def archead_quantize(W, A_c, B_c, A_w, B_w, g: int, with_error: bool = False, st
                                 ctypes.byref(e) if e is not None else None, ctypes.c_void_p(stream)),
            "archead_quantize")
     return PackedHead(V, D, r_c, r_r, g, buf), E
+
+
+def archead_logits_topk(H, head: PackedHead, k: int, stream=None):
+    """The k largest logits of each row of Y = H W_hat^T and their indices:
+    returns (values fp32 [N, k], indices int32 [N, k]) as device tensors,
+    largest first, lower index first among equal values."""
+    torch = _torch()
+    N = H.shape[0]
+    head.ensure_workspace(N, topk=True)
+    if stream is None:
+        stream = torch.cuda.current_stream(H.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    vals = torch.empty((N, k), dtype=torch.float32, device=H.device)
+    idx = torch.empty((N, k), dtype=torch.int32, device=H.device)
+    h, p = _tensor(H), head.struct()
+    _check(lib.archead_logits_topk(ctypes.byref(h), ctypes.byref(p), int(k), ctypes.c_void_p(vals.data_ptr()),
+                                   ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(stream)), "archead_logits_topk")
+    return vals, idx

@@ -258,6 +258,25 @@ ARCHEAD_API int archead_stats_workspace_bytes(const archead_dims* d, int64_t n_t
 ARCHEAD_API int archead_logits_stats(const archead_tensor* H, const archead_packed_head* head,
                                      const archead_row_stats* out, void* stream);
 
+/* Device workspace one archead_logits_topk call with n_tokens rows needs:
+ * archead_workspace_bytes for min(n_tokens, 256) rows, rounded up to 256,
+ * plus min(n_tokens, 256) x V fp32 logits rounded up to 256 (0 when
+ * n_tokens = 0).  Pure host arithmetic.  E_NULL, E_DIMS, E_SHAPE. */
+ARCHEAD_API int archead_topk_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes);
+
+/* The k largest logits of each row of Y = H W_hat^T and their vocabulary
+ * indices, what top-k agreement is measured on (ARCHead, results discussion
+ * of Table 8: top-1/5/10).  Row n gets top_val[n*k + i] (fp32) and
+ * top_idx[n*k + i] (int32) for i < k, largest value first; among equal values
+ * the lower index comes first, so the result is unique.  Device arrays of
+ * N*k elements, 4-byte aligned.  The forward runs on `stream` in chunks of
+ * 256 tokens into fp32 logits held in the workspace (the logits are read back
+ * once, not returned).  1 <= k <= 16 (E_SHAPE below 1 or above V,
+ * E_UNSUPPORTED above 16); H and head as for archead_logits, the workspace
+ * at least archead_topk_workspace_bytes.  N = 0 is a no-op. */
+ARCHEAD_API int archead_logits_topk(const archead_tensor* H, const archead_packed_head* head, int32_t k,
+                                    float* top_val, int32_t* top_idx, void* stream);
+
 /* Static string naming a status code. */
 ARCHEAD_API const char* archead_status_string(int status);
 

@@ -340,6 +340,20 @@ def row_stats(Y, targets=None):
     return out
 
 
+def row_topk(Y, k):
+    """The k largest entries of each row of Y with their column indices, what
+    top-k agreement compares (ARCHead, results discussion of Table 8:
+    top-1/5/10).  Order: larger value first, lower index first among equal
+    values (a unique answer).  Returns (values [N, k], indices [N, k] int64)."""
+    Y = np.asarray(Y)
+    N, V = Y.shape
+    idx = np.empty((N, k), np.int64)
+    for n in range(N):
+        order = np.lexsort((np.arange(V), -Y[n]))   # primary key -Y, then the index
+        idx[n] = order[:k]
+    return np.take_along_axis(Y, idx, axis=1), idx
+
+
 # ------------------------------------------------------------- quantizers ---
 #
 # The packing step of Algorithm 1 (ARCHead, Algorithm 1 and the Sec. 3

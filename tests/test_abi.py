@@ -251,6 +251,37 @@ def test_quantize_error_paths(ah):
     assert call(E=E(row_stride=D + 2)) == 6
 
 
+def test_topk_workspace_bytes(ah):
+    up = lambda x: (x + 255) // 256 * 256
+    for (V, D, r_c, r_r, g) in [(1024, 256, 16, 8, 64), (151936, 4096, 64, 64, 128)]:
+        for N in (1, 16, 17, 256, 257, 4096):
+            rows = min(N, 256)
+            want = up(ah.archead_workspace_bytes(V, D, r_c, r_r, g, rows)) + up(rows * V * 4)
+            assert ah.archead_topk_workspace_bytes(V, D, r_c, r_r, g, N) == want
+    assert ah.archead_topk_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
+
+
+def test_topk_error_paths(ah):
+    def call(H, P, k, val=FAKE + (4 << 30), idx=FAKE + (5 << 30)):
+        return ah.lib.archead_logits_topk(ctypes.byref(H), ctypes.byref(P), k, val, idx, None)
+
+    def args(**kw):
+        H, P, Y, need, total = _args(ah, **kw)
+        P.workspace_bytes = ah.archead_topk_workspace_bytes(1024, 256, 16, 8, 64, H.rows) if H.rows >= 0 else 0
+        return H, P
+
+    H, P = args()
+    assert ah.lib.archead_logits_topk(None, ctypes.byref(P), 5, FAKE, FAKE, None) == 1
+    assert call(H, P, 0) == 5
+    assert call(H, P, 17) == 3
+    assert call(H, P, 5, val=None) == 1
+    assert call(H, P, 5, idx=FAKE + 2) == 6
+    H, P = args(); P.workspace_bytes -= 1; assert call(H, P, 5) == 7
+    H, P = args(); P.workspace_bytes = ah.archead_workspace_bytes(1024, 256, 16, 8, 64, 4); assert call(H, P, 5) == 7
+    H, P = args(V=8); assert call(H, P, 9) == 5                                  # k above V
+    H, P = args(N=0); H.data = None; P.workspace = None; assert call(H, P, 5, None, None) == 0
+
+
 def test_logits_zero_tokens_is_a_noop(ah):
     H, P, Y, need, total = _args(ah, N=0)
     H.data = Y.data = None

@@ -515,6 +515,29 @@ def test_row_stats_invariants():
     assert oracle.row_stats(T)["argmax"].tolist() == [1, 0]
 
 
+def test_row_topk_worked_cases_and_brute_force():
+    """Hand-worked rows (ties to the lower index, negative values), top-1 =
+    argmax, distinct values against a descending sort, and brute force on
+    tiny rows: no excluded entry ranks before an included one."""
+    T = np.array([[1.0, 3.0, 3.0, -1.0, 2.0], [0.0, 0.0, 0.0, 0.0, 0.0], [-5.0, -1.0, -3.0, -1.0, -2.0]])
+    v, i = oracle.row_topk(T, 3)
+    assert i.tolist() == [[1, 2, 4], [0, 1, 2], [1, 3, 4]]
+    assert v.tolist() == [[3.0, 3.0, 2.0], [0.0, 0.0, 0.0], [-1.0, -1.0, -2.0]]
+    rng = np.random.default_rng(9)
+    Y = rng.normal(size=(7, 50))
+    assert np.array_equal(oracle.row_topk(Y, 1)[1][:, 0], oracle.row_stats(Y)["argmax"])
+    v, i = oracle.row_topk(Y, 10)
+    assert np.array_equal(v, -np.sort(-Y, axis=1)[:, :10])
+    Yq = rng.integers(-2, 3, size=(20, 9)).astype(np.float64)   # many ties
+    for k in (1, 4, 9):
+        v, i = oracle.row_topk(Yq, k)
+        for n in range(Yq.shape[0]):
+            before = lambda a, b: Yq[n, a] > Yq[n, b] or (Yq[n, a] == Yq[n, b] and a < b)
+            assert len(set(i[n])) == k
+            assert all(before(i[n][j], i[n][j + 1]) for j in range(k - 1))
+            assert all(before(i[n][-1], x) for x in range(9) if x not in set(i[n]))
+
+
 # -------------------------------------------------------------- quantizers ---
 
 
