@@ -238,6 +238,35 @@ def run_stats(name, steps, warmup):
 FP64_PEAK_TFLOPS = 78.6  # MI355X vector fp64
 
 
+def run_topk(name, steps, warmup, k=10):
+    """archead_logits_topk (top-k logits and indices per row; the forward
+    writes fp32 logits of 256-token chunks into the workspace and the
+    selection kernel reads them back) on one workload, K timed calls."""
+    import torch
+    import synth
+    import compressed_output_head_amd as ah
+
+    cfg = synth.config(name)
+    inp = synth.make(name)
+    head = ah.PackedHead.from_components(inp.head)
+    H = torch.from_numpy(inp.H_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    del inp
+    for _ in range(warmup):
+        ah.archead_logits_topk(H, head, k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        ah.archead_logits_topk(H, head, k)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    return {"workload": name, "k": k, "ms_per_call": round(ms, 4), "steps": steps,
+            "what": "k largest logits and their indices per row; fp32 logits of 256-token chunks pass "
+                    "through the workspace once"}
+
+
 def run_quantize(name, steps, warmup):
     """archead_quantize (the packing step) on one workload's head shape: dense
     bf16 W and fp32 factors resident in HBM, K timed calls of the whole step
@@ -401,6 +430,7 @@ def main():
                     help="workload timed through archead_logits_stats ('' to skip)")
     ap.add_argument("--quantize", default="decode",
                     help="head shape timed through archead_quantize, the packing step ('' to skip)")
+    ap.add_argument("--topk", default="batched", help="workload timed through archead_logits_topk, k=10 ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -468,6 +498,10 @@ def main():
         st = run_stats(args.stats, max(5, args.steps // 5), max(2, args.warmup // 5))
         log(f"[bench] stats on {args.stats}: {st['ms_per_call']:.3f} ms/call")
         out["stats"] = st
+    if args.topk:
+        tk = run_topk(args.topk, max(5, args.steps // 5), 2)
+        log(f"[bench] top-k on {args.topk}: {tk['ms_per_call']:.3f} ms/call")
+        out["topk"] = tk
     if args.quantize:
         q = run_quantize(args.quantize, max(3, args.steps // 10), 2)
         log(f"[bench] quantize on {args.quantize}: {q['ms_per_call']:.3f} ms/call")

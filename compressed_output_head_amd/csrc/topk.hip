@@ -1,9 +1,11 @@
 // The k largest logits of every row of Y = H W_hat^T with their vocabulary
 // indices: the quantity behind the pages' top-k agreement figures (ARCHead,
 // results discussion of Table 8: top-1/5/10).  The forward runs in chunks of
-// tokens into fp32 logits held in the caller's workspace; one workgroup per
-// row then selects the k largest.  Order: larger value first, and among equal
-// values the lower index first, so the result is unique.
+// tokens into fp32 logits held in the caller's workspace; the selection then
+// takes the k best of each vocabulary piece of a row (many workgroups per
+// row) and the k best of those candidates (one workgroup per row).  Order:
+// larger value first, and among equal values the lower index first, so the
+// result is unique.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,6 +17,11 @@ constexpr int kTkThreads = 256;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkMax = 16;             // largest k
 constexpr int64_t kTkChunkRows = 256;  // tokens per forward chunk
+constexpr int kTkBatch = 8;            // elements a thread loads before inserting
+constexpr int64_t kTkPieceWGs = 2048;  // first-stage workgroups per chunk (about)
+constexpr int64_t kTkMinPiece = 2048;  // smallest vocabulary piece
+// candidates of the first stage: at most kTkPieceWGs pieces of kTkMax
+constexpr uint64_t kTkCandBytes = (uint64_t)kTkPieceWGs * kTkMax * 8;
 
 constexpr uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
 
@@ -23,53 +30,43 @@ __device__ __forceinline__ bool tk_before(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
-// One workgroup per row of Y [rows][V] (row stride V).  Each thread keeps the
-// K best of the elements it reads (indices tid, tid + 256, ... in increasing
-// order, so a later equal value never displaces an earlier one) as a sorted
-// register list; then k rounds pick the best head among the 256 lists.
+// Insert (x, xi) into a thread's sorted list of the K best so far.
 template <int K>
-__global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(const float* Y, int64_t V, int k, float* out_val,
-                                                               int32_t* out_idx, int64_t out_ld) {
+__device__ __forceinline__ void tk_insert(float (&val)[K], int (&idx)[K], float x, int xi) {
+  if (!tk_before(x, xi, val[K - 1], idx[K - 1])) return;
+  val[K - 1] = x;
+  idx[K - 1] = xi;
+#pragma unroll
+  for (int i = K - 1; i > 0; --i) {
+    if (tk_before(val[i], idx[i], val[i - 1], idx[i - 1])) {
+      const float tv = val[i];
+      val[i] = val[i - 1];
+      val[i - 1] = tv;
+      const int ti = idx[i];
+      idx[i] = idx[i - 1];
+      idx[i - 1] = ti;
+    }
+  }
+}
+
+// k rounds over the workgroup's 256 sorted lists: each round the best head
+// wins, is written to ov[r], oi[r] and is popped by its owner (an index sits
+// in one list only).
+template <int K>
+__device__ __forceinline__ void tk_select(float (&val)[K], int (&idx)[K], int k, float* ov, int32_t* oi) {
   __shared__ float sv[kTkWaves];
   __shared__ int si[kTkWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const float* y = Y + row * V;
-  float val[K];
-  int idx[K];
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    val[i] = -INFINITY;
-    idx[i] = INT32_MAX;
-  }
-  for (int64_t v = tid; v < V; v += kTkThreads) {
-    const float x = y[v];
-    if (x > val[K - 1] || (idx[K - 1] == INT32_MAX && x == -INFINITY)) {
-      val[K - 1] = x;
-      idx[K - 1] = (int)v;
-#pragma unroll
-      for (int i = K - 1; i > 0; --i) {
-        if (tk_before(val[i], idx[i], val[i - 1], idx[i - 1])) {
-          const float tv = val[i];
-          val[i] = val[i - 1];
-          val[i - 1] = tv;
-          const int ti = idx[i];
-          idx[i] = idx[i - 1];
-          idx[i - 1] = ti;
-        }
-      }
-    }
-  }
   for (int r = 0; r < k; ++r) {
     float bv = val[0];
     int bi = idx[0];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (tk_before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
+      const float xv = __shfl_xor(bv, off);
+      const int xi = __shfl_xor(bi, off);
+      if (tk_before(xv, xi, bv, bi)) {
+        bv = xv;
+        bi = xi;
       }
     }
     if (lane == 0) {
@@ -87,10 +84,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(const float* Y, i
       }
     __syncthreads();  // sv/si are rewritten in the next round
     if (tid == 0) {
-      out_val[row * out_ld + r] = bv;
-      out_idx[row * out_ld + r] = bi;
+      ov[r] = bv;
+      oi[r] = bi;
     }
-    if (idx[0] == bi) {  // the owner of the winning element pops it (indices are unique)
+    if (idx[0] == bi) {
 #pragma unroll
       for (int i = 0; i < K - 1; ++i) {
         val[i] = val[i + 1];
@@ -102,16 +99,83 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(const float* Y, i
   }
 }
 
-hipError_t launch_topk(const float* Y, int64_t rows, int64_t V, int k, float* out_val, int32_t* out_idx,
-                       int64_t out_ld, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  if (k <= 4)
-    hipLaunchKernelGGL((topk_rows_kernel<4>), dim3((unsigned)rows), dim3(kTkThreads), 0, s, Y, V, k, out_val,
-                       out_idx, out_ld);
-  else
-    hipLaunchKernelGGL((topk_rows_kernel<kTkMax>), dim3((unsigned)rows), dim3(kTkThreads), 0, s, Y, V, k, out_val,
-                       out_idx, out_ld);
+template <int K>
+__device__ __forceinline__ void tk_clear(float (&val)[K], int (&idx)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    val[i] = -INFINITY;
+    idx[i] = INT32_MAX;
+  }
+}
+
+// Stage 1: workgroup (p, row) takes the vocabulary piece [p L, (p + 1) L) of
+// one row of Y [rows][V] and writes its k best to cand[(row P + p) k + r].
+// Each thread loads kTkBatch elements (256 apart) before inserting them.
+template <int K>
+__global__ __launch_bounds__(kTkThreads) void topk_piece_kernel(const float* Y, int64_t V, int64_t L, int k,
+                                                                float* cv, int32_t* ci) {
+  const int P = gridDim.x, p = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const float* y = Y + row * V;
+  const int64_t lo = (int64_t)p * L, hi = lo + L < V ? lo + L : V;
+  float val[K];
+  int idx[K];
+  tk_clear(val, idx);
+  for (int64_t base = lo + threadIdx.x; base < hi; base += (int64_t)kTkThreads * kTkBatch) {
+    float x[kTkBatch];
+#pragma unroll
+    for (int u = 0; u < kTkBatch; ++u) {
+      const int64_t v = base + (int64_t)kTkThreads * u;
+      x[u] = v < hi ? y[v] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kTkBatch; ++u) {
+      const int64_t v = base + (int64_t)kTkThreads * u;
+      if (v < hi) tk_insert(val, idx, x[u], (int)v);
+    }
+  }
+  const int64_t o = (row * P + p) * k;
+  tk_select(val, idx, k, cv + o, ci + o);
+}
+
+// Stage 2: one workgroup per row merges the row's n = P k candidates.
+template <int K>
+__global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const float* cv, const int32_t* ci, int n, int k,
+                                                                float* out_val, int32_t* out_idx, int64_t out_ld) {
+  const int64_t row = blockIdx.x;
+  float val[K];
+  int idx[K];
+  tk_clear(val, idx);
+  for (int c = threadIdx.x; c < n; c += kTkThreads) tk_insert(val, idx, cv[row * n + c], ci[row * n + c]);
+  tk_select(val, idx, k, out_val + row * out_ld, out_idx + row * out_ld);
+}
+
+// pieces per row: about kTkPieceWGs workgroups in all, each piece at least
+// kTkMinPiece elements
+int tk_pieces(int64_t rows, int64_t V) {
+  int64_t P = kTkPieceWGs / (rows > 0 ? rows : 1);
+  const int64_t pmax = (V + kTkMinPiece - 1) / kTkMinPiece;
+  if (P > pmax) P = pmax;
+  return P < 1 ? 1 : (int)P;
+}
+
+template <int K>
+hipError_t launch_topk_k(const float* Y, int64_t rows, int64_t V, int k, float* cv, int32_t* ci, float* out_val,
+                         int32_t* out_idx, int64_t out_ld, hipStream_t s) {
+  const int P = tk_pieces(rows, V);
+  const int64_t L = (V + P - 1) / P;
+  hipLaunchKernelGGL((topk_piece_kernel<K>), dim3((unsigned)P, (unsigned)rows), dim3(kTkThreads), 0, s, Y, V, L, k,
+                     cv, ci);
+  hipLaunchKernelGGL((topk_merge_kernel<K>), dim3((unsigned)rows), dim3(kTkThreads), 0, s, cv, ci, P * k, k,
+                     out_val, out_idx, out_ld);
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* Y, int64_t rows, int64_t V, int k, float* cv, int32_t* ci, float* out_val,
+                       int32_t* out_idx, int64_t out_ld, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  return k <= 4 ? launch_topk_k<4>(Y, rows, V, k, cv, ci, out_val, out_idx, out_ld, s)
+                : launch_topk_k<kTkMax>(Y, rows, V, k, cv, ci, out_val, out_idx, out_ld, s);
 }
 
 int topk_layout(const archead_dims* d, int64_t n_tokens, uint64_t* fwd_bytes, uint64_t* total) {
@@ -119,7 +183,7 @@ int topk_layout(const archead_dims* d, int64_t n_tokens, uint64_t* fwd_bytes, ui
   int rc = archead_workspace_bytes(d, rows, fwd_bytes);
   if (rc) return rc;
   *fwd_bytes = up256(*fwd_bytes);
-  *total = rows > 0 ? *fwd_bytes + up256((uint64_t)rows * (uint64_t)d->V * 4) : 0;
+  *total = rows > 0 ? *fwd_bytes + up256((uint64_t)rows * (uint64_t)d->V * 4) + kTkCandBytes : 0;
   return ARCHEAD_OK;
 }
 
@@ -152,6 +216,9 @@ int archead_logits_topk(const archead_tensor* H, const archead_packed_head* head
   if (head->workspace_bytes < need) return ARCHEAD_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* Yc = reinterpret_cast<float*>(static_cast<uint8_t*>(head->workspace) + fwd);
+  const uint64_t ybytes = up256((uint64_t)(N < kTkChunkRows ? N : kTkChunkRows) * (uint64_t)d->V * 4);
+  float* cv = reinterpret_cast<float*>(static_cast<uint8_t*>(head->workspace) + fwd + ybytes);
+  int32_t* ci = reinterpret_cast<int32_t*>(cv + kTkCandBytes / 8);
   for (int64_t t0 = 0; t0 < N; t0 += kTkChunkRows) {
     const int64_t rows = N - t0 < kTkChunkRows ? N - t0 : kTkChunkRows;
     archead_tensor Hc = *H;
@@ -162,7 +229,7 @@ int archead_logits_topk(const archead_tensor* H, const archead_packed_head* head
     archead_tensor Yt{Yc, rows, d->V, d->V, ARCHEAD_F32};
     rc = archead_logits(&Hc, &P, &Yt, stream);
     if (rc) return rc;
-    if (launch_topk(Yc, rows, d->V, k, top_val + t0 * k, top_idx + t0 * k, k, s) != hipSuccess)
+    if (launch_topk(Yc, rows, d->V, k, cv, ci, top_val + t0 * k, top_idx + t0 * k, k, s) != hipSuccess)
       return ARCHEAD_E_HIP;
   }
   return ARCHEAD_OK;
