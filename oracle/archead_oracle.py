@@ -450,3 +450,79 @@ def quantize(W, A_c, B_c, A_w, B_w, g):
     head = SimpleNamespace(V=V, D=D, r_c=r_c, r_r=r_r, g=g, q4=q4, c8=c8, s_R=s_R,
                            A_c=qa, s_Ac=sa, B_c=qb, s_Bc=sb, A_w=qaw, s_Aw=saw, B_w=qbw, s_Bw=sbw)
     return head, E
+
+
+# ---------------------------------------------------------------- fitting ---
+#
+# The construction of Algorithm 1 (ARCHead, Sec. 3 and Algorithm 1): the core
+# is a rank-r_c approximation of W (quantised, then the residual goes to SC4);
+# the correction is fitted to the core error E = W - W_d in a damped
+# activation metric.  Readings:
+#   - damping as the Sec. 3 metric definition states it: C_lam = C + lam c_bar I
+#     with C = H^T H / N and c_bar the mean diagonal of C (Algorithm 1's prose
+#     writes C + lam I; the mean-diagonal scaling makes lam scale-free);
+#   - T_p = Q Lam^p Q^T from the eigendecomposition C_lam = Q Lam Q^T, and
+#     T_p^{-1} = Q Lam^{-p} Q^T;
+#   - both low-rank approximations are randomized truncated SVDs (the Sec. 3
+#     sentence names one for the correction; the core uses the same routine):
+#     Y = M Omega, q rounds of re-orthonormalised power iteration, Q = qr(Y),
+#     B = Q^T M, B = U S V^T, and the factors are A = Q U_r S_r, B = V_r^T
+#     (the singular values go to the left factor);
+#   - the correction's right factor is mapped back: A_w = left factor of
+#     [E T_p]_r, B_w = (its right factor) T_p^{-1}.
+# The Gaussian test matrices Omega are inputs, so the GPU path can use the
+# same ones.
+
+def damped_covariance(H, lam):
+    """C_lam = H^T H / N + lam * mean(diag(H^T H / N)) * I  (fp64)."""
+    H = np.asarray(H, np.float64)
+    C = H.T @ H / H.shape[0]
+    return C + lam * np.mean(np.diag(C)) * np.eye(C.shape[0])
+
+
+def metric_transform(C_lam, p):
+    """(T_p, T_p^{-1}) from the eigendecomposition of the damped covariance."""
+    lam, Q = np.linalg.eigh(np.asarray(C_lam, np.float64))
+    return (Q * lam ** p) @ Q.T, (Q * lam ** (-p)) @ Q.T
+
+
+def rsvd(M, r, omega, q):
+    """Randomized rank-r truncated SVD of M with test matrix omega [D, k >= r]
+    and q power iterations: returns (A [V, r], B [r, D]) with A B ~ M."""
+    M = np.asarray(M, np.float64)
+    Y = M @ np.asarray(omega, np.float64)
+    for _ in range(q):
+        Qy = np.linalg.qr(Y)[0]
+        Qz = np.linalg.qr(M.T @ Qy)[0]
+        Y = M @ Qz
+    Q = np.linalg.qr(Y)[0]
+    U, S, Vt = np.linalg.svd(Q.T @ M, full_matrices=False)
+    return (Q @ U[:, :r]) * S[:r], Vt[:r]
+
+
+def metric_objective(Delta, T):
+    """||Delta T||_F^2: at p = 1/2 the damped logit error of Eq. 1."""
+    return float(np.sum((np.asarray(Delta, np.float64) @ T) ** 2))
+
+
+def fit(W, H_bits, r_c, r_r, g, p, lam, omega_c, omega_r, q):
+    """Algorithm 1 end to end.  W: [V, D] bf16 bits (uint16) or float32;
+    H_bits: calibration hidden states [N, D] as bf16 bits.  Returns (head, f)
+    where head is what ``pack`` reads and f holds the fp32 factors A_c, B_c,
+    A_w, B_w, the core error E and the metric transforms."""
+    W = np.asarray(W)
+    W64 = bf16_bits_to_f64(W) if W.dtype == np.uint16 else W.astype(np.float32).astype(np.float64)
+    V, D = W64.shape
+    none = (np.zeros((V, 0), np.float32), np.zeros((0, D), np.float32))
+    A_c, B_c = none
+    if r_c:
+        A_c, B_c = rsvd(W64, r_c, omega_c, q)
+        A_c, B_c = A_c.astype(np.float32), B_c.astype(np.float32)
+    _, E = quantize(W, A_c, B_c, *none, g)
+    T, Tinv = metric_transform(damped_covariance(bf16_bits_to_f64(H_bits), lam), p)
+    A_w, B_w = none
+    if r_r:
+        A_w, Bt = rsvd(E.astype(np.float64) @ T, r_r, omega_r, q)
+        A_w, B_w = A_w.astype(np.float32), (Bt @ Tinv).astype(np.float32)
+    head, _ = quantize(W, A_c, B_c, A_w, B_w, g)
+    return head, dict(A_c=A_c, B_c=B_c, A_w=A_w, B_w=B_w, E=E, T=T, Tinv=Tinv)

@@ -644,3 +644,107 @@ def test_quantize_end_to_end_reconstructs_w():
     # (rounding to 1 would clamp its largest code from 9 to 7)
     small = oracle.quant_sc4(np.array([[1.0, 0.0, 0.0051, -0.002]], np.float32), 2)
     assert small[1].tolist() == [[255, 2]] and small[0].tolist() == [[7, 0, 5, -2]]
+
+
+# ---------------------------------------------------------------- fitting ---
+
+def test_damped_covariance_worked_example():
+    """H = [[1, 2], [3, 4]]: H^T H / 2 = [[5, 7], [7, 10]], mean diagonal 7.5;
+    lam = 0.2 adds 1.5 on the diagonal.  bf16 inputs are exact here."""
+    H = np.array([[1.0, 2.0], [3.0, 4.0]])
+    C = oracle.damped_covariance(H, 0.2)
+    assert np.array_equal(C, np.array([[6.5, 7.0], [7.0, 11.5]]))
+    assert np.array_equal(oracle.damped_covariance(H, 0.0), np.array([[5.0, 7.0], [7.0, 10.0]]))
+
+
+def test_metric_transform_closed_forms():
+    """T_1 = C, T_{1/2}^2 = C, T_p T_p^{-1} = I, T_0 = I; a diagonal C gives
+    diag(c^p); a rotated diagonal matrix gives the rotated powers."""
+    rng = np.random.default_rng(4)
+    X = rng.normal(size=(40, 6))
+    C = oracle.damped_covariance(X, 0.1)
+    T1, _ = oracle.metric_transform(C, 1.0)
+    Th, _ = oracle.metric_transform(C, 0.5)
+    Tp, Tpi = oracle.metric_transform(C, 0.75)
+    T0, _ = oracle.metric_transform(C, 0.0)
+    assert np.allclose(T1, C, atol=1e-12) and np.allclose(Th @ Th, C, atol=1e-12)
+    assert np.allclose(Tp @ Tpi, np.eye(6), atol=1e-12) and np.allclose(T0, np.eye(6), atol=1e-12)
+    d = np.array([4.0, 9.0, 16.0])
+    T, Ti = oracle.metric_transform(np.diag(d), 0.5)
+    assert np.allclose(T, np.diag([2.0, 3.0, 4.0]), atol=1e-14) and np.allclose(Ti, np.diag(1 / np.array([2.0, 3.0, 4.0])))
+    c, s_ = np.cos(0.3), np.sin(0.3)
+    Rm = np.array([[c, -s_], [s_, c]])
+    T, _ = oracle.metric_transform(Rm @ np.diag([1.0, 25.0]) @ Rm.T, 0.5)
+    assert np.allclose(T, Rm @ np.diag([1.0, 5.0]) @ Rm.T, atol=1e-12)
+
+
+def test_rsvd_exact_on_low_rank_and_near_optimal():
+    """An exactly rank-5 matrix is recovered by a rank-5 randomized SVD (to
+    rounding), with the exact singular values; on a matrix with decaying
+    spectrum, power iterations bring the residual to the Eckart-Young optimum
+    (and never below it)."""
+    rng = np.random.default_rng(5)
+    M = rng.normal(size=(60, 5)) @ rng.normal(size=(5, 40))
+    A, B = oracle.rsvd(M, 5, rng.normal(size=(40, 9)), 1)
+    assert np.abs(A @ B - M).max() <= 1e-10 * np.abs(M).max()
+    s_exact = np.linalg.svd(M, compute_uv=False)[:5]
+    assert np.allclose(np.linalg.norm(A, axis=0), s_exact, rtol=1e-10)   # A = Q U S, Q U orthonormal
+    U, S, Vt = np.linalg.svd(rng.normal(size=(80, 50)), full_matrices=False)
+    M = (U * (0.7 ** np.arange(50))) @ Vt
+    opt = np.sum((0.7 ** np.arange(50))[6:] ** 2)
+    A, B = oracle.rsvd(M, 6, rng.normal(size=(50, 12)), 3)
+    res = np.sum((M - A @ B) ** 2)
+    assert opt * (1 - 1e-12) <= res <= opt * (1 + 1e-6)
+
+
+def test_metric_correction_is_the_conditional_optimum():
+    """Sec. 3.2: at p = 1/2 the metric objective is the damped logit error,
+    ||Delta T||^2 = ||H Delta^T||^2 / N + lam c_bar ||Delta||^2, and the
+    correction [E T]_r T^{-1} (exact SVD) attains its minimum over rank r,
+    sum_{i > r} sigma_i(E T)^2; random rank-r candidates and small
+    perturbations of the optimum do worse."""
+    rng = np.random.default_rng(6)
+    N, V, D, r, lam = 200, 30, 16, 3, 0.05
+    H = rng.normal(size=(N, D)) * np.where(np.arange(D) < 2, 10.0, 1.0)
+    E = rng.normal(size=(V, D))
+    C = oracle.damped_covariance(H, lam)
+    T, Ti = oracle.metric_transform(C, 0.5)
+    cbar = np.mean(np.sum(H * H, axis=0) / N)
+    Dl = rng.normal(size=(V, D))
+    lhs = oracle.metric_objective(Dl, T)
+    assert np.isclose(lhs, np.sum((H @ Dl.T) ** 2) / N + lam * cbar * np.sum(Dl ** 2), rtol=1e-12)
+    U, S, Vt = np.linalg.svd(E @ T, full_matrices=False)
+    Af, Bf = U[:, :r] * S[:r], Vt[:r] @ Ti
+    best = oracle.metric_objective(E - Af @ Bf, T)
+    assert np.isclose(best, np.sum(S[r:] ** 2), rtol=1e-12)
+    for _ in range(20):
+        Mr = rng.normal(size=(V, r)) @ rng.normal(size=(r, D))
+        assert oracle.metric_objective(E - Mr, T) > best
+        P = (Af + 1e-3 * rng.normal(size=(V, r))) @ (Bf + 1e-3 * rng.normal(size=(r, D)))   # still rank r
+        assert oracle.metric_objective(E - P, T) > best
+    # the randomized routine with power iterations reaches it closely
+    A, B = oracle.rsvd(E @ T, r, rng.normal(size=(D, r + 8)), 4)
+    assert oracle.metric_objective(E - A @ B @ Ti, T) <= best * (1 + 1e-3)
+
+
+def test_fit_end_to_end_properties():
+    """Algorithm 1 on a tiny head: the core factors span W's dominant part,
+    E is W - W_d exactly (W_d rebuilt from the packed components), and the
+    correction lowers the metric objective of E as the quantised factors
+    allow."""
+    rng = np.random.default_rng(7)
+    V, D, r_c, r_r, g, N = 96, 128, 8, 8, 32, 300
+    W = (rng.normal(size=(V, r_c)) @ rng.normal(size=(r_c, D)) * 0.05 + rng.normal(size=(V, D)) * 0.002)
+    W = W.astype(np.float32)
+    H = synth.f32_to_bf16_bits(rng.normal(size=(N, D)).astype(np.float32) * np.where(np.arange(D) < 3, 15.0, 1.0).astype(np.float32))
+    head, f = oracle.fit(W, H, r_c, r_r, g, 0.5, 0.01, rng.normal(size=(D, r_c + 8)), rng.normal(size=(D, r_r + 8)), 2)
+    core = f["A_c"].astype(np.float64) @ f["B_c"]
+    assert np.sum((W - core) ** 2) <= 1.01 * np.sum(np.linalg.svd(W.astype(np.float64), compute_uv=False)[r_c:] ** 2)
+    Wd = oracle.dequant_R(head.q4, head.c8, head.s_R, g) + \
+        oracle.dequant_rows(head.A_c, head.s_Ac) @ oracle.dequant_groups(head.B_c, head.s_Bc, g)
+    assert np.abs((W - Wd) - f["E"]).max() <= 1e-6 * np.abs(W).max()
+    T = f["T"]
+    J0 = oracle.metric_objective(f["E"], T)
+    Jf = oracle.metric_objective(f["E"] - f["A_w"].astype(np.float64) @ f["B_w"], T)
+    Jq = oracle.metric_objective(f["E"] - oracle.dequant_rows(head.A_w, head.s_Aw) @ oracle.dequant_groups(head.B_w, head.s_Bw, g), T)
+    assert Jf < 0.8 * J0 and Jq < 0.85 * J0
