@@ -25,6 +25,7 @@ STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5
 EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_pack", "archead_logits",
            "archead_logits_path", "archead_logits_events", "archead_stats_workspace_bytes",
            "archead_logits_stats", "archead_quantize", "archead_topk_workspace_bytes", "archead_logits_topk",
+           "archead_fit_workspace_bytes", "archead_fit",
            "archead_status_string", "archead_format_version")
 
 
@@ -80,6 +81,17 @@ class ArcheadDenseHead(ctypes.Structure):
                 ("B_w", ctypes.c_void_p)]
 
 
+class ArcheadFitInputs(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("W_stride", ctypes.c_int64), ("W_dtype", ctypes.c_int32),
+                ("H", ctypes.c_void_p), ("H_rows", ctypes.c_int64), ("H_stride", ctypes.c_int64),
+                ("omega_c", ctypes.c_void_p), ("omega_r", ctypes.c_void_p), ("p", ctypes.c_float),
+                ("lam", ctypes.c_float), ("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32)]
+
+
+class ArcheadFitOutputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("A_c", "B_c", "A_w", "B_w", "E")]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python compressed_output_head_amd/build.py`")
@@ -108,6 +120,9 @@ def _load():
     lib.archead_topk_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int64, P(ctypes.c_uint64)]
     lib.archead_logits_topk.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.archead_fit_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int32, P(ctypes.c_uint64)]
+    lib.archead_fit.argtypes = [P(ArcheadDims), P(ArcheadFitInputs), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                ctypes.c_uint64, P(ArcheadFitOutputs), ctypes.c_void_p]
     lib.archead_status_string.argtypes = [ctypes.c_int]
     lib.archead_status_string.restype = ctypes.c_char_p
     lib.archead_format_version.argtypes = []
@@ -365,3 +380,51 @@ def archead_logits_topk(H, head: PackedHead, k: int, stream=None):
     _check(lib.archead_logits_topk(ctypes.byref(h), ctypes.byref(p), int(k), ctypes.c_void_p(vals.data_ptr()),
                                    ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(stream)), "archead_logits_topk")
     return vals, idx
+
+
+def archead_fit_workspace_bytes(V, D, r_c, r_r, g, oversample: int) -> int:
+    out = ctypes.c_uint64(0)
+    _check(lib.archead_fit_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(oversample),
+                                           ctypes.byref(out)), "archead_fit_workspace_bytes")
+    return out.value
+
+
+def archead_fit(W, H, omega_c, omega_r, r_c: int, r_r: int, g: int, p: float = 0.75, lam: float = 0.01,
+                oversample: int = 8, power_iters: int = 2, outputs: bool = False, stream=None):
+    """Build a packed head from a dense one on the GPU (the whole construction).
+    W: bf16 or fp32 [V, D]; H: bf16 [N, D] calibration hidden states; omega_c
+    [D, r_c + oversample] and omega_r [D, r_r + oversample]: fp32 Gaussian
+    test matrices (device tensors).  Returns (PackedHead, factors) where
+    factors is a dict of fp32 device tensors A_c, B_c, A_w, B_w, E when
+    ``outputs``, else None.  The call waits for the stream."""
+    torch = _torch()
+    V, D = W.shape
+    L = archead_pack_layout(V, D, r_c, r_r, g)
+    buf = torch.empty(L["total_bytes"], dtype=torch.uint8, device=W.device)
+    ws = torch.empty(max(archead_fit_workspace_bytes(V, D, r_c, r_r, g, oversample), 256), dtype=torch.uint8,
+                     device=W.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(W.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    for name, t, shape in (("omega_c", omega_c, (D, r_c + oversample)), ("omega_r", omega_r, (D, r_r + oversample))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {shape}")
+    if H.dtype != torch.bfloat16 or H.dim() != 2 or H.shape[1] != D or H.stride(1) != 1:
+        raise ValueError("H must be a bf16 [N, D] tensor with unit column stride")
+    w = _tensor(W)
+    inp = ArcheadFitInputs(w.data, w.row_stride, w.dtype, H.data_ptr(), H.shape[0], H.stride(0),
+                           omega_c.data_ptr(), omega_r.data_ptr(), float(p), float(lam), int(oversample),
+                           int(power_iters))
+    f = None
+    if outputs:
+        f = {"A_c": torch.empty((V, r_c), dtype=torch.float32, device=W.device),
+             "B_c": torch.empty((r_c, D), dtype=torch.float32, device=W.device),
+             "A_w": torch.empty((V, r_r), dtype=torch.float32, device=W.device),
+             "B_w": torch.empty((r_r, D), dtype=torch.float32, device=W.device),
+             "E": torch.empty((V, D), dtype=torch.float32, device=W.device)}
+        outs = ArcheadFitOutputs(*(f[k].data_ptr() if f[k].numel() else None for k in ("A_c", "B_c", "A_w", "B_w", "E")))
+    _check(lib.archead_fit(ctypes.byref(_dims(V, D, r_c, r_r, g)), ctypes.byref(inp), ctypes.c_void_p(buf.data_ptr()),
+                           buf.numel(), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                           ctypes.byref(outs) if outputs else None, ctypes.c_void_p(stream)), "archead_fit")
+    return PackedHead(V, D, r_c, r_r, g, buf), f

@@ -15,7 +15,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libarchead.so")
 SOURCES = ["archead.hip", "prep.hip", "decode.hip", "mid.hip", "tile.hip", "tile_stats.hip", "stats.hip",
-           "quantize.hip", "topk.hip"]
+           "quantize.hip", "topk.hip", "fit.hip"]
+# dense products and factorisations of the construction step
+LINK_LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-lrocsolver"]
 ARCH = os.environ.get("ARCHEAD_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -58,7 +60,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda so: _run([hipcc(), *compile_flags, "-c", os.path.join(CSRC, so[0]), "-o", so[1]],
                                     verbose), zip(SOURCES, objs)))
-    _run([hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
+    _run([hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, *LINK_LIBS, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "archead.h"
+
 namespace archead {
 
 struct QuantArgs {
@@ -42,5 +44,15 @@ constexpr int kQuantMaxCoreRank = 1024;
 // B_w [r_r][D] are dense fp32 device arrays.
 hipError_t launch_quantize(const QuantArgs& q, const float* A_c, const float* B_c, const float* A_w,
                            const float* B_w, uint64_t total_bytes, hipStream_t s);
+
+// The same in two phases: the zero fill, header, core factors and SC4
+// residual (which writes E when q.E is set), then the correction factors.
+hipError_t launch_quantize_core(const QuantArgs& q, const float* A_c, const float* B_c, uint64_t total_bytes,
+                                hipStream_t s);
+hipError_t launch_quantize_corr(const QuantArgs& q, const float* A_w, const float* B_w, hipStream_t s);
+
+// Pointers of every section of a packed buffer laid out as L.
+QuantArgs quant_args(const archead_dims* d, const archead_layout& L, void* packed, const void* W, int64_t W_stride,
+                     bool w_bf16, float* E, int64_t E_stride);
 
 }  // namespace archead

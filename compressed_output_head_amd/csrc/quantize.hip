@@ -257,8 +257,8 @@ hipError_t quant_i8(const float* M, int64_t m_ld, int spr, int len, int64_t nseg
 
 }  // namespace
 
-hipError_t launch_quantize(const QuantArgs& q, const float* A_c, const float* B_c, const float* A_w,
-                           const float* B_w, uint64_t total_bytes, hipStream_t s) {
+hipError_t launch_quantize_core(const QuantArgs& q, const float* A_c, const float* B_c, uint64_t total_bytes,
+                                hipStream_t s) {
   const uint64_t n16 = total_bytes / 16;
   const unsigned zb = (unsigned)std::min<uint64_t>((n16 + kQThreads - 1) / kQThreads, 4096);
   hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(kQThreads), 0, s, reinterpret_cast<u4*>(q.buf), n16);
@@ -267,7 +267,6 @@ hipError_t launch_quantize(const QuantArgs& q, const float* A_c, const float* B_
   hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, s, q.buf, (uint64_t)q.V, (uint64_t)q.D, (uint32_t)q.r_c,
                      (uint32_t)(q.r - q.r_c), (uint32_t)q.g);
   const int ng = (int)(q.D / q.g);
-  const int r_r = q.r - q.r_c;
   if (q.r_c > 0) {
     // A_c: rows into a_codes columns [0, r_c), scales column 0; B_c: groups into rows [0, r_c)
     if ((e = quant_i8(A_c, q.r_c, 1, q.r_c, q.V, q.a_codes, q.r, q.a_scales, q.nA, s)) != hipSuccess) return e;
@@ -288,15 +287,50 @@ hipError_t launch_quantize(const QuantArgs& q, const float* A_c, const float* B_
       hipLaunchKernelGGL((core_sc4_kernel<4, kQMaxRunsPerThread>), grid, dim3(kQThreads), lds, s, q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (r_r > 0) {
-    if ((e = quant_i8(A_w, r_r, 1, r_r, q.V, q.a_codes + q.r_c, q.r, q.a_scales + (q.nA - 1), q.nA, s)) !=
-        hipSuccess)
-      return e;
-    if ((e = quant_i8(B_w, q.D, ng, q.g, (int64_t)r_r * ng, q.b_codes + (int64_t)q.r_c * q.D, q.D,
-                      q.b_scales + (int64_t)q.r_c * ng, ng, s)) != hipSuccess)
-      return e;
-  }
   return hipSuccess;
+}
+
+hipError_t launch_quantize_corr(const QuantArgs& q, const float* A_w, const float* B_w, hipStream_t s) {
+  const int ng = (int)(q.D / q.g);
+  const int r_r = q.r - q.r_c;
+  if (r_r <= 0) return hipSuccess;
+  hipError_t e = quant_i8(A_w, r_r, 1, r_r, q.V, q.a_codes + q.r_c, q.r, q.a_scales + (q.nA - 1), q.nA, s);
+  if (e != hipSuccess) return e;
+  return quant_i8(B_w, q.D, ng, q.g, (int64_t)r_r * ng, q.b_codes + (int64_t)q.r_c * q.D, q.D,
+                  q.b_scales + (int64_t)q.r_c * ng, ng, s);
+}
+
+hipError_t launch_quantize(const QuantArgs& q, const float* A_c, const float* B_c, const float* A_w,
+                           const float* B_w, uint64_t total_bytes, hipStream_t s) {
+  hipError_t e = launch_quantize_core(q, A_c, B_c, total_bytes, s);
+  return e != hipSuccess ? e : launch_quantize_corr(q, A_w, B_w, s);
+}
+
+QuantArgs quant_args(const archead_dims* d, const archead_layout& L, void* packed, const void* W, int64_t W_stride,
+                     bool w_bf16, float* E, int64_t E_stride) {
+  uint8_t* buf = static_cast<uint8_t*>(packed);
+  QuantArgs q{};
+  q.W = W;
+  q.W_stride = W_stride;
+  q.w_bf16 = w_bf16;
+  q.V = d->V;
+  q.D = d->D;
+  q.r_c = d->r_c;
+  q.r = d->r_c + d->r_r;
+  q.g = d->g;
+  q.nA = (d->r_c > 0) + (d->r_r > 0);
+  q.nb = L.padded_rows / 16;
+  q.buf = buf;
+  q.r_codes = buf + L.r_codes.offset;
+  q.r_gcodes = buf + L.r_gcodes.offset;
+  q.r_rowscale = reinterpret_cast<uint16_t*>(buf + L.r_rowscale.offset);
+  q.a_codes = reinterpret_cast<int8_t*>(buf + L.a_codes.offset);
+  q.a_scales = reinterpret_cast<uint16_t*>(buf + L.a_scales.offset);
+  q.b_codes = reinterpret_cast<int8_t*>(buf + L.b_codes.offset);
+  q.b_scales = reinterpret_cast<uint16_t*>(buf + L.b_scales.offset);
+  q.E = E;
+  q.E_stride = E_stride;
+  return q;
 }
 
 }  // namespace archead
@@ -328,28 +362,8 @@ int archead_quantize(const archead_dims* d, const archead_dense_head* src, void*
     if (E->rows != d->V || E->cols != d->D || E->row_stride < d->D) return ARCHEAD_E_SHAPE;
     if ((reinterpret_cast<uintptr_t>(E->data) | (uintptr_t)(E->row_stride * 4)) % 16) return ARCHEAD_E_ALIGN;
   }
-  uint8_t* buf = static_cast<uint8_t*>(packed);
-  QuantArgs q{};
-  q.W = src->W;
-  q.W_stride = src->W_stride;
-  q.w_bf16 = src->W_dtype == ARCHEAD_BF16;
-  q.V = d->V;
-  q.D = d->D;
-  q.r_c = d->r_c;
-  q.r = d->r_c + d->r_r;
-  q.g = d->g;
-  q.nA = (d->r_c > 0) + (d->r_r > 0);
-  q.nb = L.padded_rows / 16;
-  q.buf = buf;
-  q.r_codes = buf + L.r_codes.offset;
-  q.r_gcodes = buf + L.r_gcodes.offset;
-  q.r_rowscale = reinterpret_cast<uint16_t*>(buf + L.r_rowscale.offset);
-  q.a_codes = reinterpret_cast<int8_t*>(buf + L.a_codes.offset);
-  q.a_scales = reinterpret_cast<uint16_t*>(buf + L.a_scales.offset);
-  q.b_codes = reinterpret_cast<int8_t*>(buf + L.b_codes.offset);
-  q.b_scales = reinterpret_cast<uint16_t*>(buf + L.b_scales.offset);
-  q.E = E ? static_cast<float*>(E->data) : nullptr;
-  q.E_stride = E ? E->row_stride : 0;
+  const QuantArgs q = quant_args(d, L, packed, src->W, src->W_stride, src->W_dtype == ARCHEAD_BF16,
+                                 E ? static_cast<float*>(E->data) : nullptr, E ? E->row_stride : 0);
   const hipError_t e =
       launch_quantize(q, src->A_c, src->B_c, src->A_w, src->B_w, L.total_bytes, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ARCHEAD_OK : ARCHEAD_E_HIP;

@@ -197,6 +197,65 @@ typedef struct {
 ARCHEAD_API int archead_quantize(const archead_dims* d, const archead_dense_head* src, void* packed,
                                  uint64_t packed_bytes, archead_tensor* E, void* stream);
 
+/* Inputs of the whole construction (Algorithm 1; Sec. 3), device memory:
+ *   W        [V][D] bf16 or fp32 (W_dtype), row stride W_stride elements,
+ *            4-byte aligned: the dense head
+ *   H        [H_rows][D] bf16, row stride H_stride: calibration hidden states
+ *   omega_c  fp32 row-major [D][r_c + oversample], omega_r [D][r_r + oversample]:
+ *            the Gaussian test matrices of the two randomized SVDs (NULL for
+ *            a part of rank 0)
+ *   p, lambda   metric power and damping (lambda > 0)
+ *   oversample  extra columns of the randomized SVDs; power_iters <= 16 rounds
+ *               of power iteration. */
+typedef struct {
+  const void* W;
+  int64_t W_stride;
+  int32_t W_dtype;
+  const void* H;
+  int64_t H_rows, H_stride;
+  const float* omega_c;
+  const float* omega_r;
+  float p, lambda;
+  int32_t oversample, power_iters;
+} archead_fit_inputs;
+
+/* Optional copies of the fitted fp32 factors (row-major, contiguous) and of
+ * the core error E = W - W_d [V][D]; each pointer may be NULL. */
+typedef struct {
+  float* A_c;
+  float* B_c;
+  float* A_w;
+  float* B_w;
+  float* E;
+} archead_fit_outputs;
+
+/* Device workspace archead_fit needs (two fp32 V x D arrays, four D x D, the
+ * randomized SVDs' panels and the factors).  Pure host arithmetic.  E_NULL,
+ * E_DIMS, E_UNSUPPORTED, E_SHAPE (a rank plus oversample above V or D). */
+ARCHEAD_API int archead_fit_workspace_bytes(const archead_dims* d, int32_t oversample, uint64_t* bytes);
+
+/* Build a packed head from a dense one (Algorithm 1; Sec. 3 metric transform,
+ * quantized-core equation and packed-variant paragraph):
+ *   1. A_c B_c = rank-r_c randomized SVD of W (Y = W omega_c, power_iters
+ *      rounds of QR-orthonormalised power iteration, Q = qr(Y), Q^T W = U S V^T,
+ *      A_c = Q U_r S_r, B_c = V_r^T);
+ *   2. the packing step of archead_quantize for the core: INT8 A_c, B_c, SC4 of
+ *      R = W - Q(A_c) Q(B_c), and E = W - W_d;
+ *   3. C_lam = H^T H / H_rows + lambda c_bar I (c_bar = mean diagonal of
+ *      H^T H / H_rows), C_lam = Q Lam Q^T, T_p = Q Lam^p Q^T, T_p^{-1};
+ *   4. A_w Bt = rank-r_r randomized SVD of E T_p (omega_r), B_w = Bt T_p^{-1};
+ *   5. INT8 A_w (rows) and B_w (groups) into the same buffer.
+ * Dense products run on rocBLAS and QR / SVD / the eigendecomposition on
+ * rocSOLVER, in fp32; a rocBLAS handle is created for the call (rocBLAS may
+ * allocate its own scratch).  The call waits for the stream at the end to read
+ * the solvers' status: ARCHEAD_E_VALUE if one failed (or for a lambda that is
+ * not positive, or a non-finite p).  packed: as for archead_quantize.
+ * E_NULL, E_DIMS, E_UNSUPPORTED, E_DTYPE, E_SHAPE, E_ALIGN, E_SIZE,
+ * E_WORKSPACE, E_VALUE, E_HIP. */
+ARCHEAD_API int archead_fit(const archead_dims* d, const archead_fit_inputs* in, void* packed,
+                            uint64_t packed_bytes, void* workspace, uint64_t workspace_bytes,
+                            const archead_fit_outputs* out, void* stream);
+
 /* Y = H W_hat^T  (Algorithm 1, inference step).
  *   H: bf16 [N][D] device tensor; rows 16-byte aligned.
  *   Y: fp32 or bf16 [N][V] device tensor, written completely (every element

@@ -164,6 +164,35 @@ def draw_dense(rng, V, D, r_c, r_r, w_dtype="bf16", n_heavy_rows=4) -> Dense:
     return Dense(f32_to_bf16_bits(W) if w_dtype == "bf16" else W, A_c, B_c, A_w, B_w)
 
 
+@dataclass
+class FitInputs:
+    """Inputs of the whole construction: dense head, calibration states and the
+    randomized SVDs' Gaussian test matrices."""
+    W: np.ndarray        # [V, D] bf16 bit patterns (uint16)
+    H: np.ndarray        # [N, D] bf16 bit patterns
+    omega_c: np.ndarray  # [D, r_c + oversample] float32
+    omega_r: np.ndarray  # [D, r_r + oversample] float32
+
+
+def draw_fit(rng, V, D, r_c, r_r, N, oversample=8, n_outlier=4, outlier_scale=20.0) -> FitInputs:
+    """A head with a rank-r_c part plus noise, and calibration hidden states.
+
+    W      L R * 0.02 / sqrt(r_c) + N(0, 0.004), L [V, r_c] and R [r_c, D]
+           N(0, 1), computed in fp32 and rounded once to bf16 (the product
+           only shapes the synthetic spectrum);
+    H      as the forward's hidden states: N(0, 1) with n_outlier channels
+           x outlier_scale, bf16;
+    omega  N(0, 1) fp32.
+    Draw order: L, R, noise, H (with its outlier channels), omega_c, omega_r."""
+    L = rng.standard_normal((V, r_c), dtype=np.float32)
+    R = rng.standard_normal((r_c, D), dtype=np.float32)
+    W = (L @ R) * np.float32(0.02 / np.sqrt(max(r_c, 1))) + rng.normal(0.0, 0.004, size=(V, D)).astype(np.float32)
+    H, _ = draw_hidden(rng, N, D, n_outlier, outlier_scale)
+    om_c = rng.standard_normal((D, r_c + oversample), dtype=np.float32)
+    om_r = rng.standard_normal((D, r_r + oversample), dtype=np.float32)
+    return FitInputs(f32_to_bf16_bits(W), H, om_c, om_r)
+
+
 def make(cfg, seed: Optional[int] = None, N: Optional[int] = None, **overrides) -> Inputs:
     """Draw one workload.  ``cfg`` is a CONFIGS entry, its name or its index.
 

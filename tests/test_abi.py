@@ -282,6 +282,48 @@ def test_topk_error_paths(ah):
     H, P = args(N=0); H.data = None; P.workspace = None; assert call(H, P, 5, None, None) == 0
 
 
+def test_fit_workspace_bytes(ah):
+    up = lambda x: (x + 255) // 256 * 256
+    for (V, D, r_c, r_r, g, o) in [(1000, 256, 16, 8, 64, 8), (151936, 4096, 32, 32, 128, 8), (500, 384, 0, 24, 128, 4)]:
+        k = max(r_c, r_r) + o
+        parts = [V * D * 4, V * D * 4, V * k * 4, D * k * 4, k * 4, k * D * 4, k * 4, k * k * 4, k * D * 4,
+                 max(k, D) * 4, 64, D * D * 4, D * 4, D * D * 4, D * D * 4, D * D * 4,
+                 V * r_c * 4, r_c * D * 4, V * r_r * 4, r_r * D * 4, r_r * D * 4]
+        assert ah.archead_fit_workspace_bytes(V, D, r_c, r_r, g, o) == sum(up(x) for x in parts)
+    with pytest.raises(ah.ArcheadError):
+        ah.archead_fit_workspace_bytes(20, 128, 16, 8, 64, 8)     # rank + oversample above V
+
+
+def test_fit_error_paths(ah):
+    """archead_fit rejects bad arguments on the host, before any HIP call."""
+    V, D, r_c, r_r, g, o = 1000, 256, 16, 8, 64, 8
+    total = ah.archead_pack_layout(V, D, r_c, r_r, g)["total_bytes"]
+    ws = ah.archead_fit_workspace_bytes(V, D, r_c, r_r, g, o)
+
+    def call(dims=(V, D, r_c, r_r, g), buf=FAKE + (8 << 30), nbytes=total, w=FAKE + (16 << 30), nws=ws, **kw):
+        f = dict(W=FAKE, W_stride=D, W_dtype=1, H=FAKE + (1 << 30), H_rows=512, H_stride=D, omega_c=FAKE + (2 << 30),
+                 omega_r=FAKE + (3 << 30), p=0.75, lam=0.01, oversample=o, power_iters=2)
+        f.update(kw)
+        inp = ah.ArcheadFitInputs(*(f[k] for k in ("W", "W_stride", "W_dtype", "H", "H_rows", "H_stride", "omega_c",
+                                                   "omega_r", "p", "lam", "oversample", "power_iters")))
+        return ah.lib.archead_fit(ctypes.byref(ah._dims(*dims)), ctypes.byref(inp), buf, nbytes, w, nws, None, None)
+
+    assert ah.lib.archead_fit(None, None, None, 0, None, 0, None, None) == 1
+    assert call(W=None) == 1 and call(H=None) == 1 and call(buf=None) == 1 and call(w=None) == 1
+    assert call(omega_r=None) == 1
+    assert call(dims=(V, D, r_c, 0, g), omega_r=None, nbytes=0) == 10           # rank-0 part may be NULL
+    assert call(dims=(V, 200, r_c, r_r, g)) == 2
+    assert call(dims=(V, D, r_c, r_r, 16)) == 3
+    assert call(W_dtype=3) == 4
+    assert call(W_stride=D - 1) == 5 and call(H_stride=D - 2) == 5 and call(H_rows=0) == 5
+    assert call(oversample=-1) == 5 and call(power_iters=17) == 5
+    assert call(dims=(20, D, r_c, r_r, g)) == 5                                   # rank + oversample above V
+    assert call(lam=0.0) == 9 and call(p=float("nan")) == 9
+    assert call(buf=FAKE + 128) == 6 and call(w=FAKE + 64) == 6 and call(H=FAKE + 1) == 6
+    assert call(nbytes=total - 1) == 10
+    assert call(nws=ws - 1) == 7
+
+
 def test_logits_zero_tokens_is_a_noop(ah):
     H, P, Y, need, total = _args(ah, N=0)
     H.data = Y.data = None
