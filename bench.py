@@ -306,6 +306,44 @@ def run_quantize(name, steps, warmup):
             "algorithmic": {"fp64_flops": flops, "bytes": nbytes}}
 
 
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32
+
+
+def run_fit(name, steps, n_calib=4096, oversample=8, power_iters=2, p=0.75, lam=0.01):
+    """archead_fit (the whole construction) on one workload's head shape: bf16
+    W, n_calib bf16 calibration tokens and the test matrices resident in HBM;
+    K timed calls (each waits for its stream).  Work: the fp32 products of
+    the two randomized SVDs, the covariance, the two metric transforms, E T_p
+    and the map-back; the eigendecomposition and the small SVDs are not
+    counted."""
+    import torch
+    import synth
+    import compressed_output_head_amd as ah
+
+    cfg = synth.config(name)
+    V, D, r_c, r_r, g = cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"]
+    fi = synth.draw_fit(np.random.default_rng(77), V, D, r_c, r_r, n_calib, oversample=oversample)
+    dev = lambda x: torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
+    W, H = dev(fi.W).view(torch.bfloat16), dev(fi.H).view(torch.bfloat16)
+    oc, orr = dev(fi.omega_c), dev(fi.omega_r)
+    del fi
+    ah.archead_fit(W, H, oc, orr, r_c, r_r, g, p=p, lam=lam, oversample=oversample, power_iters=power_iters)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ah.archead_fit(W, H, oc, orr, r_c, r_r, g, p=p, lam=lam, oversample=oversample, power_iters=power_iters)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    kc, kr = r_c + oversample, r_r + oversample
+    flops = (2 * V * D * (kc + kr) * (2 * power_iters + 2) + 2 * V * kc * r_c + 2 * V * kr * r_r   # randomized SVDs
+             + 2 * n_calib * D * D + 2 * 2 * D ** 3 + 2 * V * D * D + 2 * D * D * r_r)                # metric
+    tf = flops / (ms / 1e3) / 1e12
+    return {"workload": name, "V": V, "D": D, "r_c": r_c, "r_r": r_r, "g": g, "calibration_tokens": n_calib,
+            "p": p, "lambda": lam, "oversample": oversample, "power_iters": power_iters,
+            "ms_per_call": round(ms, 2), "steps": steps, "timed": "whole call, host clock (the call waits)",
+            "fp32_tflops": round(tf, 2), "fp32_frac": round(tf / FP32_PEAK_TFLOPS, 4), "fp32_flops": flops}
+
+
 def dense_context(name, steps=10):
     """Measured ceilings for context (not the target): a dense bf16
     torch.matmul of the workload's shapes (H [N x D] times a dense [D x V]
@@ -431,6 +469,8 @@ def main():
     ap.add_argument("--quantize", default="decode",
                     help="head shape timed through archead_quantize, the packing step ('' to skip)")
     ap.add_argument("--topk", default="batched", help="workload timed through archead_logits_topk, k=10 ('' to skip)")
+    ap.add_argument("--fit", default="decode",
+                    help="head shape timed through archead_fit, the whole construction ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -506,6 +546,10 @@ def main():
         q = run_quantize(args.quantize, max(3, args.steps // 10), 2)
         log(f"[bench] quantize on {args.quantize}: {q['ms_per_call']:.3f} ms/call")
         out["quantize"] = q
+    if args.fit:
+        ft = run_fit(args.fit, 2)
+        log(f"[bench] fit on {args.fit}: {ft['ms_per_call']:.1f} ms/call")
+        out["fit"] = ft
     out["roofline"]["kernel_ms_p10_p50_p90"] = r["kernel_ms_pct"]
     if not args.no_context and args.secondary:
         out["context"] = dense_context(args.secondary)
