@@ -7,5 +7,5 @@ from .archead_oracle import (  # noqa: F401
     bf16_bits_to_f64, f16_to_f64, dequant_R, dequant_rows, dequant_groups,
     w_hat, logits, row_argmax, top2_gap, row_stats, row_topk,
     quant_int8_rows, quant_int8_groups, quant_sc4, core_residual, quantize,
-    damped_covariance, metric_transform, rsvd, metric_objective, fit,
+    damped_covariance, metric_transform, rsvd, metric_objective, fit, logit_error,
 )

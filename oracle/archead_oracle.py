@@ -452,6 +452,16 @@ def quantize(W, A_c, B_c, A_w, B_w, g):
     return head, E
 
 
+def logit_error(H_bits, head, W):
+    """The logit error of Eq. 1 before the 1/N: sum over tokens and vocabulary
+    of (H W^T - H W_hat^T)^2, and the reference energy sum of (H W^T)^2.
+    H_bits [N, D] and W [V, D] are bf16 bit patterns; fp64 throughout."""
+    H = bf16_bits_to_f64(H_bits)
+    Yd = H @ bf16_bits_to_f64(W).T
+    Yp = logits(H_bits, head)
+    return float(np.sum((Yd - Yp) ** 2)), float(np.sum(Yd ** 2))
+
+
 # ---------------------------------------------------------------- fitting ---
 #
 # The construction of Algorithm 1 (ARCHead, Sec. 3 and Algorithm 1): the core

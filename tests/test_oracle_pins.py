@@ -748,3 +748,25 @@ def test_fit_end_to_end_properties():
     Jf = oracle.metric_objective(f["E"] - f["A_w"].astype(np.float64) @ f["B_w"], T)
     Jq = oracle.metric_objective(f["E"] - oracle.dequant_rows(head.A_w, head.s_Aw) @ oracle.dequant_groups(head.B_w, head.s_Bw, g), T)
     assert Jf < 0.8 * J0 and Jq < 0.85 * J0
+
+
+def test_logit_error_pins():
+    """Eq. 1: a zero head leaves the whole reference energy as error; a zero W
+    leaves the packed logits' energy; brute force over tokens on a tiny case;
+    divided by N it equals the metric objective at p = 1/2 without damping."""
+    inp = synth.make("tiny", seed=3, V=40, D=128, N=6, r_c=8, r_r=8, g=32)
+    W = synth.f32_to_bf16_bits(np.random.default_rng(2).normal(0, 0.05, size=(40, 128)).astype(np.float32))
+    z = synth.zero_head(40, 128, 8, 8, 32)
+    err, ref = oracle.logit_error(inp.H_bits, z, W)
+    assert err == ref > 0
+    err0, _ = oracle.logit_error(inp.H_bits, inp.head, np.zeros_like(W))
+    assert np.isclose(err0, np.sum(oracle.logits(inp.H_bits, inp.head) ** 2), rtol=1e-14)
+    H = oracle.bf16_bits_to_f64(inp.H_bits)
+    Wd, Wh = oracle.bf16_bits_to_f64(W), oracle.w_hat(inp.head)
+    brute = sum(float(np.dot(H[n], Wd[v] - Wh[v])) ** 2 for n in range(6) for v in range(40))
+    err, _ = oracle.logit_error(inp.H_bits, inp.head, W)
+    assert np.isclose(err, brute, rtol=1e-10)
+    Hm = np.random.default_rng(5).normal(size=(300, 16))
+    Dl = np.random.default_rng(6).normal(size=(10, 16))
+    T, _ = oracle.metric_transform(oracle.damped_covariance(Hm, 0.0), 0.5)
+    assert np.isclose(np.sum((Hm @ Dl.T) ** 2) / 300, oracle.metric_objective(Dl, T), rtol=1e-10)
