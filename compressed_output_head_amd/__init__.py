@@ -25,7 +25,8 @@ STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5
 EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_pack", "archead_logits",
            "archead_logits_path", "archead_logits_events", "archead_stats_workspace_bytes",
            "archead_logits_stats", "archead_quantize", "archead_topk_workspace_bytes", "archead_logits_topk",
-           "archead_fit_workspace_bytes", "archead_fit",
+           "archead_fit_workspace_bytes", "archead_fit", "archead_logit_error_workspace_bytes",
+           "archead_logit_error",
            "archead_status_string", "archead_format_version")
 
 
@@ -123,6 +124,9 @@ def _load():
     lib.archead_fit_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int32, P(ctypes.c_uint64)]
     lib.archead_fit.argtypes = [P(ArcheadDims), P(ArcheadFitInputs), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                 ctypes.c_uint64, P(ArcheadFitOutputs), ctypes.c_void_p]
+    lib.archead_logit_error_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int64, P(ctypes.c_uint64)]
+    lib.archead_logit_error.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor),
+                                        P(ctypes.c_double), ctypes.c_void_p]
     lib.archead_status_string.argtypes = [ctypes.c_int]
     lib.archead_status_string.restype = ctypes.c_char_p
     lib.archead_format_version.argtypes = []
@@ -241,10 +245,10 @@ class PackedHead:
     def dims(self):
         return dict(V=self.V, D=self.D, r_c=self.r_c, r_r=self.r_r, g=self.g)
 
-    def ensure_workspace(self, n_tokens: int, stats: bool = False, topk: bool = False):
+    def ensure_workspace(self, n_tokens: int, stats: bool = False, topk: bool = False, logit_error: bool = False):
         torch = _torch()
-        size = archead_topk_workspace_bytes if topk else archead_stats_workspace_bytes if stats \
-            else archead_workspace_bytes
+        size = archead_logit_error_workspace_bytes if logit_error else archead_topk_workspace_bytes if topk \
+            else archead_stats_workspace_bytes if stats else archead_workspace_bytes
         need = size(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens)
         if self.workspace is None or self.workspace.numel() < need:
             self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.buffer.device)
@@ -428,3 +432,26 @@ def archead_fit(W, H, omega_c, omega_r, r_c: int, r_r: int, g: int, p: float = 0
                            buf.numel(), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                            ctypes.byref(outs) if outputs else None, ctypes.c_void_p(stream)), "archead_fit")
     return PackedHead(V, D, r_c, r_r, g, buf), f
+
+
+def archead_logit_error_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
+    out = ctypes.c_uint64(0)
+    _check(lib.archead_logit_error_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
+                                                   ctypes.byref(out)), "archead_logit_error_workspace_bytes")
+    return out.value
+
+
+def archead_logit_error(H, head: PackedHead, W, stream=None):
+    """(sum of squared logit differences against the dense bf16 head W, sum of
+    squared dense logits) over the rows of H, as Python floats (the call waits)."""
+    torch = _torch()
+    head.ensure_workspace(H.shape[0], logit_error=True)
+    if stream is None:
+        stream = torch.cuda.current_stream(H.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    sums = (ctypes.c_double * 2)()
+    h, p, w = _tensor(H), head.struct(), _tensor(W)
+    _check(lib.archead_logit_error(ctypes.byref(h), ctypes.byref(p), ctypes.byref(w), sums, ctypes.c_void_p(stream)),
+           "archead_logit_error")
+    return sums[0], sums[1]

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libarchead.so")
 SOURCES = ["archead.hip", "prep.hip", "decode.hip", "mid.hip", "tile.hip", "tile_stats.hip", "stats.hip",
-           "quantize.hip", "topk.hip", "fit.hip"]
+           "quantize.hip", "topk.hip", "fit.hip", "logit_error.hip"]
 # dense products and factorisations of the construction step
 LINK_LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-lrocsolver"]
 ARCH = os.environ.get("ARCHEAD_OFFLOAD_ARCH", "gfx950")

@@ -256,6 +256,25 @@ ARCHEAD_API int archead_fit(const archead_dims* d, const archead_fit_inputs* in,
                             uint64_t packed_bytes, void* workspace, uint64_t workspace_bytes,
                             const archead_fit_outputs* out, void* stream);
 
+/* Device workspace archead_logit_error needs for n_tokens rows: the
+ * forward's workspace for min(n_tokens, 256) rows rounded up to 256, two
+ * fp32 blocks of min(n_tokens, 256) x V logits (each rounded up to 256),
+ * 16 KiB of partial sums and 256 bytes (0 when n_tokens = 0).  Pure host
+ * arithmetic.  E_NULL, E_DIMS, E_SHAPE. */
+ARCHEAD_API int archead_logit_error_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes);
+
+/* The logit error of a packed head against the dense head W it replaces, on
+ * the N rows of H (ARCHead, Sec. 3, Eq. 1 before its 1/N):
+ *   sums[0] = sum_{n,v} (H W^T - H W_hat^T)[n, v]^2,  sums[1] = sum_{n,v} (H W^T)[n, v]^2,
+ * in fp64 from fp32 logits (host array of 2 doubles).  W: bf16 [V][D] device
+ * tensor.  The packed logits come from the forward, the dense ones from a
+ * rocBLAS bf16 product with fp32 accumulation, 256 tokens at a time in the
+ * workspace (at least archead_logit_error_workspace_bytes).  Waits for the
+ * stream.  H and head as for archead_logits.  E_NULL, E_DTYPE, E_SHAPE,
+ * E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP. */
+ARCHEAD_API int archead_logit_error(const archead_tensor* H, const archead_packed_head* head,
+                                    const archead_tensor* W, double* sums, void* stream);
+
 /* Y = H W_hat^T  (Algorithm 1, inference step).
  *   H: bf16 [N][D] device tensor; rows 16-byte aligned.
  *   Y: fp32 or bf16 [N][V] device tensor, written completely (every element

@@ -324,6 +324,33 @@ def test_fit_error_paths(ah):
     assert call(nws=ws - 1) == 7
 
 
+def test_logit_error_workspace_and_errors(ah):
+    up = lambda x: (x + 255) // 256 * 256
+    for N in (1, 255, 256, 1000):
+        rows = min(N, 256)
+        want = up(ah.archead_workspace_bytes(1024, 256, 16, 8, 64, rows)) + 2 * up(rows * 1024 * 4) + 16384 + 256
+        assert ah.archead_logit_error_workspace_bytes(1024, 256, 16, 8, 64, N) == want
+    assert ah.archead_logit_error_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
+    sums = (ctypes.c_double * 2)()
+
+    def call(H, P, W, out=sums):
+        return ah.lib.archead_logit_error(ctypes.byref(H), ctypes.byref(P), ctypes.byref(W), out, None)
+
+    def args():
+        H, P, Y, need, total = _args(ah)
+        P.workspace_bytes = ah.archead_logit_error_workspace_bytes(1024, 256, 16, 8, 64, 4)
+        return H, P, ah.ArcheadTensor(FAKE + (9 << 30), 1024, 256, 256, 1)
+
+    H, P, W = args(); assert call(H, P, W, None) == 1
+    H, P, W = args(); W.dtype = 2; assert call(H, P, W) == 4
+    H, P, W = args(); W.rows = 1000; assert call(H, P, W) == 5
+    H, P, W = args(); W.row_stride = 255; assert call(H, P, W) == 5
+    H, P, W = args(); W.data = FAKE + 1; assert call(H, P, W) == 6
+    H, P, W = args(); P.workspace_bytes -= 1; assert call(H, P, W) == 7
+    H, P, W = args(); H.rows = 0; H.data = None; P.workspace = None; sums[0] = 5.0
+    assert call(H, P, W) == 0 and sums[0] == 0.0
+
+
 def test_logits_zero_tokens_is_a_noop(ah):
     H, P, Y, need, total = _args(ah, N=0)
     H.data = Y.data = None
