@@ -20,8 +20,8 @@ constexpr int64_t kTkChunkRows = 256;  // tokens per forward chunk
 constexpr int kTkBatch = 8;            // elements a thread loads before inserting
 constexpr int64_t kTkPieceWGs = 2048;  // first-stage workgroups per chunk (about)
 constexpr int64_t kTkMinPiece = 2048;  // smallest vocabulary piece
-// candidates of the first stage: at most kTkPieceWGs pieces of kTkMax
-constexpr uint64_t kTkCandBytes = (uint64_t)kTkPieceWGs * kTkMax * 8;
+// candidates of the first stage: at most kTkPieceWGs pieces, kTkMax per wave
+constexpr uint64_t kTkCandBytes = (uint64_t)kTkPieceWGs * kTkWaves * kTkMax * 8;
 
 constexpr uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
 
@@ -99,6 +99,38 @@ __device__ __forceinline__ void tk_select(float (&val)[K], int (&idx)[K], int k,
   }
 }
 
+// The same over one wave's 64 lists, with shuffles only: lane 0 writes.
+template <int K>
+__device__ __forceinline__ void tk_select_wave(float (&val)[K], int (&idx)[K], int k, float* ov, int32_t* oi) {
+  const int lane = threadIdx.x & 63;
+  for (int r = 0; r < k; ++r) {
+    float bv = val[0];
+    int bi = idx[0];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float xv = __shfl_xor(bv, off);
+      const int xi = __shfl_xor(bi, off);
+      if (tk_before(xv, xi, bv, bi)) {
+        bv = xv;
+        bi = xi;
+      }
+    }
+    if (lane == 0) {
+      ov[r] = bv;
+      oi[r] = bi;
+    }
+    if (idx[0] == bi) {
+#pragma unroll
+      for (int i = 0; i < K - 1; ++i) {
+        val[i] = val[i + 1];
+        idx[i] = idx[i + 1];
+      }
+      val[K - 1] = -INFINITY;
+      idx[K - 1] = INT32_MAX;
+    }
+  }
+}
+
 template <int K>
 __device__ __forceinline__ void tk_clear(float (&val)[K], int (&idx)[K]) {
 #pragma unroll
@@ -109,8 +141,9 @@ __device__ __forceinline__ void tk_clear(float (&val)[K], int (&idx)[K]) {
 }
 
 // Stage 1: workgroup (p, row) takes the vocabulary piece [p L, (p + 1) L) of
-// one row of Y [rows][V] and writes its k best to cand[(row P + p) k + r].
-// Each thread loads kTkBatch elements (256 apart) before inserting them.
+// one row of Y [rows][V]; each wave writes the k best of its share to
+// cand[((row P + p) waves + wave) k + r] (no barriers).  Each thread loads
+// kTkBatch elements (256 apart) before inserting them.
 template <int K>
 __global__ __launch_bounds__(kTkThreads) void topk_piece_kernel(const float* Y, int64_t V, int64_t L, int k,
                                                                 float* cv, int32_t* ci) {
@@ -134,11 +167,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_piece_kernel(const float* Y, 
       if (v < hi) tk_insert(val, idx, x[u], (int)v);
     }
   }
-  const int64_t o = (row * P + p) * k;
-  tk_select(val, idx, k, cv + o, ci + o);
+  const int64_t o = ((row * P + p) * kTkWaves + (threadIdx.x >> 6)) * k;
+  tk_select_wave(val, idx, k, cv + o, ci + o);
 }
 
-// Stage 2: one workgroup per row merges the row's n = P k candidates.
+// Stage 2: one workgroup per row merges the row's n = P waves k candidates.
 template <int K>
 __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const float* cv, const int32_t* ci, int n, int k,
                                                                 float* out_val, int32_t* out_idx, int64_t out_ld) {
@@ -166,7 +199,7 @@ hipError_t launch_topk_k(const float* Y, int64_t rows, int64_t V, int k, float* 
   const int64_t L = (V + P - 1) / P;
   hipLaunchKernelGGL((topk_piece_kernel<K>), dim3((unsigned)P, (unsigned)rows), dim3(kTkThreads), 0, s, Y, V, L, k,
                      cv, ci);
-  hipLaunchKernelGGL((topk_merge_kernel<K>), dim3((unsigned)rows), dim3(kTkThreads), 0, s, cv, ci, P * k, k,
+  hipLaunchKernelGGL((topk_merge_kernel<K>), dim3((unsigned)rows), dim3(kTkThreads), 0, s, cv, ci, P * kTkWaves * k, k,
                      out_val, out_idx, out_ld);
   return hipGetLastError();
 }

@@ -338,7 +338,7 @@ ARCHEAD_API int archead_logits_stats(const archead_tensor* H, const archead_pack
 
 /* Device workspace one archead_logits_topk call with n_tokens rows needs:
  * archead_workspace_bytes for min(n_tokens, 256) rows, rounded up to 256,
- * plus min(n_tokens, 256) x V fp32 logits rounded up to 256, plus 256 KiB
+ * plus min(n_tokens, 256) x V fp32 logits rounded up to 256, plus 1 MiB
  * of first-stage candidates (0 when n_tokens = 0).  Pure host arithmetic.
  * E_NULL, E_DIMS, E_SHAPE. */
 ARCHEAD_API int archead_topk_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes);
