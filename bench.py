@@ -303,7 +303,10 @@ def run_quantize(name, steps, warmup):
             "ms_per_call": round(ms, 4), "steps": steps, "timed": "whole call",
             "fp64_tflops": round(tf, 2), "fp64_frac": round(tf / FP64_PEAK_TFLOPS, 4),
             "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic": {"fp64_flops": flops, "bytes": nbytes}}
+            "algorithmic": {"fp64_flops": flops, "bytes": nbytes},
+            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP64_PEAK_TFLOPS, 4), "traffic": None,
+                         "timed": "whole call; the fp64 core products of the residual kernel"}}
 
 
 FP32_PEAK_TFLOPS = 157.3  # MI355X fp32
@@ -341,7 +344,10 @@ def run_fit(name, steps, n_calib=4096, oversample=8, power_iters=2, p=0.75, lam=
     return {"workload": name, "V": V, "D": D, "r_c": r_c, "r_r": r_r, "g": g, "calibration_tokens": n_calib,
             "p": p, "lambda": lam, "oversample": oversample, "power_iters": power_iters,
             "ms_per_call": round(ms, 2), "steps": steps, "timed": "whole call, host clock (the call waits)",
-            "fp32_tflops": round(tf, 2), "fp32_frac": round(tf / FP32_PEAK_TFLOPS, 4), "fp32_flops": flops}
+            "fp32_tflops": round(tf, 2), "fp32_frac": round(tf / FP32_PEAK_TFLOPS, 4), "fp32_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP32_PEAK_TFLOPS, 4), "traffic": None,
+                         "timed": "whole call; fp32 products only (QR panels and the eigensolver are latency-bound)"}}
 
 
 def dense_context(name, steps=10):
