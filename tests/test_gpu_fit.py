@@ -84,3 +84,44 @@ def test_fit_rejects_nonpositive_damping_before_launch():
     fi = synth.draw_fit(np.random.default_rng(1), 200, 256, 8, 8, 100)
     with pytest.raises(ah.ArcheadError):
         ah.archead_fit(_dev(fi.W), _dev(fi.H), _dev(fi.omega_c), _dev(fi.omega_r), 8, 8, 64, lam=0.0)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_fit_full_size_sampled_rows():
+    """The decode/batched head shape (V=151936, D=4096, r_c=r_r=32, g=128) with
+    4096 calibration tokens, in the configuration bench.py times (oversample 8,
+    two power iterations, p=0.75, lambda=0.01).  On 64 seeded rows: the packing
+    of the GPU's factors is exact; the core residual of each row matches the
+    oracle's randomized SVD of the whole W (same test matrix, fp64) to 1e-3 of
+    the rows' total; the correction lowers the rows' metric objective."""
+    cfg = synth.config("decode")
+    V, D, r_c, r_r, g = cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"]
+    p, lam, o, q = 0.75, 0.01, 8, 2
+    log(f"full-size fit V={V} D={D} r_c={r_c} r_r={r_r} N=4096")
+    fi = synth.draw_fit(np.random.default_rng(77), V, D, r_c, r_r, 4096, oversample=o)
+    buf, f = _run(fi, r_c, r_r, g, p, lam, o, q)
+    rows = np.unique(np.concatenate([[0, V - 1], np.random.default_rng(8).choice(V, 62, replace=False)]))
+    got = oracle.unpack(buf, V, D, r_c, r_r, g)
+    ref, E_ref = oracle.quantize(fi.W[rows], f["A_c"][rows], f["B_c"], f["A_w"][rows], f["B_w"], g)
+    for k in ("q4", "c8", "s_R", "A_c", "s_Ac", "A_w", "s_Aw"):
+        a, b = np.ascontiguousarray(got[k][rows]), np.ascontiguousarray(getattr(ref, k))
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), k
+    for k in ("B_c", "s_Bc", "B_w", "s_Bw"):
+        a, b = np.ascontiguousarray(got[k]), np.ascontiguousarray(getattr(ref, k))
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), k
+    assert np.array_equal(f["E"][rows].view(np.uint32), E_ref.view(np.uint32))
+    log("  packing exact on sampled rows; oracle randomized SVD of the whole W ...")
+    W64 = oracle.bf16_bits_to_f64(fi.W)
+    A, B = oracle.rsvd(W64, r_c, fi.omega_c, q)
+    res_o = np.sum((W64[rows] - A[rows] @ B) ** 2, axis=1)
+    del W64, A
+    res_g = np.sum((oracle.bf16_bits_to_f64(fi.W[rows]) - f["A_c"][rows].astype(np.float64) @ f["B_c"]) ** 2, axis=1)
+    log(f"  core residual on the rows: gpu {res_g.sum():.6e} oracle {res_o.sum():.6e}")
+    assert np.abs(res_g - res_o).max() <= 1e-3 * res_o.sum()
+    T, _ = oracle.metric_transform(oracle.damped_covariance(oracle.bf16_bits_to_f64(fi.H), lam), p)
+    E = f["E"][rows].astype(np.float64)
+    J0 = oracle.metric_objective(E, T)
+    Jg = oracle.metric_objective(E - f["A_w"][rows].astype(np.float64) @ f["B_w"], T)
+    log(f"  metric objective on the rows: none {J0:.6e} corrected {Jg:.6e}")
+    assert Jg < J0
