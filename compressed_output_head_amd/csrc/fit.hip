@@ -316,6 +316,9 @@ int archead_fit(const archead_dims* d, const archead_fit_inputs* in, void* packe
     for (int i = 0; i < 16; ++i)
       if (info[i] != 0 && st.rc == ARCHEAD_OK) st.rc = ARCHEAD_E_VALUE;
   } while (false);
+  // rocSOLVER's scratch belongs to the handle: nothing may still run on the
+  // stream when it is destroyed (an error can leave work enqueued)
+  if (hipStreamSynchronize(s) != hipSuccess && st.rc == ARCHEAD_OK) st.rc = ARCHEAD_E_HIP;
   rocblas_destroy_handle(h);
   return st.rc;
 }

@@ -145,9 +145,9 @@ int archead_logit_error(const archead_tensor* H, const archead_packed_head* head
     hipLaunchKernelGGL(sq_total_kernel, dim3(1), dim3(kLeThreads), 0, s, part, kLeBlocks, acc, t0 == 0 ? 1 : 0);
     if (hipGetLastError() != hipSuccess) rc = ARCHEAD_E_HIP;
   }
-  if (rc == ARCHEAD_OK && (hipMemcpyAsync(sums, acc, 16, hipMemcpyDeviceToHost, s) != hipSuccess ||
-                           hipStreamSynchronize(s) != hipSuccess))
-    rc = ARCHEAD_E_HIP;
+  if (rc == ARCHEAD_OK && hipMemcpyAsync(sums, acc, 16, hipMemcpyDeviceToHost, s) != hipSuccess) rc = ARCHEAD_E_HIP;
+  // the handle's scratch must outlive everything enqueued with it, also after an error
+  if (hipStreamSynchronize(s) != hipSuccess && rc == ARCHEAD_OK) rc = ARCHEAD_E_HIP;
   rocblas_destroy_handle(h);
   return rc;
 }
