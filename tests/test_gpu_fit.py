@@ -125,3 +125,14 @@ def test_fit_full_size_sampled_rows():
     Jg = oracle.metric_objective(E - f["A_w"][rows].astype(np.float64) @ f["B_w"], T)
     log(f"  metric objective on the rows: none {J0:.6e} corrected {Jg:.6e}")
     assert Jg < J0
+
+
+def test_fit_with_no_factors_is_plain_sc4():
+    """r_c = r_r = 0: the packed head is SC4 of W alone and E = W - SC4(W)."""
+    V, D, g = 300, 256, 64
+    fi = synth.draw_fit(np.random.default_rng(2), V, D, 0, 0, 200, oversample=4)
+    buf, f = _run(fi, 0, 0, g, 0.75, 0.01, 4, 1)
+    none = (np.zeros((V, 0), np.float32), np.zeros((0, D), np.float32))
+    head_ref, E_ref = oracle.quantize(fi.W, *none, *none, g)
+    assert np.array_equal(buf, oracle.pack(head_ref))
+    assert np.array_equal(f["E"].view(np.uint32), E_ref.view(np.uint32))

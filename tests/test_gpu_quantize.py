@@ -119,3 +119,15 @@ def test_quantize_full_size_sampled_rows():
         a, b = np.ascontiguousarray(got[k]), np.ascontiguousarray(getattr(ref, k))
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), k
     assert np.array_equal(E[rows].view(np.uint32), E_ref.view(np.uint32))
+
+
+def test_quantize_at_the_core_rank_limit():
+    """Core rank 1024, the most the residual kernel keeps in LDS (8 rows x 1024
+    fp64 values = 64 KiB), and D = 8192 with 4 rows per workgroup."""
+    for V, D, r_c, r_r in [(70, 256, 1024, 8), (40, 8192, 1024, 0)]:
+        log(f"quantize at the rank limit V={V} D={D} r_c={r_c}")
+        dense = synth.draw_dense(np.random.default_rng(D), V, D, r_c, r_r, "bf16")
+        head_ref, E_ref = oracle.quantize(dense.W, dense.A_c, dense.B_c, dense.A_w, dense.B_w, 128)
+        head, E = _quantize(dense, 128)
+        assert np.array_equal(head.buffer.cpu().numpy(), oracle.pack(head_ref))
+        assert np.array_equal(E.view(np.uint32), E_ref.view(np.uint32))

@@ -93,3 +93,21 @@ def test_topk_full_size_batched():
     Yr = oracle.logits(inp.H_bits, inp.head, rows=rows)
     rv, _ = oracle.row_topk(Yr, 10)
     assert np.abs(vals.astype(np.float64) - rv).max() <= TOL * np.abs(Yr).max()
+
+
+@pytest.mark.parametrize("V,k", [(16, 16), (10, 10), (33, 16), (1, 1)])
+def test_topk_small_vocabularies(V, k):
+    """k equal to V (every index comes back, sorted), vocabularies smaller
+    than one piece, and a single row of vocabulary."""
+    D, N = 256, 20
+    inp = synth.make("tiny", seed=V, V=V, D=D, N=N, r_c=8, r_r=8, g=32)
+    ah = ah_mod()
+    head = ah.PackedHead.from_components(inp.head)
+    H = device_H(inp.H_bits)
+    vals, idx = ah.archead_logits_topk(H, head, k)
+    torch_mod().cuda.synchronize()
+    vals, idx = vals.cpu().numpy(), idx.cpu().numpy()
+    ov, oi = oracle.row_topk(_own_logits(head, H), k)
+    assert np.array_equal(idx, oi) and np.array_equal(vals, ov.astype(np.float32))
+    if k == V:
+        assert (np.sort(idx, axis=1) == np.arange(V)).all()
