@@ -10,14 +10,19 @@
  *     (group-wise INT8) (Sec. 3, packed-variant paragraph; Algorithm 1),
  * and inference evaluates  Y = H W_d^T + (H B_w^T) A_w^T  (Algorithm 1, last
  * step), with W_d = Q(A_c) Q(B_c) + SC4(R).  This library computes exactly that
- * forward from the packed bytes; it never forms the V x D matrix.
+ * forward from the packed bytes; it never forms the V x D matrix.  Around the
+ * forward: per-row statistics and top-k of the logits, the logit error of
+ * Eq. 1, and the construction itself (packing, and the full fit of Algorithm 1).
  *
  * Conventions for every entry point:
  *   - All functions return an archead_status (0 = ARCHEAD_OK).  They never
  *     abort, throw or print.  Arguments are checked on the host before any
  *     HIP call; on a non-zero status nothing has been enqueued.
  *   - The caller owns all memory.  The library allocates nothing on the
- *     device and keeps no pointer after a call returns.
+ *     device and keeps no pointer after a call returns, except that
+ *     archead_fit and archead_logit_error create a rocBLAS handle for the call
+ *     (rocBLAS and rocSOLVER allocate their own scratch) and wait for the
+ *     stream before returning.
  *   - Device pointers must stay valid until the stream has passed the work
  *     enqueued by the call.  Calls on different streams need different
  *     workspaces; the library holds no global state and is re-entrant.
