@@ -136,3 +136,22 @@ def test_fit_with_no_factors_is_plain_sc4():
     head_ref, E_ref = oracle.quantize(fi.W, *none, *none, g)
     assert np.array_equal(buf, oracle.pack(head_ref))
     assert np.array_equal(f["E"].view(np.uint32), E_ref.view(np.uint32))
+
+
+def test_fit_fp32_strided_w():
+    """W given as fp32 through a strided view (row stride D + 64) gives the
+    same packed head as the contiguous bf16 values it holds."""
+    V, D, r_c, r_r, g = 500, 256, 8, 8, 64
+    fi = synth.draw_fit(np.random.default_rng(12), V, D, r_c, r_r, 300, oversample=4)
+    torch = torch_mod()
+    ah = ah_mod()
+    W32 = oracle.bf16_bits_to_f64(fi.W).astype(np.float32)
+    pad = np.zeros((V, D + 64), np.float32)
+    pad[:, :D] = W32
+    Wv = torch.from_numpy(pad).to("cuda")[:, :D]
+    head_a, _ = ah.archead_fit(Wv, _dev(fi.H), _dev(fi.omega_c), _dev(fi.omega_r), r_c, r_r, g, oversample=4,
+                               power_iters=1)
+    head_b, _ = ah.archead_fit(_dev(fi.W), _dev(fi.H), _dev(fi.omega_c), _dev(fi.omega_r), r_c, r_r, g, oversample=4,
+                               power_iters=1)
+    torch.cuda.synchronize()
+    assert torch.equal(head_a.buffer, head_b.buffer)
