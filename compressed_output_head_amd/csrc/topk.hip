@@ -2,8 +2,8 @@
 // indices: the quantity behind the pages' top-k agreement figures (ARCHead,
 // results discussion of Table 8: top-1/5/10).  The forward runs in chunks of
 // tokens into fp32 logits held in the caller's workspace; the selection then
-// takes the k best of each vocabulary piece of a row (many workgroups per
-// row) and the k best of those candidates (one workgroup per row).  Order:
+// takes the k best of every 1024-element span of a row (one wave each) and
+// the k best of those candidates (one workgroup per row).  Order:
 // larger value first, and among equal values the lower index first, so the
 // result is unique.
 #include <hip/hip_runtime.h>
@@ -17,11 +17,9 @@ constexpr int kTkThreads = 256;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkMax = 16;             // largest k
 constexpr int64_t kTkChunkRows = 256;  // tokens per forward chunk
-constexpr int kTkBatch = 8;            // elements a thread loads before inserting
-constexpr int64_t kTkPieceWGs = 2048;  // first-stage workgroups per chunk (about)
-constexpr int64_t kTkMinPiece = 2048;  // smallest vocabulary piece
-// candidates of the first stage: at most kTkPieceWGs pieces, kTkMax per wave
-constexpr uint64_t kTkCandBytes = (uint64_t)kTkPieceWGs * kTkWaves * kTkMax * 8;
+constexpr int kTkPer = 16;                              // first stage: elements per lane
+constexpr int64_t kTkWaveSpan = 64 * kTkPer;            // elements per wave
+constexpr int64_t kTkPiece = kTkWaves * kTkWaveSpan;    // elements per first-stage workgroup
 
 constexpr uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
 
@@ -99,13 +97,48 @@ __device__ __forceinline__ void tk_select(float (&val)[K], int (&idx)[K], int k,
   }
 }
 
-// The same over one wave's 64 lists, with shuffles only: lane 0 writes.
 template <int K>
-__device__ __forceinline__ void tk_select_wave(float (&val)[K], int (&idx)[K], int k, float* ov, int32_t* oi) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void tk_clear(float (&val)[K], int (&idx)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    val[i] = -INFINITY;
+    idx[i] = INT32_MAX;
+  }
+}
+
+// Stage 1: wave w of workgroup (p, row) takes the kTkWaveSpan elements of
+// one row of Y [rows][V] from (p waves + w) kTkWaveSpan on, kTkPer per lane
+// (64 apart, all loads in flight together), and writes its k best to
+// cand[((row P + p) waves + w) k + r]: k rounds of a shuffle reduction over
+// the lanes' best remaining element; the winner's lane marks it taken.
+// Elements past V never win (index INT32_MAX); with fewer than k elements the
+// remaining outputs are (-inf, INT32_MAX) and lose every merge.
+__global__ __launch_bounds__(kTkThreads) void topk_piece_kernel(const float* Y, int64_t V, int k, float* cv,
+                                                                int32_t* ci) {
+  const int P = gridDim.x, p = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.y;
+  const float* y = Y + row * V;
+  const int64_t base = ((int64_t)p * kTkWaves + wave) * kTkWaveSpan + lane;
+  float x[kTkPer];
+#pragma unroll
+  for (int e = 0; e < kTkPer; ++e) {
+    const int64_t v = base + 64 * e;
+    x[e] = v < V ? y[v] : -INFINITY;
+  }
+  uint32_t taken = 0u;
+  const int64_t o = ((row * P + p) * kTkWaves + wave) * k;
   for (int r = 0; r < k; ++r) {
-    float bv = val[0];
-    int bi = idx[0];
+    float bv = -INFINITY;
+    int bi = INT32_MAX;
+#pragma unroll
+    for (int e = 0; e < kTkPer; ++e) {
+      const int64_t v = base + 64 * e;
+      const int vi = v < V ? (int)v : INT32_MAX;
+      if (!((taken >> e) & 1u) && tk_before(x[e], vi, bv, bi)) {
+        bv = x[e];
+        bi = vi;
+      }
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       const float xv = __shfl_xor(bv, off);
@@ -116,59 +149,11 @@ __device__ __forceinline__ void tk_select_wave(float (&val)[K], int (&idx)[K], i
       }
     }
     if (lane == 0) {
-      ov[r] = bv;
-      oi[r] = bi;
+      cv[o + r] = bv;
+      ci[o + r] = bi;
     }
-    if (idx[0] == bi) {
-#pragma unroll
-      for (int i = 0; i < K - 1; ++i) {
-        val[i] = val[i + 1];
-        idx[i] = idx[i + 1];
-      }
-      val[K - 1] = -INFINITY;
-      idx[K - 1] = INT32_MAX;
-    }
+    if (bi != INT32_MAX && (bi - base) % 64 == 0 && bi >= base) taken |= 1u << (int)((bi - base) / 64);
   }
-}
-
-template <int K>
-__device__ __forceinline__ void tk_clear(float (&val)[K], int (&idx)[K]) {
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    val[i] = -INFINITY;
-    idx[i] = INT32_MAX;
-  }
-}
-
-// Stage 1: workgroup (p, row) takes the vocabulary piece [p L, (p + 1) L) of
-// one row of Y [rows][V]; each wave writes the k best of its share to
-// cand[((row P + p) waves + wave) k + r] (no barriers).  Each thread loads
-// kTkBatch elements (256 apart) before inserting them.
-template <int K>
-__global__ __launch_bounds__(kTkThreads) void topk_piece_kernel(const float* Y, int64_t V, int64_t L, int k,
-                                                                float* cv, int32_t* ci) {
-  const int P = gridDim.x, p = blockIdx.x;
-  const int64_t row = blockIdx.y;
-  const float* y = Y + row * V;
-  const int64_t lo = (int64_t)p * L, hi = lo + L < V ? lo + L : V;
-  float val[K];
-  int idx[K];
-  tk_clear(val, idx);
-  for (int64_t base = lo + threadIdx.x; base < hi; base += (int64_t)kTkThreads * kTkBatch) {
-    float x[kTkBatch];
-#pragma unroll
-    for (int u = 0; u < kTkBatch; ++u) {
-      const int64_t v = base + (int64_t)kTkThreads * u;
-      x[u] = v < hi ? y[v] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < kTkBatch; ++u) {
-      const int64_t v = base + (int64_t)kTkThreads * u;
-      if (v < hi) tk_insert(val, idx, x[u], (int)v);
-    }
-  }
-  const int64_t o = ((row * P + p) * kTkWaves + (threadIdx.x >> 6)) * k;
-  tk_select_wave(val, idx, k, cv + o, ci + o);
 }
 
 // Stage 2: one workgroup per row merges the row's n = P waves k candidates.
@@ -183,24 +168,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const float* cv,
   tk_select(val, idx, k, out_val + row * out_ld, out_idx + row * out_ld);
 }
 
-// pieces per row: about kTkPieceWGs workgroups in all, each piece at least
-// kTkMinPiece elements
-int tk_pieces(int64_t rows, int64_t V) {
-  int64_t P = kTkPieceWGs / (rows > 0 ? rows : 1);
-  const int64_t pmax = (V + kTkMinPiece - 1) / kTkMinPiece;
-  if (P > pmax) P = pmax;
-  return P < 1 ? 1 : (int)P;
+int64_t tk_pieces(int64_t V) { return (V + kTkPiece - 1) / kTkPiece; }
+
+// candidate bytes of the first stage for a chunk of `rows` rows
+uint64_t tk_cand_bytes(int64_t rows, int64_t V) {
+  return up256((uint64_t)rows * (uint64_t)tk_pieces(V) * kTkWaves * kTkMax * 4) * 2;
 }
 
 template <int K>
 hipError_t launch_topk_k(const float* Y, int64_t rows, int64_t V, int k, float* cv, int32_t* ci, float* out_val,
                          int32_t* out_idx, int64_t out_ld, hipStream_t s) {
-  const int P = tk_pieces(rows, V);
-  const int64_t L = (V + P - 1) / P;
-  hipLaunchKernelGGL((topk_piece_kernel<K>), dim3((unsigned)P, (unsigned)rows), dim3(kTkThreads), 0, s, Y, V, L, k,
-                     cv, ci);
-  hipLaunchKernelGGL((topk_merge_kernel<K>), dim3((unsigned)rows), dim3(kTkThreads), 0, s, cv, ci, P * kTkWaves * k, k,
-                     out_val, out_idx, out_ld);
+  const int P = (int)tk_pieces(V);
+  hipLaunchKernelGGL(topk_piece_kernel, dim3((unsigned)P, (unsigned)rows), dim3(kTkThreads), 0, s, Y, V, k, cv, ci);
+  hipLaunchKernelGGL((topk_merge_kernel<K>), dim3((unsigned)rows), dim3(kTkThreads), 0, s, cv, ci,
+                     P * kTkWaves * k, k, out_val, out_idx, out_ld);
   return hipGetLastError();
 }
 
@@ -216,7 +197,7 @@ int topk_layout(const archead_dims* d, int64_t n_tokens, uint64_t* fwd_bytes, ui
   int rc = archead_workspace_bytes(d, rows, fwd_bytes);
   if (rc) return rc;
   *fwd_bytes = up256(*fwd_bytes);
-  *total = rows > 0 ? *fwd_bytes + up256((uint64_t)rows * (uint64_t)d->V * 4) + kTkCandBytes : 0;
+  *total = rows > 0 ? *fwd_bytes + up256((uint64_t)rows * (uint64_t)d->V * 4) + tk_cand_bytes(rows, d->V) : 0;
   return ARCHEAD_OK;
 }
 
@@ -250,8 +231,10 @@ int archead_logits_topk(const archead_tensor* H, const archead_packed_head* head
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* Yc = reinterpret_cast<float*>(static_cast<uint8_t*>(head->workspace) + fwd);
   const uint64_t ybytes = up256((uint64_t)(N < kTkChunkRows ? N : kTkChunkRows) * (uint64_t)d->V * 4);
+  const int64_t crow = N < kTkChunkRows ? N : kTkChunkRows;
   float* cv = reinterpret_cast<float*>(static_cast<uint8_t*>(head->workspace) + fwd + ybytes);
-  int32_t* ci = reinterpret_cast<int32_t*>(cv + kTkCandBytes / 8);
+  int32_t* ci = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(head->workspace) + fwd + ybytes +
+                                           tk_cand_bytes(crow, d->V) / 2);
   for (int64_t t0 = 0; t0 < N; t0 += kTkChunkRows) {
     const int64_t rows = N - t0 < kTkChunkRows ? N - t0 : kTkChunkRows;
     archead_tensor Hc = *H;

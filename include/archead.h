@@ -343,8 +343,9 @@ ARCHEAD_API int archead_logits_stats(const archead_tensor* H, const archead_pack
 
 /* Device workspace one archead_logits_topk call with n_tokens rows needs:
  * archead_workspace_bytes for min(n_tokens, 256) rows, rounded up to 256,
- * plus min(n_tokens, 256) x V fp32 logits rounded up to 256, plus 1 MiB
- * of first-stage candidates (0 when n_tokens = 0).  Pure host arithmetic.
+ * plus min(n_tokens, 256) x V fp32 logits rounded up to 256, plus twice
+ * min(n_tokens, 256) x ceil(V / 4096) x 256 bytes rounded up to 256 of
+ * first-stage candidates (0 when n_tokens = 0).  Pure host arithmetic.
  * E_NULL, E_DIMS, E_SHAPE. */
 ARCHEAD_API int archead_topk_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes);
 
@@ -355,8 +356,8 @@ ARCHEAD_API int archead_topk_workspace_bytes(const archead_dims* d, int64_t n_to
  * the lower index comes first, so the result is unique.  Device arrays of
  * N*k elements, 4-byte aligned.  The forward runs on `stream` in chunks of
  * 256 tokens into fp32 logits held in the workspace (the logits are read back
- * once, not returned); the selection takes the k best of each vocabulary
- * piece of a row, then the k best of those candidates.  1 <= k <= 16 (E_SHAPE below 1 or above V,
+ * once, not returned); the selection takes the k best of every 1024-element
+ * span of a row, then the k best of those candidates.  1 <= k <= 16 (E_SHAPE below 1 or above V,
  * E_UNSUPPORTED above 16); H and head as for archead_logits, the workspace
  * at least archead_topk_workspace_bytes.  N = 0 is a no-op. */
 ARCHEAD_API int archead_logits_topk(const archead_tensor* H, const archead_packed_head* head, int32_t k,

@@ -256,7 +256,7 @@ def test_topk_workspace_bytes(ah):
     for (V, D, r_c, r_r, g) in [(1024, 256, 16, 8, 64), (151936, 4096, 64, 64, 128)]:
         for N in (1, 16, 17, 256, 257, 4096):
             rows = min(N, 256)
-            want = up(ah.archead_workspace_bytes(V, D, r_c, r_r, g, rows)) + up(rows * V * 4) + (1 << 20)
+            want = up(ah.archead_workspace_bytes(V, D, r_c, r_r, g, rows)) + up(rows * V * 4) + 2 * up(rows * -(-V // 4096) * 4 * 16 * 4)
             assert ah.archead_topk_workspace_bytes(V, D, r_c, r_r, g, N) == want
     assert ah.archead_topk_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
 
