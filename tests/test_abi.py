@@ -368,6 +368,21 @@ def test_status_strings(ah):
     assert "unknown" in ah.archead_status_string(99)
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/archead.h compiles as strict C99 (the ABI is C, not C++)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use.c"
+    src.write_text('#include "archead.h"\nint main(void) { archead_fit_inputs f; archead_layout l; '
+                   '(void)f; (void)l; return ARCHEAD_FORMAT_VERSION == 1 ? 0 : 1; }\n')
+    res = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                          "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
 def test_every_kernel_has_its_host_launch_stub(ah):
     """A kernel whose host-side instantiation is dropped leaves an undefined
     launch stub behind, and the library then fails to load on a machine with a GPU."""
