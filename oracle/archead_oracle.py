@@ -26,8 +26,16 @@ Large Language Model Output Heads" (arXiv:2608.02703), Sec. 3 and Algorithm 1.
 
 Readings taken where the page leaves the format open (the bit width of Q_b,
 SC4 internals, nibble order, the tile order of the stored residual) are the
-byte format described in ``FORMAT`` below.  Every floating-point step is fp64;
+byte format described in ``FORMAT`` below.  The forward is fp64 throughout;
 all dequantised values are exact in fp64.
+
+Around the forward, each with its own section below: per-row statistics and
+top-k of the logits (the quantities of the pages' quality metrics), the
+quantisers and the core residual of the packing step (decisions in fp32, as
+their section states), the fitting steps of Algorithm 1 (damped covariance,
+metric transform, randomized SVD, correction map-back) and the logit error of
+Eq. 1.  Every function here is pinned by ``tests/test_oracle_pins.py``
+against closed forms, worked examples, library routines or brute force.
 """
 from __future__ import annotations
 
