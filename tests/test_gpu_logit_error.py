@@ -46,3 +46,20 @@ def test_logit_error_of_an_unrelated_head():
     err, ref = _gpu(inp.head, inp.H_bits, W)
     err_o, ref_o = oracle.logit_error(inp.H_bits, inp.head, W)
     assert abs(ref - ref_o) <= 1e-4 * ref_o and abs(err - err_o) <= 1e-4 * err_o
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_logit_error_full_size_batched():
+    """The batched workload (V=151936, D=4096, N=64): its seeded packed head
+    against an independent seeded dense bf16 head, every logit, against the
+    oracle's fp64 sums."""
+    cfg = synth.config("batched")
+    inp = synth.make("batched")
+    V, D = cfg["V"], cfg["D"]
+    log(f"full-size logit error V={V} D={D} N={cfg['N']}")
+    W = synth.f32_to_bf16_bits(np.random.default_rng(31).normal(0, 0.02, size=(V, D)).astype(np.float32))
+    err, ref = _gpu(inp.head, inp.H_bits, W)
+    err_o, ref_o = oracle.logit_error(inp.H_bits, inp.head, W)
+    log(f"  error {err:.6e} vs {err_o:.6e}; reference {ref:.6e} vs {ref_o:.6e}")
+    assert abs(ref - ref_o) <= 1e-4 * ref_o and abs(err - err_o) <= 1e-4 * err_o
