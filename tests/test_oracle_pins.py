@@ -770,3 +770,73 @@ def test_logit_error_pins():
     Dl = np.random.default_rng(6).normal(size=(10, 16))
     T, _ = oracle.metric_transform(oracle.damped_covariance(Hm, 0.0), 0.5)
     assert np.isclose(np.sum((Hm @ Dl.T) ** 2) / 300, oracle.metric_objective(Dl, T), rtol=1e-10)
+
+
+def _fit_case():
+    """A tiny head with a dominant rank-r_c part and calibration tokens whose
+    first channels are outliers (so the metric is far from the identity)."""
+    rng = np.random.default_rng(31)
+    V, D, r_c, r_r, g, N = 48, 128, 8, 8, 32, 400
+    W = (rng.normal(size=(V, r_c)) @ rng.normal(size=(r_c, D)) * 0.05 + rng.normal(size=(V, D)) * 0.002)
+    W = W.astype(np.float32)
+    sc = np.where(np.arange(D) < 4, 15.0, 1.0).astype(np.float32)
+    H = synth.f32_to_bf16_bits(rng.normal(size=(N, D)).astype(np.float32) * sc)
+    # V + 8 test columns for the correction: the sketch spans all of E T's
+    # column space, so the randomized SVD is exact
+    return dict(W=W, H_bits=H, r_c=r_c, r_r=r_r, g=g, p=0.75, lam=0.01,
+                omega_c=rng.normal(size=(D, r_c + 8)), omega_r=rng.normal(size=(D, V + 8)), q=1)
+
+
+def _correction_gap(case, f):
+    """(J_f / J_opt - 1, max |A_w B_w - [E T]_r T^-1| / max |[E T]_r T^-1|):
+    how far the fitted correction is from the conditional optimum, with T the
+    metric of the case's calibration tokens (computed here, not taken from f)."""
+    T, Ti = oracle.metric_transform(oracle.damped_covariance(oracle.bf16_bits_to_f64(case["H_bits"]), case["lam"]),
+                                    case["p"])
+    E = f["E"].astype(np.float64)
+    U, S, Vt = np.linalg.svd(E @ T, full_matrices=False)
+    r = case["r_r"]
+    opt = float(np.sum(S[r:] ** 2))
+    prod = f["A_w"].astype(np.float64) @ f["B_w"].astype(np.float64)
+    Jf = oracle.metric_objective(E - prod, T)
+    closed = (U[:, :r] * S[:r]) @ Vt[:r] @ Ti
+    return Jf / opt - 1.0, float(np.abs(prod - closed).max() / np.abs(closed).max())
+
+
+def test_fit_correction_reaches_the_conditional_optimum():
+    """Sec. 3.2 (conditional optimum) with the Sec. 3 metric transform and
+    Algorithm 1's map-back: for the core error E that oracle.fit leaves, the
+    rank-r_r correction it returns attains min over rank r_r of
+    ||(E - A_w B_w) T_p||_F^2 = sum_{i > r_r} sigma_i(E T_p)^2 (Eckart-Young
+    in the metric), i.e. A_w B_w = [E T_p]_{r_r} T_p^{-1}.  The test matrices
+    make the randomized SVD exact, so only the fp32 storage of the factors
+    separates the two (the objective is flat to first order at its minimum)."""
+    case = _fit_case()
+    _, f = oracle.fit(case["W"], case["H_bits"], case["r_c"], case["r_r"], case["g"], case["p"], case["lam"],
+                      case["omega_c"], case["omega_r"], case["q"])
+    dJ, dP = _correction_gap(case, f)
+    assert abs(dJ) <= 1e-6, dJ
+    assert dP <= 1e-6, dP
+
+
+@pytest.mark.parametrize("mutant", ["frobenius", "map_back_with_T", "metric_p_zero"])
+def test_fit_pin_rejects_plausible_mistakes(monkeypatch, mutant):
+    """The pin above fails for the mistakes it is there to catch, each planted
+    in the oracle on the CPU: fitting E itself (T_p = I, an ordinary low-rank
+    fix of the core error, which the pages say does not repair the loss),
+    mapping the right factor back through T_p instead of T_p^{-1}, and
+    ignoring the exponent p (T = C_lam^0)."""
+    case = _fit_case()
+    real = oracle.archead_oracle.metric_transform
+    if mutant == "frobenius":
+        fake = lambda C, p: (np.eye(C.shape[0]), np.eye(C.shape[0]))  # noqa: E731
+    elif mutant == "map_back_with_T":
+        fake = lambda C, p: (real(C, p)[0], real(C, p)[0])  # noqa: E731
+    else:
+        fake = lambda C, p: real(C, 0.0)  # noqa: E731
+    monkeypatch.setattr(oracle.archead_oracle, "metric_transform", fake)
+    _, f = oracle.fit(case["W"], case["H_bits"], case["r_c"], case["r_r"], case["g"], case["p"], case["lam"],
+                      case["omega_c"], case["omega_r"], case["q"])
+    monkeypatch.setattr(oracle.archead_oracle, "metric_transform", real)
+    dJ, dP = _correction_gap(case, f)
+    assert dJ > 1e-2 and dP > 1e-2, (mutant, dJ, dP)
