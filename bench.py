@@ -34,10 +34,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 # sources that decide each main kernel's code (a counter summary is only
 # reported while these are unchanged)
 KERNEL_SOURCES = {
-    "decode_lds_kernel": ["decode.hip", "device_common.h", "internal.h"],
     "decode_kernel": ["decode.hip", "device_common.h", "internal.h"],
-    "mid_kernel": ["mid.hip", "device_common.h", "internal.h"],
-    "tile_kernel": ["tile.hip", "device_common.h", "internal.h"],
     "tile32_kernel": ["tile.hip", "tile32.h", "rowstat.h", "device_common.h", "internal.h"],
 }
 
@@ -47,21 +44,23 @@ def log(*a):
 
 
 def algorithmic(cfg, L, N):
-    """Algorithmic bytes and flops of one forward, split as the kernels split it.
+    """Algorithmic bytes and flops of one forward.
 
-    Per vocabulary row the decode kernel must read D/2 + D/g + 2 + r + 2*nA
-    bytes of the packed head and write N logits; per call it reads the
-    converted hidden states (2*N*D) and the pre-projection (4*N*(rc32+rr32)).
-    The main contraction does 2*(D + r) flops per logit; the pre-projection
-    2*N*D*r.
+    Bytes: per vocabulary row D/2 + D/g + 2 + r + 2*nA bytes of the packed
+    head plus N logits written; per call the B factors (r*D + 2*r*D/g bytes)
+    and the bf16 hidden states (2*N*D).  That is payload_bytes + H + Y.  On the
+    decode path a small pre-projection kernel reads B and H first and the
+    streaming kernel reads the rest; the streaming kernel's figure counts the
+    whole call's bytes (B is under 0.1% of them at the decode workloads).
+    Flops: the main contraction does 2*(D + r) per logit (the tile kernel's
+    unit); the pre-projection 2*N*D*r.
     """
     V, D, g, r_c, r_r = cfg["V"], cfg["D"], cfg["g"], cfg["r_c"], cfg["r_r"]
     r = r_c + r_r
     nA = (r_c > 0) + (r_r > 0)
     ysz = 2 if cfg["y_dtype"] == "bf16" else 4
-    rc32, rr32 = -(-r_c // 32) * 32, -(-r_r // 32) * 32
     per_row = D // 2 + D // g + 2 + r + 2 * nA
-    main_bytes = V * per_row + N * V * ysz + 2 * N * D + 4 * N * (rc32 + rr32)
+    main_bytes = L["payload_bytes"] + 2 * N * D + N * V * ysz
     main_flops = 2 * N * V * (D + r)
     total_flops = main_flops + 2 * N * D * r
     return dict(per_row_bytes=per_row, main_bytes=main_bytes, main_flops=main_flops,
@@ -140,21 +139,25 @@ def pmc_summary(workload, kernel, fetch_csv, write_csv, commands):
     return out
 
 
-def dominant_kernel(N):
-    """Name of the main kernel the library launches for N tokens (automatic path)."""
-    if N <= 16:
-        return "decode_lds_kernel"
-    return "tile32_kernel"
+def dominant_kernel(cfg):
+    """Name of the main kernel the library launches for a workload (automatic
+    path): the decode kernel when the call needs no more workspace than its Z."""
+    import compressed_output_head_amd as ah
+    ws = ah.archead_workspace_bytes(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], cfg["N"])
+    tile = ah.archead_workspace_bytes_path(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], cfg["N"], 2)
+    return "decode_kernel" if ws < tile else "tile32_kernel"
 
 
-def run_workload(name, steps, warmup, path=0):
+def run_workload(name, steps, warmup, path=0, n_tokens=None):
     import torch
     import synth
     import compressed_output_head_amd as ah
 
     cfg = synth.config(name)
+    if n_tokens is not None:
+        cfg["N"] = n_tokens
     t0 = time.time()
-    inp = synth.make(name)
+    inp = synth.make(name, N=cfg["N"])
     packed = ah.archead_pack(inp.head)
     L = ah.archead_pack_layout(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"])
     heads = [ah.PackedHead(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], packed)]
@@ -197,7 +200,7 @@ def run_workload(name, steps, warmup, path=0):
         torch.cuda.synchronize()
     kms = [evb[i].elapsed_time(eve[i]) for i in range(steps)]
     A = algorithmic(cfg, L, N)
-    return dict(cfg=cfg, L=L, A=A, ms=ms, kernel=dominant_kernel(N), kernel_ms=float(np.mean(kms)),
+    return dict(cfg=cfg, L=L, A=A, ms=ms, kernel=dominant_kernel(cfg), kernel_ms=float(np.mean(kms)),
                 kernel_ms_min=float(np.min(kms)), kernel_ms_max=float(np.max(kms)),
                 kernel_ms_pct=[round(float(np.percentile(kms, q)), 5) for q in (10, 50, 90)])
 
@@ -466,6 +469,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode", help="headline workload (decode, batched, prefill, head70b)")
+    ap.add_argument("--n", type=int, default=None, help="token count of the headline workload (default: its own)")
     ap.add_argument("--secondary", default="prefill", help="second workload ('' to skip)")
     ap.add_argument("--cpu-sample-rows", type=int, default=None,
                     help="vocabulary rows the CPU oracle is timed on (default: all for decode-type "
@@ -507,7 +511,7 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
-    r = run_workload(args.config, args.steps, args.warmup)
+    r = run_workload(args.config, args.steps, args.warmup, n_tokens=args.n)
     cfg, A = r["cfg"], r["A"]
     value, unit, roof = summary(r)
     log(f"[bench] {args.config}: {r['ms'] * 1e3:.1f} us/step, {r['kernel']} {r['kernel_ms'] * 1e3:.1f} us")

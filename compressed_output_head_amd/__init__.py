@@ -22,7 +22,8 @@ ARCHEAD_BF16, ARCHEAD_F32 = 1, 2
 ARCHEAD_PATH_AUTO, ARCHEAD_PATH_DECODE, ARCHEAD_PATH_TILE = 0, 1, 2
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5: "E_SHAPE",
           6: "E_ALIGN", 7: "E_WORKSPACE", 8: "E_HIP", 9: "E_VALUE", 10: "E_SIZE"}
-EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_pack", "archead_logits",
+EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_workspace_bytes_path", "archead_pack",
+           "archead_logits",
            "archead_logits_path", "archead_logits_events", "archead_stats_workspace_bytes",
            "archead_logits_stats", "archead_quantize", "archead_topk_workspace_bytes", "archead_logits_topk",
            "archead_fit_workspace_bytes", "archead_fit", "archead_logit_error_workspace_bytes",
@@ -107,6 +108,7 @@ def _load():
     P = ctypes.POINTER
     lib.archead_pack_layout.argtypes = [P(ArcheadDims), P(ArcheadLayout)]
     lib.archead_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int64, P(ctypes.c_uint64)]
+    lib.archead_workspace_bytes_path.argtypes = [P(ArcheadDims), ctypes.c_int64, ctypes.c_int, P(ctypes.c_uint64)]
     lib.archead_pack.argtypes = [P(ArcheadDims), P(ArcheadHostComponents), ctypes.c_void_p, ctypes.c_uint64]
     lib.archead_logits.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor), ctypes.c_void_p]
     lib.archead_logits_path.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor),
@@ -173,6 +175,13 @@ def archead_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
     b = ctypes.c_uint64()
     _check(lib.archead_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
                                        ctypes.byref(b)), "archead_workspace_bytes")
+    return b.value
+
+
+def archead_workspace_bytes_path(V, D, r_c, r_r, g, n_tokens: int, path: int) -> int:
+    b = ctypes.c_uint64()
+    _check(lib.archead_workspace_bytes_path(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens), int(path),
+                                            ctypes.byref(b)), "archead_workspace_bytes_path")
     return b.value
 
 
@@ -245,11 +254,15 @@ class PackedHead:
     def dims(self):
         return dict(V=self.V, D=self.D, r_c=self.r_c, r_r=self.r_r, g=self.g)
 
-    def ensure_workspace(self, n_tokens: int, stats: bool = False, topk: bool = False, logit_error: bool = False):
+    def ensure_workspace(self, n_tokens: int, stats: bool = False, topk: bool = False, logit_error: bool = False,
+                         path: int = ARCHEAD_PATH_AUTO):
         torch = _torch()
-        size = archead_logit_error_workspace_bytes if logit_error else archead_topk_workspace_bytes if topk \
-            else archead_stats_workspace_bytes if stats else archead_workspace_bytes
-        need = size(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens)
+        if logit_error or topk or stats:
+            size = archead_logit_error_workspace_bytes if logit_error else archead_topk_workspace_bytes if topk \
+                else archead_stats_workspace_bytes
+            need = size(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens)
+        else:
+            need = archead_workspace_bytes_path(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens, path)
         if self.workspace is None or self.workspace.numel() < need:
             self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.buffer.device)
         return self.workspace
@@ -273,7 +286,7 @@ def _tensor(t) -> ArcheadTensor:
 def archead_logits_path(H, head: PackedHead, Y, path: int = ARCHEAD_PATH_AUTO, stream=None):
     """Y = H W_hat^T on the GPU.  H: bf16 [N, D]; Y: fp32 or bf16 [N, V] (written)."""
     torch = _torch()
-    head.ensure_workspace(H.shape[0])
+    head.ensure_workspace(H.shape[0], path=path)
     if stream is None:
         stream = torch.cuda.current_stream(H.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -288,7 +301,7 @@ def archead_logits_events(H, head: PackedHead, Y, path: int, ev_begin, ev_end, s
     """archead_logits_path that also records two torch.cuda.Event objects
     around the main kernel (each must have been recorded once, so it exists)."""
     torch = _torch()
-    head.ensure_workspace(H.shape[0])
+    head.ensure_workspace(H.shape[0], path=path)
     if stream is None:
         stream = torch.cuda.current_stream(H.device).cuda_stream
     h, y, p = _tensor(H), _tensor(Y), head.struct()

@@ -57,13 +57,15 @@ void compute_layout(const archead_dims* d, archead_layout* L) {
   L->payload_bytes = payload;
 }
 
-WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool stats) {
+WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool stats, uint64_t split_cap,
+                                 bool allow_decode) {
   WorkspaceLayout w{};
-  w.n16 = (int64_t)round_up((uint64_t)std::max<int64_t>(n_tokens, 0), 16);
+  const uint64_t n = (uint64_t)std::max<int64_t>(n_tokens, 0);
+  w.decode = allow_decode && decode_fits(d, n_tokens);
   w.rc32 = (int)round_up((uint64_t)d->r_c, 32);
   w.rr32 = (int)round_up((uint64_t)d->r_r, 32);
   w.zsteps = (w.rc32 + w.rr32) / 32;
-  w.n32 = (int64_t)round_up((uint64_t)std::max<int64_t>(n_tokens, 0), 32);
+  w.n32 = (int64_t)round_up(n, 32);
   const uint64_t n32 = (uint64_t)w.n32, D = (uint64_t)d->D;
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) {
@@ -71,22 +73,25 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
     off = round_up(off + bytes, ARCHEAD_ALIGNMENT);
     return at;
   };
-  w.hf = take(n32 * D * 2);
-  w.hscale = take(n32 * 4);
-  w.zf = take(n32 * (uint64_t)w.zsteps * 2 * 32 * 2);
-  w.zscale = take(n32 * 4);
-  const uint64_t nsmall = n_tokens <= kDecodeLdsTokens ? (uint64_t)std::max<int64_t>(n_tokens, 0) : 0;
-  w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
-  w.hc = take(nsmall * D * 2);
-  w.split_bytes = n_tokens > kDecodeLdsTokens ? kSplitBytes : 0;
-  w.split = take(w.split_bytes);
-  if (stats) {  // statistics pieces, and Y of a few-token call
-    const uint64_t n = (uint64_t)std::max<int64_t>(n_tokens, 0);
+  if (!w.decode) {
+    w.hf = take(n32 * D * 2);
+    w.hscale = take(n32 * 4);
+    w.zf = take(n32 * (uint64_t)w.zsteps * 2 * 32 * 2);
+    w.zscale = take(n32 * 4);
+    w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
+  } else {  // the decode path: partial sums of Z
+    w.z32 = take(decode_workspace_bytes(d, n_tokens));
+  }
+  if (stats) {  // statistics pieces, and Y of a call the decode kernel takes
     w.st_nparts = std::max<int64_t>(kStatChunks, (int64_t)(round_up((uint64_t)d->V, 16) + 255) / 256);
     w.st_part = take(n * (uint64_t)w.st_nparts * 16);
-    w.st_y = take(n <= (uint64_t)kDecodeLdsTokens ? n * (uint64_t)d->V * 4 : 0);
+    w.st_y = take(w.decode ? n * (uint64_t)d->V * 4 : 0);
   }
-  w.total = n32 ? off : 0;
+  // the partial sums of split tiles come last, so a caller with a fixed
+  // budget can give them what is left
+  w.split_bytes = w.decode ? 0 : std::min<uint64_t>(split_cap, kSplitBytes) / ARCHEAD_ALIGNMENT * ARCHEAD_ALIGNMENT;
+  w.split = take(w.split_bytes);
+  w.total = n ? off : 0;
   return w;
 }
 
@@ -143,13 +148,18 @@ int archead_pack_layout(const archead_dims* d, archead_layout* out) {
   return ARCHEAD_OK;
 }
 
-int archead_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes) {
+int archead_workspace_bytes_path(const archead_dims* d, int64_t n_tokens, int path, uint64_t* bytes) {
   if (!d || !bytes) return ARCHEAD_E_NULL;
   const int rc = check_dims(d);
   if (rc) return rc;
   if (n_tokens < 0) return ARCHEAD_E_SHAPE;
-  *bytes = workspace_layout(d, n_tokens).total;
+  if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
+  *bytes = workspace_layout(d, n_tokens, false, kSplitBytes, path != ARCHEAD_PATH_TILE).total;
   return ARCHEAD_OK;
+}
+
+int archead_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes) {
+  return archead_workspace_bytes_path(d, n_tokens, ARCHEAD_PATH_AUTO, bytes);
 }
 
 int archead_pack(const archead_dims* d, const archead_host_components* src, void* dst,
@@ -249,7 +259,7 @@ namespace {
 // Checks shared by the entry points that run kernels, then every field of
 // `a` except the output's.
 int setup_args(const archead_tensor* H, const archead_packed_head* head, bool stats, FwdArgs& a,
-               WorkspaceLayout& W) {
+               WorkspaceLayout& W, bool allow_decode = true) {
   if (!H || !head) return ARCHEAD_E_NULL;
   const archead_dims* d = &head->dims;
   int rc = check_kernel_dims(d);
@@ -259,14 +269,15 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
   if (N < 0 || H->cols != d->D || H->row_stride < d->D) return ARCHEAD_E_SHAPE;
   if (N > (int64_t(1) << 22)) return ARCHEAD_E_UNSUPPORTED;
   if (N == 0) return ARCHEAD_OK;
-  if (!H->data || !head->buffer || !head->workspace) return ARCHEAD_E_NULL;
+  if (!H->data || !head->buffer) return ARCHEAD_E_NULL;
   if ((uintptr_t)head->buffer % ARCHEAD_ALIGNMENT || (uintptr_t)head->workspace % ARCHEAD_ALIGNMENT)
     return ARCHEAD_E_ALIGN;
   if ((uintptr_t)H->data % 16 || (H->row_stride * 2) % 16) return ARCHEAD_E_ALIGN;
   archead_layout L;
   compute_layout(d, &L);
   if (head->buffer_bytes < L.total_bytes) return ARCHEAD_E_SIZE;
-  W = workspace_layout(d, N, stats);
+  W = workspace_layout(d, N, stats, kSplitBytes, allow_decode);
+  if (W.total > 0 && !head->workspace) return ARCHEAD_E_NULL;
   if (head->workspace_bytes < W.total) return ARCHEAD_E_WORKSPACE;
 
   const uint8_t* buf = static_cast<const uint8_t*>(head->buffer);
@@ -275,7 +286,6 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
   a.V = d->V;
   a.D = d->D;
   a.N = N;
-  a.n16 = W.n16;
   a.n32 = W.n32;
   a.nb = L.padded_rows / 16;
   a.r_c = d->r_c;
@@ -302,7 +312,6 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
   a.zf = reinterpret_cast<_Float16*>(ws + W.zf);
   a.zscale = reinterpret_cast<float*>(ws + W.zscale);
   a.z32 = reinterpret_cast<float*>(ws + W.z32);
-  a.hc = reinterpret_cast<_Float16*>(ws + W.hc);
   a.part = W.split_bytes ? reinterpret_cast<float*>(ws + W.split) : nullptr;
   a.part_bytes = W.split_bytes;
   if (stats) {
@@ -326,10 +335,9 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   if (Y->dtype != ARCHEAD_F32 && Y->dtype != ARCHEAD_BF16) return ARCHEAD_E_DTYPE;
   const int64_t N = H->rows;
   if (Y->cols != head->dims.V || Y->rows != N || Y->row_stride < head->dims.V) return ARCHEAD_E_SHAPE;
-  if (path == ARCHEAD_PATH_DECODE && N > kDecodeMaxTokens) return ARCHEAD_E_UNSUPPORTED;
   FwdArgs a;
   WorkspaceLayout W;
-  int rc = setup_args(H, head, false, a, W);
+  int rc = setup_args(H, head, false, a, W, path != ARCHEAD_PATH_TILE);
   if (rc || N == 0) return rc;
   const int ysz = Y->dtype == ARCHEAD_F32 ? 4 : 2;
   if (!Y->data) return ARCHEAD_E_NULL;
@@ -339,22 +347,18 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   a.y_bf16 = Y->dtype == ARCHEAD_BF16;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // auto: the decode kernel when it takes the call, else the tile path; the
+  // caller may force either (a forced decode path it does not take is an error)
+  const bool decode = W.decode;
+  if (path == ARCHEAD_PATH_DECODE && !decode) return ARCHEAD_E_UNSUPPORTED;
+  // the decode kernel stores Y through 32-bit offsets
+  if (decode && (uint64_t)(N - 1) * (uint64_t)Y->row_stride * ysz + (uint64_t)head->dims.V * ysz >= (1ull << 32))
+    return ARCHEAD_E_UNSUPPORTED;
+  if (!decode && !tile32_eligible(a)) return ARCHEAD_E_UNSUPPORTED;
   (void)hipGetLastError();  // start from a clean error state
-  // auto: the LDS decode kernel for a few tokens, else the tile path.
-  // decode path: the LDS kernel when it applies, else the batched kernel (the
-  // 16-row decode kernel only when offsets exceed 32 bits); tile path: the
-  // 32-row kernel unless offsets exceed 32 bits (launch_tile decides the same way)
-  const bool small = (path == ARCHEAD_PATH_DECODE || (path == ARCHEAD_PATH_AUTO && N <= kDecodeMaxTokens)) &&
-                     decode_lds_eligible(a);
-  const bool decode = path == ARCHEAD_PATH_DECODE || small;
-  const bool mid = decode && !small && mid_eligible(a);
-  const bool rows32 = mid || (!decode && tile32_eligible(a));
-  if ((small ? launch_prep_z(a, s) : launch_prep(a, rows32, s)) != hipSuccess) return ARCHEAD_E_HIP;
+  if ((decode ? launch_decode_prep(a, s) : launch_prep(a, s)) != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return ARCHEAD_E_HIP;
-  const hipError_t e = small ? launch_decode_lds(a, s)
-                       : mid ? launch_mid(a, s)
-                       : decode ? launch_decode(a, s)
-                                : launch_tile(a, s);
+  const hipError_t e = decode ? launch_decode(a, s) : launch_tile(a, s);
   if (e != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
   return ARCHEAD_OK;
@@ -394,19 +398,19 @@ int archead_logits_stats(const archead_tensor* H, const archead_packed_head* hea
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
   hipError_t e;
-  if (decode_lds_eligible(a)) {
+  if (W.decode) {
     // a few tokens: Y (at most 16 rows) into the workspace, then its pieces
     float* Yw = reinterpret_cast<float*>(static_cast<uint8_t*>(head->workspace) + W.st_y);
     a.Y = Yw;
     a.Y_stride = a.V;
     a.y_bf16 = 0;
     a.st_nparts = kStatChunks;
-    e = launch_prep_z(a, s);
-    if (e == hipSuccess) e = launch_decode_lds(a, s);
+    e = launch_decode_prep(a, s);
+    if (e == hipSuccess) e = launch_decode(a, s);
     if (e == hipSuccess) e = launch_rowstats_y(a, Yw, a.V, s);
   } else if (tile32_eligible(a)) {
     a.st_nparts = tile_stat_parts(a);
-    e = launch_prep(a, true, s);
+    e = launch_prep(a, s);
     if (e == hipSuccess) e = launch_tile_stats(a, s);
   } else {
     return ARCHEAD_E_UNSUPPORTED;

@@ -51,7 +51,8 @@ typedef enum {
   ARCHEAD_E_NULL = 1,        /* a required pointer is NULL                        */
   ARCHEAD_E_DIMS = 2,        /* dims are invalid (V<1, D not a multiple of 128, D % g != 0, rank < 0) */
   ARCHEAD_E_UNSUPPORTED = 3, /* valid but not implemented (g not in {32,64,128,256}, rank not a multiple of 8,
-                                rank above 1024, forced decode path with more than 64 tokens) */
+                                rank above 1024, a forced decode path the decode kernel does not take,
+                                section offsets past 32 bits) */
   ARCHEAD_E_DTYPE = 4,       /* H is not bf16, or Y is neither fp32 nor bf16       */
   ARCHEAD_E_SHAPE = 5,       /* H.cols != D, Y.cols != V, Y.rows != H.rows, bad strides */
   ARCHEAD_E_ALIGN = 6,       /* buffer/workspace not 256-byte aligned, H rows not 16-byte aligned,
@@ -65,9 +66,13 @@ typedef enum {
 typedef enum { ARCHEAD_BF16 = 1, ARCHEAD_F32 = 2 } archead_dtype;
 
 typedef enum {
-  ARCHEAD_PATH_AUTO = 0,   /* up to 16 tokens whose H and Z fit LDS: decode path; else tile path */
-  ARCHEAD_PATH_DECODE = 1, /* skinny path (streams the head once for all N <= 64 tokens) */
-  ARCHEAD_PATH_TILE = 2    /* LDS-tiled MFMA path (any N)                          */
+  ARCHEAD_PATH_AUTO = 0,   /* the decode path when it takes the call, else the tile path */
+  ARCHEAD_PATH_DECODE = 1, /* one kernel that streams the head once for up to 16 tokens whose
+                              converted H fits the 160 KiB of LDS of a workgroup
+                              (N <= 16 at D = 4096, N <= 8 at D = 8192), with
+                              N (r_c + r_r) <= 2048, round_up(r_c, 32) +
+                              round_up(r_r, 32) <= 256 and D/g <= 128 */
+  ARCHEAD_PATH_TILE = 2    /* LDS-tiled MFMA path (any N); needs the workspace    */
 } archead_path;
 
 /* Shape of a packed head (Algorithm 1 inputs: vocabulary V, hidden size D,
@@ -150,12 +155,20 @@ typedef struct {
  * no HIP call.  E_NULL, E_DIMS. */
 ARCHEAD_API int archead_pack_layout(const archead_dims* d, archead_layout* out);
 
-/* Device workspace one archead_logits call with n_tokens rows of H needs
- * (converted hidden states, the low-rank pre-projection and per-token scales;
- * above 16 tokens also 64 MiB for partial sums of output tiles whose hidden
- * dimension is split over several workgroups).
- * Pure host arithmetic.  E_NULL, E_DIMS. */
+/* Device workspace one archead_logits call with n_tokens rows of H needs on
+ * the automatic path: when the decode path takes the call, the partial sums of
+ * the pre-projection (n_tokens (r_c + r_r) zst fp32, zst = ceil(D / 1024)
+ * rounded up to a multiple of 4; 0 when r_c + r_r = 0, and the workspace
+ * pointer may then be NULL); on the tile path the converted hidden states,
+ * the low-rank pre-projection, per-token scales and 64 MiB for partial sums
+ * of output tiles whose hidden dimension is split over several workgroups.
+ * Pure host arithmetic.  E_NULL, E_DIMS, E_SHAPE (n_tokens < 0). */
 ARCHEAD_API int archead_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes);
+
+/* Same for a call with the path chosen by the caller (archead_path):
+ * ARCHEAD_PATH_TILE always needs the tile path's workspace.  E_NULL, E_DIMS,
+ * E_SHAPE, E_UNSUPPORTED (unknown path). */
+ARCHEAD_API int archead_workspace_bytes_path(const archead_dims* d, int64_t n_tokens, int path, uint64_t* bytes);
 
 /* Serialise host components into `dst` (host memory, dst_bytes >=
  * layout.total_bytes), writing every byte of the layout including padding.
@@ -285,23 +298,29 @@ ARCHEAD_API int archead_logit_error(const archead_tensor* H, const archead_packe
  *   Y: fp32 or bf16 [N][V] device tensor, written completely (every element
  *      once); bf16 output is rounded to nearest even from the fp32 result.
  *   stream: a hipStream_t (NULL = the default stream).
- * Enqueues the pre-projection kernels and then the decode path (up to 16
- * tokens whose H and Z fit LDS) or the tile path on `stream` and returns
- * without synchronising.
+ * Enqueues the decode path (up to 16 tokens whose converted H and Z fit
+ * LDS: a small pre-projection kernel, then one kernel that streams the head)
+ * or the tile path (pre-projection kernels, then the tile kernel) on `stream`
+ * and returns without synchronising.
  * N = 0 is a no-op that returns ARCHEAD_OK.  Faults inside kernels surface at
  * the caller's next synchronisation with the stream. */
 ARCHEAD_API int archead_logits(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y,
                    void* stream);
 
 /* Same as archead_logits with the path chosen by the caller (archead_path).
- * ARCHEAD_PATH_DECODE requires N <= 64.  Both paths compute the same Y. */
+ * ARCHEAD_PATH_DECODE gives E_UNSUPPORTED for a call the decode kernel does
+ * not take; ARCHEAD_PATH_TILE needs archead_workspace_bytes_path(.., TILE).
+ * A decode-path call (automatic or forced) whose N rows of Y span 4 GiB or
+ * more gives E_UNSUPPORTED (that kernel stores through 32-bit offsets).
+ * Both paths compute the same Y up to fp32 summation order. */
 ARCHEAD_API int archead_logits_path(const archead_tensor* H, const archead_packed_head* head,
                         archead_tensor* Y, int path, void* stream);
 
 /* Same as archead_logits_path, and records the caller's events ev_begin and
  * ev_end (hipEvent_t handles, either may be NULL) on `stream` immediately
- * before and after the main kernel (decode or tile), after the pre-projection
- * kernels.  For timing the dominant kernel on the stream it runs on. */
+ * before and after the main kernel (decode or tile), after either path's
+ * pre-projection kernels.  For timing the dominant kernel on the stream it
+ * runs on. */
 ARCHEAD_API int archead_logits_events(const archead_tensor* H, const archead_packed_head* head,
                                       archead_tensor* Y, int path, void* stream, void* ev_begin,
                                       void* ev_end);

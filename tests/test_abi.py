@@ -103,19 +103,37 @@ def test_layout_dims_errors(ah):
     assert ah.lib.archead_pack_layout(ctypes.byref(ah.ArcheadDims(16, 256, 0, 0, 64)), None) == 1
 
 
-def test_workspace_bytes(ah):
-    # hf (N32*D*2) | hscale (N32*4) | zf (N32*2*(rc32+rr32)*2) | zscale (N32*4) |
-    # z32 (N32*r*4) | hc (N*D*2), only for N <= 16 | split-tile partial sums
-    # (64 MiB), only for N > 16; each 256-aligned
+def _tile_workspace(V, D, r_c, r_r, g, N):
+    """hf (N32*D*2) | hscale (N32*4) | zf (N32*2*(rc32+rr32)*2) | zscale (N32*4) |
+    z32 (N32*r*4) | split-tile partial sums (64 MiB); each 256-aligned."""
     up = lambda x: (x + 255) // 256 * 256
-    for (V, D, r_c, r_r, g), N in [((1024, 256, 16, 8, 64), 4), ((151936, 4096, 32, 32, 128), 1),
-                                   ((151936, 4096, 64, 64, 128), 4096), ((64, 128, 0, 0, 32), 17)]:
-        n32 = (N + 31) // 32 * 32
-        rc32, rr32 = (r_c + 31) // 32 * 32, (r_r + 31) // 32 * 32
-        want = (up(n32 * D * 2) + up(n32 * 4) + up(n32 * 2 * (rc32 + rr32) * 2) + up(n32 * 4) +
-                up(n32 * (r_c + r_r) * 4) + up(N * D * 2 if N <= 16 else 0) + (64 << 20 if N > 16 else 0))
-        assert ah.archead_workspace_bytes(V, D, r_c, r_r, g, N) == want
+    n32 = (N + 31) // 32 * 32
+    rc32, rr32 = (r_c + 31) // 32 * 32, (r_r + 31) // 32 * 32
+    return (up(n32 * D * 2) + up(n32 * 4) + up(n32 * 2 * (rc32 + rr32) * 2) + up(n32 * 4) +
+            up(n32 * (r_c + r_r) * 4) + (64 << 20))
+
+
+def test_workspace_bytes(ah):
+    # calls the decode kernel takes (up to 16 tokens whose H fits its LDS,
+    # 32-rank steps rc32 + rr32 <= 256) need the partial sums of Z; the tile
+    # path needs its operand fragments and the split-tile partial sums
+    for (V, D, r_c, r_r, g), N, decode in [((1024, 256, 16, 8, 64), 4, True), ((151936, 4096, 32, 32, 128), 1, True),
+                                           ((1024, 256, 64, 96, 64), 4, True), ((1024, 256, 64, 96, 64), 16, True),
+                                           ((1024, 256, 129, 128, 64), 1, False),
+                                           ((151936, 4096, 32, 32, 128), 16, True),
+                                           ((128256, 8192, 64, 64, 128), 8, True),
+                                           ((128256, 8192, 64, 64, 128), 9, False),
+                                           ((151936, 4096, 64, 64, 128), 4096, False), ((64, 128, 0, 0, 32), 17, False)]:
+        up = lambda x: (x + 255) // 256 * 256
+        zst = (-(-(D // 128) // 8) + 3) // 4 * 4  # Z partial sums per element: slices of 8 k-tiles, padded to 4
+        want = up(N * (r_c + r_r) * zst * 4) if decode else _tile_workspace(V, D, r_c, r_r, g, N)
+        assert ah.archead_workspace_bytes(V, D, r_c, r_r, g, N) == want, (V, D, N)
+        assert ah.archead_workspace_bytes_path(V, D, r_c, r_r, g, N, 0) == want
+        assert ah.archead_workspace_bytes_path(V, D, r_c, r_r, g, N, 1) == want
+        assert ah.archead_workspace_bytes_path(V, D, r_c, r_r, g, N, 2) == _tile_workspace(V, D, r_c, r_r, g, N)
     assert ah.archead_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
+    with pytest.raises(ah.ArcheadError):
+        ah.archead_workspace_bytes_path(1024, 256, 16, 8, 64, 4, 3)
 
 
 # ------------------------------------------------ argument checks of logits ---
@@ -159,16 +177,20 @@ def test_logits_error_paths(ah):
     H, P, Y, need, total = _args(ah, r_r=2048); cases.append((H, P, Y, 0, 3))         # rank cap
     H, P, Y, need, total = _args(ah, V=0); cases.append((H, P, Y, 0, 2))
     H, P, Y, need, total = _args(ah); cases.append((H, P, Y, 7, 3))                    # bad path
-    H, P, Y, need, total = _args(ah, N=65); cases.append((H, P, Y, 1, 3))             # decode > 64
+    H, P, Y, need, total = _args(ah, N=17); cases.append((H, P, Y, 1, 3))             # decode kernel: <= 16
+    H, P, Y, need, total = _args(ah, N=9, V=128256, D=8192, r_c=64, r_r=64, g=128)
+    cases.append((H, P, Y, 1, 3))                                                       # ... whose H fits LDS
     H, P, Y, need, total = _args(ah); H.data = None; cases.append((H, P, Y, 0, 1))
-    H, P, Y, need, total = _args(ah); P.workspace = None; cases.append((H, P, Y, 0, 1))
+    H, P, Y, need, total = _args(ah); P.workspace = None; cases.append((H, P, Y, 2, 1))  # the tile path needs one
+    H, P, Y, need, total = _args(ah, N=20); P.workspace = None; cases.append((H, P, Y, 0, 1))
     H, P, Y, need, total = _args(ah); P.buffer = FAKE + 16; cases.append((H, P, Y, 0, 6))
     H, P, Y, need, total = _args(ah); P.workspace = FAKE + 128; cases.append((H, P, Y, 0, 6))
     H, P, Y, need, total = _args(ah); H.data = FAKE + 2; cases.append((H, P, Y, 0, 6))
     H, P, Y, need, total = _args(ah); H.row_stride = 260; cases.append((H, P, Y, 0, 6))  # 520-byte rows
     H, P, Y, need, total = _args(ah); Y.data = FAKE + 2; cases.append((H, P, Y, 0, 6))   # fp32 Y at 2 mod 4
     H, P, Y, need, total = _args(ah, buf=100); cases.append((H, P, Y, 0, 10))
-    H, P, Y, need, total = _args(ah, ws=1); cases.append((H, P, Y, 0, 7))
+    H, P, Y, need, total = _args(ah, ws=1); cases.append((H, P, Y, 2, 7))             # tile path: too small
+    H, P, Y, need, total = _args(ah, N=20, ws=1); cases.append((H, P, Y, 0, 7))
     H, P, Y, need, total = _args(ah, N=4096, V=151936, D=4096, r_c=64, r_r=64, g=128, ydt=1, ws=12345)
     cases.append((H, P, Y, 2, 7))
     for i, (H, P, Y, path, want) in enumerate(cases):
@@ -177,7 +199,7 @@ def test_logits_error_paths(ah):
 
 def test_stats_workspace_bytes(ah):
     # the logits workspace, then statistics pieces (N * max(64, ceil(V16/256)) * 16 B)
-    # and, for N <= 16, Y in fp32 (N * V * 4 B); each 256-aligned
+    # and, for calls the decode kernel takes, Y in fp32 (N * V * 4 B); each 256-aligned
     up = lambda x: (x + 255) // 256 * 256
     for (V, D, r_c, r_r, g), N in [((1024, 256, 16, 8, 64), 4), ((151936, 4096, 32, 32, 128), 1),
                                    ((151936, 4096, 64, 64, 128), 4096), ((64, 128, 0, 0, 32), 17)]:
@@ -349,6 +371,16 @@ def test_logit_error_workspace_and_errors(ah):
     H, P, W = args(); P.workspace_bytes -= 1; assert call(H, P, W) == 7
     H, P, W = args(); H.rows = 0; H.data = None; P.workspace = None; sums[0] = 5.0
     assert call(H, P, W) == 0 and sums[0] == 0.0
+
+
+def test_logits_offsets_past_32_bits_are_unsupported(ah):
+    """A head whose residual section reaches 4 GiB (V = 2^21 rows of D = 4096)
+    is refused on every path before any HIP call: the kernels address every
+    section with 32-bit offsets."""
+    for path in (0, 1, 2):
+        H, P, Y, need, total = _args(ah, N=1, V=1 << 21, D=4096, r_c=0, r_r=0, g=128)
+        P.workspace_bytes = ah.archead_workspace_bytes_path(1 << 21, 4096, 0, 0, 128, 1, 2)
+        assert _call(ah, H, P, Y, path) == 3, path
 
 
 def test_logits_zero_tokens_is_a_noop(ah):

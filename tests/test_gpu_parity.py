@@ -42,14 +42,14 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("shape", SHAPES)
-@pytest.mark.parametrize("N", [1, 2, 3, 17, 63, 64, 65, 130])
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 16, 17, 63, 64, 65, 130])
 def test_shapes_and_ragged_tails(shape, N):
     V, D, r_c, r_r, g = shape
     log(f"shape V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N}")
     inp = synth.make("tiny", seed=V + N, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=4)
     head = _head(inp)
     Yr = oracle.logits(inp.H_bits, inp.head)
-    paths = (DECODE, TILE) if N <= 64 else (TILE,)
+    paths = (DECODE, TILE) if N <= 16 else (TILE,)
     outs = {}
     for path in paths:
         outs[path] = to_f64(run(head, inp.H_bits, path))
@@ -58,6 +58,30 @@ def test_shapes_and_ragged_tails(shape, N):
     # and must give the same bits as the path it takes
     auto = to_f64(run(head, inp.H_bits, 0))
     assert np.array_equal(auto, outs[DECODE if N <= 16 else TILE])
+    if N > 16:  # the decode kernel takes at most 16 tokens: a forced decode path is refused
+        with pytest.raises(ah_mod().ArcheadError, match="UNSUPPORTED"):
+            run(head, inp.H_bits, DECODE)
+
+
+# More groups per row than the tile kernel's group-code table holds (D/g > 64):
+# the decode kernel reads the group codes with every tile and takes them; the
+# tile path refuses them.
+MANY_GROUPS = [(1000, 4096, 16, 16, 32), (600, 8192, 16, 8, 64)]
+
+
+@pytest.mark.parametrize("shape", MANY_GROUPS)
+@pytest.mark.parametrize("N", [1, 7, 8])
+def test_many_groups_per_row_decode(shape, N):
+    V, D, r_c, r_r, g = shape
+    log(f"many groups V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N}")
+    inp = synth.make("tiny", seed=V + N + g, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=4)
+    head = _head(inp)
+    Yr = oracle.logits(inp.H_bits, inp.head)
+    Yd = to_f64(run(head, inp.H_bits, DECODE))
+    check_parity(Yd, Yr, "decode")
+    assert np.array_equal(to_f64(run(head, inp.H_bits, 0)), Yd)
+    with pytest.raises(ah_mod().ArcheadError, match="UNSUPPORTED"):
+        run(head, inp.H_bits, TILE)
 
 
 LARGE_N_SHAPES = [
@@ -90,7 +114,8 @@ def test_large_n_tiles(shape, N):
 def test_one_hot_rows_recover_weights_bit_exactly(path, g, rows):
     """H = unit rows e_k, r_c = r_r = 0: Y[n, v] = q4[v,k] * c8[v,k//g] * s_R[v],
     a single product of exact operands, so the GPU must return it exactly.
-    256 rows take the large-N kernel, 64 rows the small-N ones."""
+    The tile path takes 64 or 256 rows per call (its two token-tile sizes),
+    the decode kernel 16 per call (64 rows in four calls)."""
     V, D = 300, 512
     inp = synth.make("tiny", seed=g, V=V, D=D, N=1, r_c=0, r_r=0, g=g)
     h = inp.head
@@ -111,7 +136,8 @@ def test_one_hot_rows_recover_weights_bit_exactly(path, g, rows):
     eye[np.arange(ks.size), ks] = 1.0
     Hb = synth.f32_to_bf16_bits(eye)
     head = _head(inp)
-    Y = run(head, Hb, path).cpu().numpy()
+    step = 16 if path == DECODE else ks.size
+    Y = np.concatenate([run(head, Hb[i:i + step], path).cpu().numpy() for i in range(0, ks.size, step)])
     R = oracle.dequant_R(h.q4, h.c8, h.s_R, g)          # exact in fp64 and fp32
     want = R[:, ks].T.astype(np.float32)
     # value equality (+0 and -0 are the same weight); no NaN anywhere
@@ -152,19 +178,19 @@ def test_hidden_state_edge_values(path):
         assert err <= 2e-3 * scale or (scale == 0 and err == 0), (n, err, scale)
 
 
-@pytest.mark.parametrize("path", [DECODE, TILE])
-def test_deterministic(path):
-    inp = synth.make("tiny", seed=3, V=2000, D=512, N=33, r_c=16, r_r=16, g=128)
+@pytest.mark.parametrize("path,N", [(DECODE, 13), (TILE, 33)])
+def test_deterministic(path, N):
+    inp = synth.make("tiny", seed=3, V=2000, D=512, N=N, r_c=16, r_r=16, g=128)
     head = _head(inp)
     a = run(head, inp.H_bits, path).cpu().numpy()
     b = run(head, inp.H_bits, path).cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("path", [DECODE, TILE])
-def test_bf16_output_is_rounded_fp32_output(path):
+@pytest.mark.parametrize("path,N", [(DECODE, 12), (TILE, 20)])
+def test_bf16_output_is_rounded_fp32_output(path, N):
     torch = torch_mod()
-    inp = synth.make("tiny", seed=11, V=1500, D=256, N=20, r_c=16, r_r=8, g=64)
+    inp = synth.make("tiny", seed=11, V=1500, D=256, N=N, r_c=16, r_r=8, g=64)
     head = _head(inp)
     y32 = run(head, inp.H_bits, path, "f32")
     y16 = run(head, inp.H_bits, path, "bf16")
