@@ -23,7 +23,7 @@ ARCHEAD_PATH_AUTO, ARCHEAD_PATH_DECODE, ARCHEAD_PATH_TILE = 0, 1, 2
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5: "E_SHAPE",
           6: "E_ALIGN", 7: "E_WORKSPACE", 8: "E_HIP", 9: "E_VALUE", 10: "E_SIZE"}
 EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_workspace_bytes_path", "archead_pack",
-           "archead_logits",
+           "archead_logits", "archead_logits_noalloc",
            "archead_logits_path", "archead_logits_events", "archead_stats_workspace_bytes",
            "archead_logits_stats", "archead_quantize", "archead_topk_workspace_bytes", "archead_logits_topk",
            "archead_fit_workspace_bytes", "archead_fit", "archead_logit_error_workspace_bytes",
@@ -111,6 +111,7 @@ def _load():
     lib.archead_workspace_bytes_path.argtypes = [P(ArcheadDims), ctypes.c_int64, ctypes.c_int, P(ctypes.c_uint64)]
     lib.archead_pack.argtypes = [P(ArcheadDims), P(ArcheadHostComponents), ctypes.c_void_p, ctypes.c_uint64]
     lib.archead_logits.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor), ctypes.c_void_p]
+    lib.archead_logits_noalloc.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor), ctypes.c_void_p]
     lib.archead_logits_path.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor),
                                         ctypes.c_int, ctypes.c_void_p]
     lib.archead_logits_events.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor),
@@ -313,6 +314,24 @@ def archead_logits_events(H, head: PackedHead, Y, path: int, ev_begin, ev_end, s
 
 def archead_logits(H, head: PackedHead, Y, stream=None):
     return archead_logits_path(H, head, Y, ARCHEAD_PATH_AUTO, stream)
+
+
+# workspace the library holds per GPU for archead_logits_noalloc
+ARCHEAD_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def archead_logits_noalloc(H, head: PackedHead, Y, stream=None):
+    """archead_logits with the library's own per-GPU workspace: allocates
+    nothing (head's workspace is neither allocated nor used)."""
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(H.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    h, y, p = _tensor(H), _tensor(Y), head.struct()
+    _check(lib.archead_logits_noalloc(ctypes.byref(h), ctypes.byref(p), ctypes.byref(y), ctypes.c_void_p(stream)),
+           "archead_logits_noalloc")
+    return Y
 
 
 def logits(H, head: PackedHead, out_dtype=None, path: int = ARCHEAD_PATH_AUTO):

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -253,13 +254,23 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
 
 }  // extern "C"
 
+// The workspace of archead_logits_noalloc: one array per GPU (each device
+// holds its own copy of this code object's data), kept until the process
+// ends.  Host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device: on the host the array's name is not a
+// device address.
+namespace archead {
+constexpr uint64_t kNoAllocScratchBytes = ARCHEAD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+}  // namespace archead
+
 namespace archead {
 namespace {
 
 // Checks shared by the entry points that run kernels, then every field of
 // `a` except the output's.
 int setup_args(const archead_tensor* H, const archead_packed_head* head, bool stats, FwdArgs& a,
-               WorkspaceLayout& W, bool allow_decode = true) {
+               WorkspaceLayout& W, bool allow_decode = true, uint64_t split_cap = kSplitBytes) {
   if (!H || !head) return ARCHEAD_E_NULL;
   const archead_dims* d = &head->dims;
   int rc = check_kernel_dims(d);
@@ -276,7 +287,7 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
   archead_layout L;
   compute_layout(d, &L);
   if (head->buffer_bytes < L.total_bytes) return ARCHEAD_E_SIZE;
-  W = workspace_layout(d, N, stats, kSplitBytes, allow_decode);
+  W = workspace_layout(d, N, stats, split_cap, allow_decode);
   if (W.total > 0 && !head->workspace) return ARCHEAD_E_NULL;
   if (head->workspace_bytes < W.total) return ARCHEAD_E_WORKSPACE;
 
@@ -321,13 +332,10 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
   return ARCHEAD_OK;
 }
 
-}  // namespace
-}  // namespace archead
-
-extern "C" {
-
-int archead_logits_events(const archead_tensor* H, const archead_packed_head* head,
-                          archead_tensor* Y, int path, void* stream, void* ev_begin, void* ev_end) {
+// Y = H W_hat^T on the path `path`, with the split-tile partial sums capped
+// at split_cap bytes of the workspace.
+int logits_impl(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y, int path,
+                void* stream, void* ev_begin, void* ev_end, uint64_t split_cap) {
   if (!H || !head || !Y) return ARCHEAD_E_NULL;
   if (int rc0 = check_kernel_dims(&head->dims)) return rc0;
   if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
@@ -337,7 +345,7 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   if (Y->cols != head->dims.V || Y->rows != N || Y->row_stride < head->dims.V) return ARCHEAD_E_SHAPE;
   FwdArgs a;
   WorkspaceLayout W;
-  int rc = setup_args(H, head, false, a, W, path != ARCHEAD_PATH_TILE);
+  int rc = setup_args(H, head, false, a, W, path != ARCHEAD_PATH_TILE, split_cap);
   if (rc || N == 0) return rc;
   const int ysz = Y->dtype == ARCHEAD_F32 ? 4 : 2;
   if (!Y->data) return ARCHEAD_E_NULL;
@@ -362,6 +370,53 @@ int archead_logits_events(const archead_tensor* H, const archead_packed_head* he
   if (e != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
   return ARCHEAD_OK;
+}
+
+constexpr int kMaxDevices = 64;
+// ---- allocation-free variant: the scratch address of each device ---------------
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch (looked up once per device).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ARCHEAD_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ARCHEAD_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ARCHEAD_OK;
+}
+
+}  // namespace
+}  // namespace archead
+
+extern "C" {
+
+int archead_logits_events(const archead_tensor* H, const archead_packed_head* head,
+                          archead_tensor* Y, int path, void* stream, void* ev_begin, void* ev_end) {
+  return logits_impl(H, head, Y, path, stream, ev_begin, ev_end, kSplitBytes);
+}
+
+int archead_logits_noalloc(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y,
+                           void* stream) {
+  if (!H || !head || !Y) return ARCHEAD_E_NULL;
+  if (int rc = check_kernel_dims(&head->dims)) return rc;
+  if (H->rows < 0) return ARCHEAD_E_SHAPE;
+  if (H->rows == 0) return ARCHEAD_OK;
+  // the call's workspace without split-tile partial sums must fit; whatever
+  // is left goes to them (the tile kernel splits no tile it has no room for)
+  const uint64_t need = workspace_layout(&head->dims, H->rows, false, 0, true).total;
+  if (need > kNoAllocScratchBytes) return ARCHEAD_E_WORKSPACE;
+  void* ws = nullptr;
+  if (int rc = scratch_address(&ws)) return rc;
+  archead_packed_head h = *head;
+  h.workspace = ws;
+  h.workspace_bytes = kNoAllocScratchBytes;
+  return logits_impl(H, &h, Y, ARCHEAD_PATH_AUTO, stream, nullptr, nullptr, kNoAllocScratchBytes - need);
 }
 
 int archead_logits_path(const archead_tensor* H, const archead_packed_head* head,

@@ -307,6 +307,23 @@ ARCHEAD_API int archead_logit_error(const archead_tensor* H, const archead_packe
 ARCHEAD_API int archead_logits(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y,
                    void* stream);
 
+/* Y = H W_hat^T exactly as archead_logits (automatic path), for callers that
+ * cannot allocate device memory or call hipMalloc (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * workspace comes from an array of ARCHEAD_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends; head->workspace
+ * and head->workspace_bytes are ignored.  Calls whose workspace (without the
+ * optional split-tile partial sums, which get whatever is left) exceeds it
+ * give E_WORKSPACE before anything is enqueued: at D = 4096, r_c = r_r = 64
+ * that is past about 1790 tokens (960 at D = 8192).  Allocates nothing and calls no allocating
+ * routine; the first call on a device looks the array's address up.  Every
+ * call on one GPU uses the same array and nothing in it needs to start at
+ * zero: calls that overlap on one GPU (other streams, other threads) race and
+ * give undefined results.  Other arguments and errors as archead_logits. */
+#define ARCHEAD_NOALLOC_SCRATCH_BYTES (16ull << 20)
+ARCHEAD_API int archead_logits_noalloc(const archead_tensor* H, const archead_packed_head* head,
+                                       archead_tensor* Y, void* stream);
+
 /* Same as archead_logits with the path chosen by the caller (archead_path).
  * ARCHEAD_PATH_DECODE gives E_UNSUPPORTED for a call the decode kernel does
  * not take; ARCHEAD_PATH_TILE needs archead_workspace_bytes_path(.., TILE).
