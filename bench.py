@@ -35,6 +35,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 # reported while these are unchanged)
 KERNEL_SOURCES = {
     "decode_kernel": ["decode.hip", "device_common.h", "internal.h"],
+    "small_decode_kernel": ["decode_small.hip", "device_common.h", "internal.h"],
     "tile32_kernel": ["tile.hip", "tile32.h", "rowstat.h", "device_common.h", "internal.h"],
 }
 
@@ -139,16 +140,23 @@ def pmc_summary(workload, kernel, fetch_csv, write_csv, commands):
     return out
 
 
-def dominant_kernel(cfg):
-    """Name of the main kernel the library launches for a workload (automatic
-    path): the decode kernel when the call needs no more workspace than its Z."""
+def dominant_kernel(cfg, n_rows=None, path=0):
+    """Name of the main kernel the library launches for a call of n_rows
+    (default: all N) tokens of a workload on `path`."""
     import compressed_output_head_amd as ah
-    ws = ah.archead_workspace_bytes(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], cfg["N"])
-    tile = ah.archead_workspace_bytes_path(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], cfg["N"], 2)
-    return "decode_kernel" if ws < tile else "tile32_kernel"
+    return ah.archead_main_kernel(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"],
+                                  cfg["N"] if n_rows is None else n_rows, path)
 
 
-def run_workload(name, steps, warmup, path=0, n_tokens=None):
+# workloads whose logits are written in row chunks, one call per chunk into
+# one reused buffer (the prefill workload: 512-row chunks of bf16 logits)
+CHUNK_ROWS = {"prefill": 512}
+
+
+def run_workload(name, steps, warmup, path=0, n_tokens=None, chunk=None):
+    """K timed steps of one workload.  A step is one forward of all N tokens:
+    one call, or with ``chunk`` rows one call per chunk into one reused
+    [chunk x V] output buffer."""
     import torch
     import synth
     import compressed_output_head_amd as ah
@@ -165,22 +173,29 @@ def run_workload(name, steps, warmup, path=0, n_tokens=None):
     N = cfg["N"]
     H = torch.from_numpy(inp.H_bits.view(np.int16)).view(torch.bfloat16).cuda()
     ydt = torch.bfloat16 if cfg["y_dtype"] == "bf16" else torch.float32
-    Y = torch.empty((N, cfg["V"]), dtype=ydt, device="cuda")
+    rows = min(chunk or N, N)
+    Y = torch.empty((rows, cfg["V"]), dtype=ydt, device="cuda")
+    parts = [H[i:i + rows] for i in range(0, N, rows)]
     for h in heads:
-        h.ensure_workspace(N)
+        h.ensure_workspace(rows)
     del inp
     log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s "
         f"(packed head {L['payload_bytes'] / 1e6:.1f} MB payload, x2 copies)")
 
     stream = torch.cuda.current_stream()
+
+    def step(i):
+        for Hp in parts:
+            ah.archead_logits_path(Hp, heads[i % 2], Y[:Hp.shape[0]], path)
+
     for i in range(warmup):
-        ah.archead_logits_path(H, heads[i % 2], Y, path)
-    # timed region: K whole forward calls, nothing else on the stream
+        step(i)
+    # timed region: K whole forward steps, nothing else on the stream
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        ah.archead_logits_path(H, heads[i % 2], Y, path)
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
@@ -190,17 +205,23 @@ def run_workload(name, steps, warmup, path=0, n_tokens=None):
     # queued back to back the start marker waits behind the previous call and
     # the pre-projection, and the span then includes dispatch gaps that are
     # not the kernel's
-    evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    eve = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # (a chunked step's kernel time is the sum over its chunks)
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts))]
+    eve = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts))]
     for e in evb + eve:
         e.record(stream)  # creates the underlying hipEvent
     torch.cuda.synchronize()
+    kms = []
     for i in range(steps):
-        ah.archead_logits_events(H, heads[i % 2], Y, path, evb[i], eve[i])
-        torch.cuda.synchronize()
-    kms = [evb[i].elapsed_time(eve[i]) for i in range(steps)]
+        t = 0.0
+        for j, Hp in enumerate(parts):
+            ah.archead_logits_events(Hp, heads[i % 2], Y[:Hp.shape[0]], path, evb[j], eve[j])
+            torch.cuda.synchronize()
+            t += evb[j].elapsed_time(eve[j])
+        kms.append(t)
     A = algorithmic(cfg, L, N)
-    return dict(cfg=cfg, L=L, A=A, ms=ms, kernel=dominant_kernel(cfg), kernel_ms=float(np.mean(kms)),
+    return dict(cfg=cfg, L=L, A=A, ms=ms, kernel=dominant_kernel(cfg, rows, path), kernel_ms=float(np.mean(kms)),
+                chunk_rows=rows if rows < N else None, calls_per_step=len(parts),
                 kernel_ms_min=float(np.min(kms)), kernel_ms_max=float(np.max(kms)),
                 kernel_ms_pct=[round(float(np.percentile(kms, q)), 5) for q in (10, 50, 90)])
 
@@ -401,39 +422,76 @@ def tile_workload(N):
     return N > 64
 
 
-def cpu_baseline(name, sample_rows, min_seconds=10.0):
+def blas_info():
+    """The BLAS numpy (and so the oracle's matrix products) runs on, and its threads."""
+    info = {"name": None, "version": None, "threads": None}
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        info["name"], info["version"] = b.get("name"), b.get("version")
+    except Exception:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            info["threads"] = max(p.get("num_threads", 1) for p in pools)
+            info["name"] = info["name"] or pools[0].get("internal_api")
+    except Exception:
+        pass
+    return info
+
+
+def cpu_baseline(name, sample_rows, min_seconds=6.0):
     """The oracle as it stands, timed on a bounded sample of the workload:
     the first ``sample_rows`` vocabulary rows, repeated until at least
     ``min_seconds`` of host time have passed.  Reported in the workload's own
-    unit: GB/s of packed bytes of those rows, or TFLOP/s of their logits."""
+    unit: GB/s of packed bytes of those rows, or TFLOP/s of their logits.
+    ``gemm_only`` times the fp64 product H W_hat^T alone on the same rows
+    (W_hat rebuilt once beforehand), to show how much of the oracle is the
+    unpacking and rebuilding of W_hat."""
     import synth
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    blas = blas_info()
     cfg = synth.config(name)
     inp = synth.make(name)
     cols = np.arange(min(sample_rows, cfg["V"]))
-    reps, t0 = 0, time.time()
-    while True:
-        oracle.logits(inp.H_bits, inp.head, cols=cols)
-        reps += 1
-        if time.time() - t0 >= min_seconds:
-            break
-    dt = time.time() - t0
+
+    def timed(fn):
+        reps, t0 = 0, time.time()
+        while True:
+            fn()
+            reps += 1
+            if time.time() - t0 >= min_seconds:
+                return reps, time.time() - t0
+
+    reps, dt = timed(lambda: oracle.logits(inp.H_bits, inp.head, cols=cols))
+    Hf = oracle.bf16_bits_to_f64(inp.H_bits)
+    Wc = oracle.w_hat(inp.head, 0, int(cols.size))  # the rows of the sample: 0 .. n-1
+    reps_g, dt_g = timed(lambda: Hf @ Wc.T)
     what = (f"fp64 oracle (unpack, rebuild W_hat, H W_hat^T) on vocabulary rows 0..{cols.size - 1} "
-            f"of the {name} workload, {reps} passes in {dt:.1f}s; ")
+            f"of the {name} workload (N={cfg['N']}), {reps} passes in {dt:.1f}s; ")
+    common = dict(cores=int(blas["threads"] or 1), kind="oracle", blas=blas,
+                  sample_rows=int(cols.size), seconds=round(dt, 2))
     if tile_workload(cfg["N"]):
         r = cfg["r_c"] + cfg["r_r"]
-        flops = 2 * cfg["N"] * cols.size * (cfg["D"] + r) * reps
-        return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
+        per_pass = 2 * cfg["N"] * cols.size * (cfg["D"] + r)
+        v, vg = per_pass * reps / dt / 1e12, 2 * cfg["N"] * cols.size * cfg["D"] * reps_g / dt_g / 1e12
+        return dict(value=round(v, 6), unit="TFLOP/s", **common,
+                    gemm_only=dict(value=round(vg, 6), unit="TFLOP/s of the dgemm's own flops",
+                                   seconds=round(dt_g, 2), passes=reps_g),
                     sample=what + "TFLOP/s of the logits of those rows (2 N (D + r_c + r_r) per logit)")
     L = oracle.layout(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"])
-    sample_bytes = L["payload_bytes"] * cols.size / cfg["V"] * reps
-    return dict(value=round(sample_bytes / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+    per_pass = L["payload_bytes"] * cols.size / cfg["V"]
+    return dict(value=round(per_pass * reps / dt / 1e9, 4), unit="GB/s", **common,
+                gemm_only=dict(value=round(per_pass * reps_g / dt_g / 1e9, 4),
+                               unit="GB/s of the same packed bytes, H W_hat^T alone",
+                               seconds=round(dt_g, 2), passes=reps_g),
                 sample=what + "GB/s of packed bytes of those rows")
+
+
+# vocabulary rows of each workload the CPU oracle is timed on (about 5-10 s each)
+CPU_SAMPLE_ROWS = {"decode": 151936, "batched": 32768, "prefill": 1024, "head70b": 4096}
 
 
 def roofline_decode(r):
@@ -470,10 +528,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode", help="headline workload (decode, batched, prefill, head70b)")
     ap.add_argument("--n", type=int, default=None, help="token count of the headline workload (default: its own)")
-    ap.add_argument("--secondary", default="prefill", help="second workload ('' to skip)")
+    ap.add_argument("--secondary", default="prefill,batched,head70b",
+                    help="further workloads, comma-separated ('' to skip); the first is also reported as "
+                         "'secondary'")
     ap.add_argument("--cpu-sample-rows", type=int, default=None,
-                    help="vocabulary rows the CPU oracle is timed on (default: all for decode-type "
-                         "workloads, 4096 for tile-type ones)")
+                    help="vocabulary rows the CPU oracle is timed on (default: per workload, CPU_SAMPLE_ROWS)")
+    ap.add_argument("--cpu-workloads", default="all",
+                    help="workloads the CPU oracle is timed on: 'all' (the headline and --secondary) or the "
+                         "headline only ('headline')")
     ap.add_argument("--stats", default="prefill",
                     help="workload timed through archead_logits_stats ('' to skip)")
     ap.add_argument("--quantize", default="decode",
@@ -533,17 +595,30 @@ def main():
                    "packed_payload_bytes": A["payload"], "head_copies_rotated": 2},
         "roofline": roof,
     }
-    if args.secondary:
+    names = [w for w in args.secondary.split(",") if w]
+    if names:
+        out["workloads"] = {}
+    for w in names:
         steps2 = max(5, args.steps // 5)
-        s = run_workload(args.secondary, steps2, max(2, args.warmup // 5))
+        s = run_workload(w, steps2, max(2, args.warmup // 5), chunk=CHUNK_ROWS.get(w))
         v2, u2, roof2 = summary(s)
-        log(f"[bench] {args.secondary}: {s['ms']:.3f} ms/step, {s['kernel']} {s['kernel_ms']:.3f} ms")
-        out["secondary"] = {
-            "workload": s["cfg"]["name"], "value": v2, "unit": u2,
-            "ms_per_step": round(s["ms"], 4), "steps": steps2,
+        log(f"[bench] {w}: {s['ms']:.3f} ms/step ({s['calls_per_step']} calls), {s['kernel']} {s['kernel_ms']:.3f} ms")
+        entry = {
+            "workload": w, "value": v2, "unit": u2,
+            "ms_per_step": round(s["ms"], 4), "steps": steps2, "calls_per_step": s["calls_per_step"],
             "config": {k: s["cfg"][k] for k in ("V", "D", "N", "r_c", "r_r", "g")} | {"logits": s["cfg"]["y_dtype"]},
             "roofline": roof2,
         }
+        if s["chunk_rows"]:
+            entry["chunk_rows"] = s["chunk_rows"]
+            one = run_workload(w, max(3, steps2 // 2), 1)
+            v1, _, roof1 = summary(one)
+            entry["one_call"] = {"value": v1, "ms_per_step": round(one["ms"], 4),
+                                 "kernel_ms": round(one["kernel_ms"], 4), "roofline_frac": roof1["frac"]}
+            log(f"[bench] {w} in one call: {one['ms']:.3f} ms")
+        out["workloads"][w] = entry
+        if "secondary" not in out:
+            out["secondary"] = entry
     if args.stats:
         st = run_stats(args.stats, max(5, args.steps // 5), max(2, args.warmup // 5))
         log(f"[bench] stats on {args.stats}: {st['ms_per_call']:.3f} ms/call")
@@ -561,14 +636,18 @@ def main():
         log(f"[bench] fit on {args.fit}: {ft['ms_per_call']:.1f} ms/call")
         out["fit"] = ft
     out["roofline"]["kernel_ms_p10_p50_p90"] = r["kernel_ms_pct"]
-    if not args.no_context and args.secondary:
-        out["context"] = dense_context(args.secondary)
+    if not args.no_context and names:
+        out["context"] = dense_context(names[0])
         log(f"[bench] context: {out['context']}")
     out["kernel_sources"] = kernel_hash()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        rows = args.cpu_sample_rows or (4096 if tile_workload(cfg["N"]) else cfg["V"])
+        rows = args.cpu_sample_rows or CPU_SAMPLE_ROWS.get(args.config, 4096)
         out["cpu_baseline"] = cpu_baseline(args.config, rows)
+        if args.cpu_workloads == "all":
+            for w in names:
+                log(f"[bench] timing the CPU oracle on {w} ...")
+                out["workloads"][w]["cpu_baseline"] = cpu_baseline(w, CPU_SAMPLE_ROWS.get(w, 4096))
     print(json.dumps(out), flush=True)
 
 

@@ -20,9 +20,12 @@ LIB_PATH = os.path.join(_HERE, "libarchead.so")
 ARCHEAD_OK = 0
 ARCHEAD_BF16, ARCHEAD_F32 = 1, 2
 ARCHEAD_PATH_AUTO, ARCHEAD_PATH_DECODE, ARCHEAD_PATH_TILE = 0, 1, 2
+# main kernels (archead_main_kernel), by the names the profiler shows
+KERNEL_NAMES = {0: "tile32_kernel", 1: "small_decode_kernel", 2: "decode_kernel"}
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5: "E_SHAPE",
           6: "E_ALIGN", 7: "E_WORKSPACE", 8: "E_HIP", 9: "E_VALUE", 10: "E_SIZE"}
-EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_workspace_bytes_path", "archead_pack",
+EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_workspace_bytes_path", "archead_main_kernel",
+           "archead_pack",
            "archead_logits", "archead_logits_noalloc",
            "archead_logits_path", "archead_logits_events", "archead_stats_workspace_bytes",
            "archead_logits_stats", "archead_quantize", "archead_topk_workspace_bytes", "archead_logits_topk",
@@ -109,6 +112,7 @@ def _load():
     lib.archead_pack_layout.argtypes = [P(ArcheadDims), P(ArcheadLayout)]
     lib.archead_workspace_bytes.argtypes = [P(ArcheadDims), ctypes.c_int64, P(ctypes.c_uint64)]
     lib.archead_workspace_bytes_path.argtypes = [P(ArcheadDims), ctypes.c_int64, ctypes.c_int, P(ctypes.c_uint64)]
+    lib.archead_main_kernel.argtypes = [P(ArcheadDims), ctypes.c_int64, ctypes.c_int, P(ctypes.c_int)]
     lib.archead_pack.argtypes = [P(ArcheadDims), P(ArcheadHostComponents), ctypes.c_void_p, ctypes.c_uint64]
     lib.archead_logits.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor), ctypes.c_void_p]
     lib.archead_logits_noalloc.argtypes = [P(ArcheadTensor), P(ArcheadPackedHead), P(ArcheadTensor), ctypes.c_void_p]
@@ -184,6 +188,14 @@ def archead_workspace_bytes_path(V, D, r_c, r_r, g, n_tokens: int, path: int) ->
     _check(lib.archead_workspace_bytes_path(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens), int(path),
                                             ctypes.byref(b)), "archead_workspace_bytes_path")
     return b.value
+
+
+def archead_main_kernel(V, D, r_c, r_r, g, n_tokens: int, path: int = ARCHEAD_PATH_AUTO) -> str:
+    """Name of the main kernel a call of n_tokens rows on `path` launches."""
+    k = ctypes.c_int()
+    _check(lib.archead_main_kernel(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens), int(path),
+                                   ctypes.byref(k)), "archead_main_kernel")
+    return KERNEL_NAMES[k.value]
 
 
 def archead_stats_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:

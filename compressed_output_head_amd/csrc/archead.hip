@@ -62,7 +62,8 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
                                  bool allow_decode) {
   WorkspaceLayout w{};
   const uint64_t n = (uint64_t)std::max<int64_t>(n_tokens, 0);
-  w.decode = allow_decode && decode_fits(d, n_tokens);
+  w.small = allow_decode && small_decode_fits(d, n_tokens);
+  w.decode = w.small || (allow_decode && decode_fits(d, n_tokens));
   w.rc32 = (int)round_up((uint64_t)d->r_c, 32);
   w.rr32 = (int)round_up((uint64_t)d->r_r, 32);
   w.zsteps = (w.rc32 + w.rr32) / 32;
@@ -80,6 +81,10 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
     w.zf = take(n32 * (uint64_t)w.zsteps * 2 * 32 * 2);
     w.zscale = take(n32 * 4);
     w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
+  } else if (w.small) {  // the few-token decode kernels: converted H, its scales, Z
+    w.hc = take(n * D * 2);
+    w.hscale = take(n * 4);
+    w.z32 = take(n * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
   } else {  // the decode path: partial sums of Z
     w.z32 = take(decode_workspace_bytes(d, n_tokens));
   }
@@ -156,6 +161,18 @@ int archead_workspace_bytes_path(const archead_dims* d, int64_t n_tokens, int pa
   if (n_tokens < 0) return ARCHEAD_E_SHAPE;
   if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
   *bytes = workspace_layout(d, n_tokens, false, kSplitBytes, path != ARCHEAD_PATH_TILE).total;
+  return ARCHEAD_OK;
+}
+
+int archead_main_kernel(const archead_dims* d, int64_t n_tokens, int path, int* kernel) {
+  if (!d || !kernel) return ARCHEAD_E_NULL;
+  const int rc = check_dims(d);
+  if (rc) return rc;
+  if (n_tokens < 0) return ARCHEAD_E_SHAPE;
+  if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
+  const WorkspaceLayout w = workspace_layout(d, n_tokens, false, kSplitBytes, path != ARCHEAD_PATH_TILE);
+  if (path == ARCHEAD_PATH_DECODE && !w.decode) return ARCHEAD_E_UNSUPPORTED;
+  *kernel = !w.decode ? ARCHEAD_KERNEL_TILE : w.small ? ARCHEAD_KERNEL_DECODE_FEW : ARCHEAD_KERNEL_DECODE_STREAM;
   return ARCHEAD_OK;
 }
 
@@ -323,6 +340,7 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
   a.zf = reinterpret_cast<_Float16*>(ws + W.zf);
   a.zscale = reinterpret_cast<float*>(ws + W.zscale);
   a.z32 = reinterpret_cast<float*>(ws + W.z32);
+  a.hc = reinterpret_cast<_Float16*>(ws + W.hc);
   a.part = W.split_bytes ? reinterpret_cast<float*>(ws + W.split) : nullptr;
   a.part_bytes = W.split_bytes;
   if (stats) {
@@ -364,9 +382,10 @@ int logits_impl(const archead_tensor* H, const archead_packed_head* head, archea
     return ARCHEAD_E_UNSUPPORTED;
   if (!decode && !tile32_eligible(a)) return ARCHEAD_E_UNSUPPORTED;
   (void)hipGetLastError();  // start from a clean error state
-  if ((decode ? launch_decode_prep(a, s) : launch_prep(a, s)) != hipSuccess) return ARCHEAD_E_HIP;
+  const hipError_t ep = !decode ? launch_prep(a, s) : W.small ? launch_small_prep(a, s) : launch_decode_prep(a, s);
+  if (ep != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return ARCHEAD_E_HIP;
-  const hipError_t e = decode ? launch_decode(a, s) : launch_tile(a, s);
+  const hipError_t e = !decode ? launch_tile(a, s) : W.small ? launch_small_decode(a, s) : launch_decode(a, s);
   if (e != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
   return ARCHEAD_OK;
@@ -460,8 +479,8 @@ int archead_logits_stats(const archead_tensor* H, const archead_packed_head* hea
     a.Y_stride = a.V;
     a.y_bf16 = 0;
     a.st_nparts = kStatChunks;
-    e = launch_decode_prep(a, s);
-    if (e == hipSuccess) e = launch_decode(a, s);
+    e = W.small ? launch_small_prep(a, s) : launch_decode_prep(a, s);
+    if (e == hipSuccess) e = W.small ? launch_small_decode(a, s) : launch_decode(a, s);
     if (e == hipSuccess) e = launch_rowstats_y(a, Yw, a.V, s);
   } else if (tile32_eligible(a)) {
     a.st_nparts = tile_stat_parts(a);

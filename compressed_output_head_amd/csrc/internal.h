@@ -30,6 +30,8 @@ void compute_layout(const archead_dims* d, archead_layout* L);
 // Whether a call with n_tokens rows of H runs the decode kernel (pure host
 // arithmetic: dims, token count and the LDS the kernel would need).
 bool decode_fits(const archead_dims* d, int64_t n_tokens);
+// the few-token decode path (decode_small.hip) takes the call
+bool small_decode_fits(const archead_dims* d, int64_t n_tokens);
 // workspace of a decode-path call: partial sums of Z
 uint64_t decode_workspace_bytes(const archead_dims* d, int64_t n_tokens);
 
@@ -37,11 +39,12 @@ uint64_t decode_workspace_bytes(const archead_dims* d, int64_t n_tokens);
 // kernel needs none (its statistics call needs the pieces and Y); the tile
 // path needs the converted H, Z and the partial sums of split tiles.
 struct WorkspaceLayout {
-  bool decode;          // the call runs the decode kernel
+  bool decode;          // the call runs the decode path
+  bool small;           // ... and its few-token kernels
   int64_t n32;          // tokens rounded up to 32 (rows of every per-token workspace section)
   int rc32, rr32;       // ranks rounded up to 32
   int zsteps;           // (rc32 + rr32) / 32
-  uint64_t hf, hscale, zf, zscale, z32, split, split_bytes;
+  uint64_t hf, hscale, zf, zscale, z32, hc, split, split_bytes;
   uint64_t st_part, st_y;  // row statistics only: pieces [N][st_nparts], Y [N][V] fp32 (decode kernel)
   int64_t st_nparts;
   uint64_t total;
@@ -73,6 +76,7 @@ struct FwdArgs {
   // workspace of the tile path: operand fragments of the 32 x 32 x 16 MFMA,
   //   hf [n32/32][D/128][8][64][8],  zf [n32/32][4*zsteps][64][8]
   _Float16* hf;               // converted, scaled H
+  _Float16* hc;               // few-token decode path: H [N][D] converted in kernel k-order
   float* hscale;              // [n32]
   _Float16* zf;               // hi/lo pre-projection
   float* zscale;              // [n32]
@@ -91,6 +95,8 @@ bool tile32_eligible(const FwdArgs& a);
 hipError_t launch_tile(const FwdArgs& a, hipStream_t s);
 // decode path: the partial sums of Z into the workspace, then the streaming kernel
 hipError_t launch_decode_prep(const FwdArgs& a, hipStream_t s);
+hipError_t launch_small_prep(const FwdArgs& a, hipStream_t s);
+hipError_t launch_small_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
 int tile_stat_parts(const FwdArgs& a);
 hipError_t launch_tile_stats(const FwdArgs& a, hipStream_t s);

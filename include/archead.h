@@ -67,10 +67,14 @@ typedef enum { ARCHEAD_BF16 = 1, ARCHEAD_F32 = 2 } archead_dtype;
 
 typedef enum {
   ARCHEAD_PATH_AUTO = 0,   /* the decode path when it takes the call, else the tile path */
-  ARCHEAD_PATH_DECODE = 1, /* one kernel that streams the head once for up to 16 tokens whose
-                              converted H fits the 160 KiB of LDS of a workgroup
-                              (N <= 16 at D = 4096, N <= 8 at D = 8192), with
-                              N (r_c + r_r) <= 2048, round_up(r_c, 32) +
+  ARCHEAD_PATH_DECODE = 1, /* one kernel that streams the head once for up to 16 tokens:
+                              the few-token kernel when H (N + 1 rows of D + 8
+                              halves) and Z (N (r_c + r_r) fp32) fit 48 KiB of
+                              LDS and D/128 is a multiple of 4 (N <= 4 at
+                              D = 4096, r = 64), else the k-tile-major kernel
+                              when the converted H fits the 160 KiB of LDS of a
+                              workgroup (N <= 16 at D = 4096, N <= 8 at D = 8192),
+                              with N (r_c + r_r) <= 2048, round_up(r_c, 32) +
                               round_up(r_r, 32) <= 256 and D/g <= 128 */
   ARCHEAD_PATH_TILE = 2    /* LDS-tiled MFMA path (any N); needs the workspace    */
 } archead_path;
@@ -156,8 +160,11 @@ typedef struct {
 ARCHEAD_API int archead_pack_layout(const archead_dims* d, archead_layout* out);
 
 /* Device workspace one archead_logits call with n_tokens rows of H needs on
- * the automatic path: when the decode path takes the call, the partial sums of
- * the pre-projection (n_tokens (r_c + r_r) zst fp32, zst = ceil(D / 1024)
+ * the automatic path: when the few-token decode kernel takes the call, H
+ * converted to fp16 (n_tokens D halves), its per-token scales and Z
+ * (n_tokens (r_c + r_r) fp32), each section rounded up to 256 bytes; when the
+ * k-tile-major decode kernel takes it, the partial sums of the
+ * pre-projection (n_tokens (r_c + r_r) zst fp32, zst = ceil(D / 1024)
  * rounded up to a multiple of 4; 0 when r_c + r_r = 0, and the workspace
  * pointer may then be NULL); on the tile path the converted hidden states,
  * the low-rank pre-projection, per-token scales and 64 MiB for partial sums
@@ -169,6 +176,24 @@ ARCHEAD_API int archead_workspace_bytes(const archead_dims* d, int64_t n_tokens,
  * ARCHEAD_PATH_TILE always needs the tile path's workspace.  E_NULL, E_DIMS,
  * E_SHAPE, E_UNSUPPORTED (unknown path). */
 ARCHEAD_API int archead_workspace_bytes_path(const archead_dims* d, int64_t n_tokens, int path, uint64_t* bytes);
+
+/* The main kernel a successful archead_logits_path call of n_tokens rows
+ * launches (after its pre-projection kernel):
+ *   ARCHEAD_KERNEL_TILE           tile32_kernel, the LDS-tiled MFMA path
+ *   ARCHEAD_KERNEL_DECODE_FEW     small_decode_kernel: few tokens whose bf16
+ *                                 rows and Z fit in 48 KB of LDS (N <= 4 at
+ *                                 D = 4096, r = 64)
+ *   ARCHEAD_KERNEL_DECODE_STREAM  decode_kernel: the k-tile-major streaming
+ *                                 kernel for the other calls of up to 16 tokens
+ * Host only; lets a caller or profiler name the kernel it times.  E_NULL,
+ * E_DIMS, E_SHAPE, E_UNSUPPORTED (unknown path, or a forced decode path the
+ * call cannot take). */
+enum archead_kernel {
+  ARCHEAD_KERNEL_TILE = 0,
+  ARCHEAD_KERNEL_DECODE_FEW = 1,
+  ARCHEAD_KERNEL_DECODE_STREAM = 2
+};
+ARCHEAD_API int archead_main_kernel(const archead_dims* d, int64_t n_tokens, int path, int* kernel);
 
 /* Serialise host components into `dst` (host memory, dst_bytes >=
  * layout.total_bytes), writing every byte of the layout including padding.

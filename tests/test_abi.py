@@ -113,6 +113,12 @@ def _tile_workspace(V, D, r_c, r_r, g, N):
             up(n32 * (r_c + r_r) * 4) + (64 << 20))
 
 
+def _few_tokens(V, D, r_c, r_r, g, N):
+    """The few-token decode kernels take the call: H (N + 1 rows of D + 8
+    halves) and Z (N r fp32) within 48 KiB of LDS, k-tiles a multiple of 4."""
+    return 1 <= N <= 16 and (D // 128) % 4 == 0 and (N + 1) * (D + 8) * 2 + N * (r_c + r_r) * 4 <= 48 * 1024
+
+
 def test_workspace_bytes(ah):
     # calls the decode kernel takes (up to 16 tokens whose H fits its LDS,
     # 32-rank steps rc32 + rr32 <= 256) need the partial sums of Z; the tile
@@ -125,12 +131,26 @@ def test_workspace_bytes(ah):
                                            ((128256, 8192, 64, 64, 128), 9, False),
                                            ((151936, 4096, 64, 64, 128), 4096, False), ((64, 128, 0, 0, 32), 17, False)]:
         up = lambda x: (x + 255) // 256 * 256
-        zst = (-(-(D // 128) // 8) + 3) // 4 * 4  # Z partial sums per element: slices of 8 k-tiles, padded to 4
-        want = up(N * (r_c + r_r) * zst * 4) if decode else _tile_workspace(V, D, r_c, r_r, g, N)
+        if not decode:
+            want = _tile_workspace(V, D, r_c, r_r, g, N)
+        elif _few_tokens(V, D, r_c, r_r, g, N):  # converted H [N][D] fp16, its scales, Z [N][r] fp32
+            want = up(N * D * 2) + up(N * 4) + up(N * (r_c + r_r) * 4)
+        else:  # Z partial sums per element: slices of 8 k-tiles, padded to 4
+            zst = (-(-(D // 128) // 8) + 3) // 4 * 4
+            want = up(N * (r_c + r_r) * zst * 4)
         assert ah.archead_workspace_bytes(V, D, r_c, r_r, g, N) == want, (V, D, N)
         assert ah.archead_workspace_bytes_path(V, D, r_c, r_r, g, N, 0) == want
         assert ah.archead_workspace_bytes_path(V, D, r_c, r_r, g, N, 1) == want
         assert ah.archead_workspace_bytes_path(V, D, r_c, r_r, g, N, 2) == _tile_workspace(V, D, r_c, r_r, g, N)
+        kern = ("tile32_kernel" if not decode else
+                "small_decode_kernel" if _few_tokens(V, D, r_c, r_r, g, N) else "decode_kernel")
+        assert ah.archead_main_kernel(V, D, r_c, r_r, g, N) == kern, (V, D, N)
+        assert ah.archead_main_kernel(V, D, r_c, r_r, g, N, 2) == "tile32_kernel"
+        if decode:
+            assert ah.archead_main_kernel(V, D, r_c, r_r, g, N, 1) == kern
+        else:
+            with pytest.raises(ah.ArcheadError):
+                ah.archead_main_kernel(V, D, r_c, r_r, g, N, 1)
     assert ah.archead_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
     with pytest.raises(ah.ArcheadError):
         ah.archead_workspace_bytes_path(1024, 256, 16, 8, 64, 4, 3)

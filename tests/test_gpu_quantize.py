@@ -91,9 +91,13 @@ def test_quantized_head_runs_the_forward():
     head_ref, _ = oracle.quantize(dense.W, dense.A_c, dense.B_c, dense.A_w, dense.B_w, g)
     inp = synth.make("tiny", seed=11, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g)
     Yr = oracle.logits(inp.H_bits, head_ref)
-    for path in (0, 1):
+    for path in (0, 2):
         Yg = to_f64(run(head, inp.H_bits, path, H_dev=device_H(inp.H_bits)))
         check_parity(Yg, Yr, f"path {path}")
+    # the decode path takes at most 16 tokens: the first 8 rows
+    H8 = inp.H_bits[:8].copy()
+    Yg = to_f64(run(head, H8, 1, H_dev=device_H(H8)))
+    check_parity(Yg, Yr[:8], "path 1")
 
 
 @pytest.mark.slow
