@@ -21,7 +21,7 @@ ARCHEAD_OK = 0
 ARCHEAD_BF16, ARCHEAD_F32 = 1, 2
 ARCHEAD_PATH_AUTO, ARCHEAD_PATH_DECODE, ARCHEAD_PATH_TILE = 0, 1, 2
 # main kernels (archead_main_kernel), by the names the profiler shows
-KERNEL_NAMES = {0: "tile32_kernel", 1: "small_decode_kernel", 2: "decode_kernel"}
+KERNEL_NAMES = {0: "tile32_kernel", 1: "small_decode_kernel", 2: "decode_kernel", 3: "batch_kernel"}
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5: "E_SHAPE",
           6: "E_ALIGN", 7: "E_WORKSPACE", 8: "E_HIP", 9: "E_VALUE", 10: "E_SIZE"}
 EXPORTS = ("archead_pack_layout", "archead_workspace_bytes", "archead_workspace_bytes_path", "archead_main_kernel",

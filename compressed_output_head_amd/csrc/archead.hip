@@ -63,7 +63,8 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
   WorkspaceLayout w{};
   const uint64_t n = (uint64_t)std::max<int64_t>(n_tokens, 0);
   w.small = allow_decode && small_decode_fits(d, n_tokens);
-  w.decode = w.small || (allow_decode && decode_fits(d, n_tokens));
+  w.batch = allow_decode && !w.small && batch_fits(d, n_tokens);
+  w.decode = w.small || w.batch || (allow_decode && decode_fits(d, n_tokens));
   w.rc32 = (int)round_up((uint64_t)d->r_c, 32);
   w.rr32 = (int)round_up((uint64_t)d->r_r, 32);
   w.zsteps = (w.rc32 + w.rr32) / 32;
@@ -81,7 +82,7 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
     w.zf = take(n32 * (uint64_t)w.zsteps * 2 * 32 * 2);
     w.zscale = take(n32 * 4);
     w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
-  } else if (w.small) {  // the few-token decode kernels: converted H, its scales, Z
+  } else if (w.small || w.batch) {  // few-token and batched decode kernels: converted H, its scales, Z
     w.hc = take(n * D * 2);
     w.hscale = take(n * 4);
     w.z32 = take(n * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
@@ -172,7 +173,10 @@ int archead_main_kernel(const archead_dims* d, int64_t n_tokens, int path, int* 
   if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
   const WorkspaceLayout w = workspace_layout(d, n_tokens, false, kSplitBytes, path != ARCHEAD_PATH_TILE);
   if (path == ARCHEAD_PATH_DECODE && !w.decode) return ARCHEAD_E_UNSUPPORTED;
-  *kernel = !w.decode ? ARCHEAD_KERNEL_TILE : w.small ? ARCHEAD_KERNEL_DECODE_FEW : ARCHEAD_KERNEL_DECODE_STREAM;
+  *kernel = !w.decode ? ARCHEAD_KERNEL_TILE
+            : w.small ? ARCHEAD_KERNEL_DECODE_FEW
+            : w.batch ? ARCHEAD_KERNEL_DECODE_BATCH
+                      : ARCHEAD_KERNEL_DECODE_STREAM;
   return ARCHEAD_OK;
 }
 
@@ -382,10 +386,13 @@ int logits_impl(const archead_tensor* H, const archead_packed_head* head, archea
     return ARCHEAD_E_UNSUPPORTED;
   if (!decode && !tile32_eligible(a)) return ARCHEAD_E_UNSUPPORTED;
   (void)hipGetLastError();  // start from a clean error state
-  const hipError_t ep = !decode ? launch_prep(a, s) : W.small ? launch_small_prep(a, s) : launch_decode_prep(a, s);
+  const hipError_t ep = !decode ? launch_prep(a, s) : (W.small || W.batch) ? launch_small_prep(a, s) : launch_decode_prep(a, s);
   if (ep != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return ARCHEAD_E_HIP;
-  const hipError_t e = !decode ? launch_tile(a, s) : W.small ? launch_small_decode(a, s) : launch_decode(a, s);
+  const hipError_t e = !decode ? launch_tile(a, s)
+                       : W.small ? launch_small_decode(a, s)
+                       : W.batch ? launch_batch(a, s)
+                                 : launch_decode(a, s);
   if (e != hipSuccess) return ARCHEAD_E_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
   return ARCHEAD_OK;
@@ -479,8 +486,8 @@ int archead_logits_stats(const archead_tensor* H, const archead_packed_head* hea
     a.Y_stride = a.V;
     a.y_bf16 = 0;
     a.st_nparts = kStatChunks;
-    e = W.small ? launch_small_prep(a, s) : launch_decode_prep(a, s);
-    if (e == hipSuccess) e = W.small ? launch_small_decode(a, s) : launch_decode(a, s);
+    e = (W.small || W.batch) ? launch_small_prep(a, s) : launch_decode_prep(a, s);
+    if (e == hipSuccess) e = W.small ? launch_small_decode(a, s) : W.batch ? launch_batch(a, s) : launch_decode(a, s);
     if (e == hipSuccess) e = launch_rowstats_y(a, Yw, a.V, s);
   } else if (tile32_eligible(a)) {
     a.st_nparts = tile_stat_parts(a);

@@ -32,6 +32,8 @@ void compute_layout(const archead_dims* d, archead_layout* L);
 bool decode_fits(const archead_dims* d, int64_t n_tokens);
 // the few-token decode path (decode_small.hip) takes the call
 bool small_decode_fits(const archead_dims* d, int64_t n_tokens);
+// the batched decode kernel (batch.hip, 17 to 64 tokens) takes the call
+bool batch_fits(const archead_dims* d, int64_t n_tokens);
 // workspace of a decode-path call: partial sums of Z
 uint64_t decode_workspace_bytes(const archead_dims* d, int64_t n_tokens);
 
@@ -41,6 +43,7 @@ uint64_t decode_workspace_bytes(const archead_dims* d, int64_t n_tokens);
 struct WorkspaceLayout {
   bool decode;          // the call runs the decode path
   bool small;           // ... and its few-token kernels
+  bool batch;           // ... and its batched kernel (same workspace as the few-token kernels)
   int64_t n32;          // tokens rounded up to 32 (rows of every per-token workspace section)
   int rc32, rr32;       // ranks rounded up to 32
   int zsteps;           // (rc32 + rr32) / 32
@@ -98,6 +101,7 @@ hipError_t launch_decode_prep(const FwdArgs& a, hipStream_t s);
 hipError_t launch_small_prep(const FwdArgs& a, hipStream_t s);
 hipError_t launch_small_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
+hipError_t launch_batch(const FwdArgs& a, hipStream_t s);
 int tile_stat_parts(const FwdArgs& a);
 hipError_t launch_tile_stats(const FwdArgs& a, hipStream_t s);
 // statistics pieces of a fp32 Y already in memory, kStatChunks per token

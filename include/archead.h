@@ -67,15 +67,20 @@ typedef enum { ARCHEAD_BF16 = 1, ARCHEAD_F32 = 2 } archead_dtype;
 
 typedef enum {
   ARCHEAD_PATH_AUTO = 0,   /* the decode path when it takes the call, else the tile path */
-  ARCHEAD_PATH_DECODE = 1, /* one kernel that streams the head once for up to 16 tokens:
-                              the few-token kernel when H (N + 1 rows of D + 8
+  ARCHEAD_PATH_DECODE = 1, /* one kernel that streams the head once for up to 64 tokens.
+                              Up to 16 tokens: the few-token kernel when H (N + 1 rows of D + 8
                               halves) and Z (N (r_c + r_r) fp32) fit 48 KiB of
                               LDS and D/128 is a multiple of 4 (N <= 4 at
                               D = 4096, r = 64), else the k-tile-major kernel
                               when the converted H fits the 160 KiB of LDS of a
                               workgroup (N <= 16 at D = 4096, N <= 8 at D = 8192),
                               with N (r_c + r_r) <= 2048, round_up(r_c, 32) +
-                              round_up(r_r, 32) <= 256 and D/g <= 128 */
+                              round_up(r_r, 32) <= 256 and D/g <= 128.
+                              17 to 64 tokens: the batched kernel (accumulators
+                              of all tokens for its vocabulary rows held over
+                              the whole hidden dimension) when round_up(r_c, 32)
+                              + round_up(r_r, 32) <= 128, D/g <= 64 and D is a
+                              multiple of 512 */
   ARCHEAD_PATH_TILE = 2    /* LDS-tiled MFMA path (any N); needs the workspace    */
 } archead_path;
 
@@ -185,13 +190,18 @@ ARCHEAD_API int archead_workspace_bytes_path(const archead_dims* d, int64_t n_to
  *                                 D = 4096, r = 64)
  *   ARCHEAD_KERNEL_DECODE_STREAM  decode_kernel: the k-tile-major streaming
  *                                 kernel for the other calls of up to 16 tokens
+ *   ARCHEAD_KERNEL_DECODE_BATCH   batch_kernel: the batched streaming kernel
+ *                                 for 17 to 64 tokens (r_c, r_r rounded up to
+ *                                 32 sum to at most 128, D/g <= 64, D a
+ *                                 multiple of 512)
  * Host only; lets a caller or profiler name the kernel it times.  E_NULL,
  * E_DIMS, E_SHAPE, E_UNSUPPORTED (unknown path, or a forced decode path the
  * call cannot take). */
 enum archead_kernel {
   ARCHEAD_KERNEL_TILE = 0,
   ARCHEAD_KERNEL_DECODE_FEW = 1,
-  ARCHEAD_KERNEL_DECODE_STREAM = 2
+  ARCHEAD_KERNEL_DECODE_STREAM = 2,
+  ARCHEAD_KERNEL_DECODE_BATCH = 3
 };
 ARCHEAD_API int archead_main_kernel(const archead_dims* d, int64_t n_tokens, int path, int* kernel);
 

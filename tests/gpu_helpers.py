@@ -7,6 +7,13 @@ import numpy as np
 import oracle
 
 TOL = 2e-3  # max|Y_gpu - Y_ref| <= TOL * max|Y_ref|
+# Every fp32-output path multiplies exact operands (INT4/INT8 codes as fp16
+# integers, H as fp16 times a power of two, Z as a 22-bit hi/lo pair) and
+# accumulates in fp32, so its error is a few fp32 roundings of the logit
+# magnitudes (measured 1e-7 .. 3e-7).  A regression guard well above that: a
+# stale register, a lost term or a one-sided rounding shows up far beyond it
+# while still passing the 2e-3 contract.
+DESIGN_TOL = 1e-5
 
 
 def torch_mod():
@@ -58,6 +65,7 @@ def check_parity(Yg, Yr, what=""):
     rel = err / scale if scale > 0 else err
     log(f"  {what}: max|dY|/max|Y| = {rel:.3e}")
     assert rel <= TOL, f"{what}: {rel:.3e} > {TOL}"
+    assert rel <= DESIGN_TOL, f"{what}: {rel:.3e} is within the 2e-3 contract but above the kernels' design bound"
     ag, ar = np.argmax(Yg, 1), oracle.row_argmax(Yr)
     bad = np.flatnonzero(ag != ar)
     if bad.size:

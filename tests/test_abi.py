@@ -119,6 +119,14 @@ def _few_tokens(V, D, r_c, r_r, g, N):
     return 1 <= N <= 16 and (D // 128) % 4 == 0 and (N + 1) * (D + 8) * 2 + N * (r_c + r_r) * 4 <= 48 * 1024
 
 
+def _batched(V, D, r_c, r_r, g, N):
+    """The batched decode kernel takes the call: 17 to 64 tokens, ranks rounded
+    up to 32 summing to at most 128, at most 64 groups per row, D a multiple
+    of 512."""
+    up32 = lambda x: (x + 31) // 32 * 32
+    return 17 <= N <= 64 and up32(r_c) + up32(r_r) <= 128 and D // g <= 64 and D % 512 == 0
+
+
 def test_workspace_bytes(ah):
     # calls the decode kernel takes (up to 16 tokens whose H fits its LDS,
     # 32-rank steps rc32 + rr32 <= 256) need the partial sums of Z; the tile
@@ -129,11 +137,18 @@ def test_workspace_bytes(ah):
                                            ((151936, 4096, 32, 32, 128), 16, True),
                                            ((128256, 8192, 64, 64, 128), 8, True),
                                            ((128256, 8192, 64, 64, 128), 9, False),
-                                           ((151936, 4096, 64, 64, 128), 4096, False), ((64, 128, 0, 0, 32), 17, False)]:
+                                           ((151936, 4096, 64, 64, 128), 4096, False), ((64, 128, 0, 0, 32), 17, False),
+                                           ((64, 512, 0, 0, 32), 17, True),
+                                           ((151936, 4096, 32, 32, 128), 64, True),
+                                           ((151936, 4096, 32, 32, 128), 65, False),
+                                           ((1024, 256, 64, 96, 64), 17, False),
+                                           ((1000, 4096, 16, 16, 64), 40, True),
+                                           ((1000, 4096, 16, 16, 32), 63, False)]:
         up = lambda x: (x + 255) // 256 * 256
         if not decode:
             want = _tile_workspace(V, D, r_c, r_r, g, N)
-        elif _few_tokens(V, D, r_c, r_r, g, N):  # converted H [N][D] fp16, its scales, Z [N][r] fp32
+        elif _few_tokens(V, D, r_c, r_r, g, N) or _batched(V, D, r_c, r_r, g, N):
+            # converted H [N][D] fp16, its scales, Z [N][r] fp32
             want = up(N * D * 2) + up(N * 4) + up(N * (r_c + r_r) * 4)
         else:  # Z partial sums per element: slices of 8 k-tiles, padded to 4
             zst = (-(-(D // 128) // 8) + 3) // 4 * 4
@@ -143,7 +158,8 @@ def test_workspace_bytes(ah):
         assert ah.archead_workspace_bytes_path(V, D, r_c, r_r, g, N, 1) == want
         assert ah.archead_workspace_bytes_path(V, D, r_c, r_r, g, N, 2) == _tile_workspace(V, D, r_c, r_r, g, N)
         kern = ("tile32_kernel" if not decode else
-                "small_decode_kernel" if _few_tokens(V, D, r_c, r_r, g, N) else "decode_kernel")
+                "small_decode_kernel" if _few_tokens(V, D, r_c, r_r, g, N) else
+                "batch_kernel" if _batched(V, D, r_c, r_r, g, N) else "decode_kernel")
         assert ah.archead_main_kernel(V, D, r_c, r_r, g, N) == kern, (V, D, N)
         assert ah.archead_main_kernel(V, D, r_c, r_r, g, N, 2) == "tile32_kernel"
         if decode:
@@ -197,7 +213,7 @@ def test_logits_error_paths(ah):
     H, P, Y, need, total = _args(ah, r_r=2048); cases.append((H, P, Y, 0, 3))         # rank cap
     H, P, Y, need, total = _args(ah, V=0); cases.append((H, P, Y, 0, 2))
     H, P, Y, need, total = _args(ah); cases.append((H, P, Y, 7, 3))                    # bad path
-    H, P, Y, need, total = _args(ah, N=17); cases.append((H, P, Y, 1, 3))             # decode kernel: <= 16
+    H, P, Y, need, total = _args(ah, N=65); cases.append((H, P, Y, 1, 3))             # decode path: <= 64
     H, P, Y, need, total = _args(ah, N=9, V=128256, D=8192, r_c=64, r_r=64, g=128)
     cases.append((H, P, Y, 1, 3))                                                       # ... whose H fits LDS
     H, P, Y, need, total = _args(ah); H.data = None; cases.append((H, P, Y, 0, 1))
@@ -225,7 +241,7 @@ def test_stats_workspace_bytes(ah):
                                    ((151936, 4096, 64, 64, 128), 4096), ((64, 128, 0, 0, 32), 17)]:
         pieces = max(64, ((V + 15) // 16 * 16 + 255) // 256)
         want = (ah.archead_workspace_bytes(V, D, r_c, r_r, g, N) + up(N * pieces * 16) +
-                up(N * V * 4 if N <= 16 else 0))
+                up(N * V * 4 if N <= 16 or _batched(V, D, r_c, r_r, g, N) else 0))
         assert ah.archead_stats_workspace_bytes(V, D, r_c, r_r, g, N) == want
     assert ah.archead_stats_workspace_bytes(1024, 256, 16, 8, 64, 0) == 0
 

@@ -35,7 +35,7 @@ def test_full_size_workload(name):
         rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 46, replace=False)]))
     H = device_H(inp.H_bits)
     Yr = oracle.logits(inp.H_bits, inp.head, rows=rows)
-    paths = (0, 2) if N <= 16 else (0,)  # auto = decode kernel up to 16 tokens; forced tile path
+    paths = (0, 2) if N <= 64 else (0,)  # auto = decode path up to 64 tokens; forced tile path
     for path in paths:
         Y = run(head, inp.H_bits, path, "f32", H_dev=H)
         check_parity(to_f64(Y[torch.as_tensor(rows, device="cuda")]), Yr, f"{name} path={path}")

@@ -41,31 +41,44 @@ SHAPES = [
 ]
 
 
+def decode_takes(D, r_c, r_r, g, N):
+    """The decode path's rule for the shapes below: every call of up to 16
+    tokens; 17 to 64 tokens (the batched kernel) when the ranks rounded up to
+    32 sum to at most 128, a row has at most 64 groups and D is a multiple of
+    512."""
+    up32 = lambda x: (x + 31) // 32 * 32
+    return N <= 16 or (N <= 64 and up32(r_c) + up32(r_r) <= 128 and D // g <= 64 and D % 512 == 0)
+
+
 @pytest.mark.parametrize("shape", SHAPES)
-@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 16, 17, 63, 64, 65, 130])
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 16, 17, 24, 33, 48, 63, 64, 65, 130])
 def test_shapes_and_ragged_tails(shape, N):
     V, D, r_c, r_r, g = shape
     log(f"shape V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N}")
     inp = synth.make("tiny", seed=V + N, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=4)
     head = _head(inp)
     Yr = oracle.logits(inp.H_bits, inp.head)
-    paths = (DECODE, TILE) if N <= 16 else (TILE,)
+    dec = decode_takes(D, r_c, r_r, g, N)
+    assert ah_mod().archead_main_kernel(V, D, r_c, r_r, g, N) == (
+        "tile32_kernel" if not dec else "batch_kernel" if N > 16 else
+        ah_mod().archead_main_kernel(V, D, r_c, r_r, g, N, DECODE))
+    paths = (DECODE, TILE) if dec else (TILE,)
     outs = {}
     for path in paths:
         outs[path] = to_f64(run(head, inp.H_bits, path))
         check_parity(outs[path], Yr, f"path={path}")
-    # the auto path takes the decode path up to 16 tokens, else the tile path,
-    # and must give the same bits as the path it takes
+    # the auto path takes the decode path when it can, else the tile path, and
+    # must give the same bits as the path it takes
     auto = to_f64(run(head, inp.H_bits, 0))
-    assert np.array_equal(auto, outs[DECODE if N <= 16 else TILE])
-    if N > 16:  # the decode kernel takes at most 16 tokens: a forced decode path is refused
+    assert np.array_equal(auto, outs[DECODE if dec else TILE])
+    if not dec:  # a forced decode path it does not take is refused
         with pytest.raises(ah_mod().ArcheadError, match="UNSUPPORTED"):
             run(head, inp.H_bits, DECODE)
 
 
-# More groups per row than the tile kernel's group-code table holds (D/g > 64):
-# the decode kernel reads the group codes with every tile and takes them; the
-# tile path refuses them.
+# More groups per row than the tile and batched kernels' group-code tables hold
+# (D/g > 64): the decode kernel for up to 16 tokens reads the group codes with
+# every tile and takes them; the other paths refuse them.
 MANY_GROUPS = [(1000, 4096, 16, 16, 32), (600, 8192, 16, 8, 64)]
 
 
@@ -82,6 +95,23 @@ def test_many_groups_per_row_decode(shape, N):
     assert np.array_equal(to_f64(run(head, inp.H_bits, 0)), Yd)
     with pytest.raises(ah_mod().ArcheadError, match="UNSUPPORTED"):
         run(head, inp.H_bits, TILE)
+    for n in (17, 64):  # past 16 tokens: no path takes such a head
+        with pytest.raises(ah_mod().ArcheadError, match="UNSUPPORTED"):
+            run(head, np.repeat(inp.H_bits[:1], n, axis=0), 0)
+
+
+# 64 groups per row (D/g = 64) and D = 8192 on the batched kernel
+@pytest.mark.parametrize("N", [17, 40, 64])
+def test_batched_deep_rows(N):
+    V, D, r_c, r_r, g = 700, 8192, 32, 32, 128
+    log(f"batched deep rows V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N}")
+    inp = synth.make("tiny", seed=N + 7, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=8)
+    head = _head(inp)
+    assert ah_mod().archead_main_kernel(V, D, r_c, r_r, g, N) == "batch_kernel"
+    Yr = oracle.logits(inp.H_bits, inp.head)
+    Yd = to_f64(run(head, inp.H_bits, DECODE))
+    check_parity(Yd, Yr, "batched D=8192")
+    check_parity(to_f64(run(head, inp.H_bits, TILE)), Yr, "tile D=8192")
 
 
 LARGE_N_SHAPES = [
@@ -109,13 +139,15 @@ def test_large_n_tiles(shape, N):
     assert np.array_equal(to_f64(run(head, inp.H_bits, 0)), Yt)
 
 
-@pytest.mark.parametrize("path,rows", [(DECODE, 64), (TILE, 64), (TILE, 256)])
+@pytest.mark.parametrize("path,rows,step", [(DECODE, 64, 16), (DECODE, 64, 64), (DECODE, 60, 20),
+                                            (TILE, 64, 64), (TILE, 256, 256)])
 @pytest.mark.parametrize("g", [32, 64, 128, 256])
-def test_one_hot_rows_recover_weights_bit_exactly(path, g, rows):
+def test_one_hot_rows_recover_weights_bit_exactly(path, g, rows, step):
     """H = unit rows e_k, r_c = r_r = 0: Y[n, v] = q4[v,k] * c8[v,k//g] * s_R[v],
     a single product of exact operands, so the GPU must return it exactly.
-    The tile path takes 64 or 256 rows per call (its two token-tile sizes),
-    the decode kernel 16 per call (64 rows in four calls)."""
+    The tile path takes 64 or 256 rows per call (its two token-tile sizes);
+    the decode path 16 per call (its k-tile-major kernel), or 64 or 20 (its
+    batched kernel)."""
     V, D = 300, 512
     inp = synth.make("tiny", seed=g, V=V, D=D, N=1, r_c=0, r_r=0, g=g)
     h = inp.head
@@ -136,7 +168,6 @@ def test_one_hot_rows_recover_weights_bit_exactly(path, g, rows):
     eye[np.arange(ks.size), ks] = 1.0
     Hb = synth.f32_to_bf16_bits(eye)
     head = _head(inp)
-    step = 16 if path == DECODE else ks.size
     Y = np.concatenate([run(head, Hb[i:i + step], path).cpu().numpy() for i in range(0, ks.size, step)])
     R = oracle.dequant_R(h.q4, h.c8, h.s_R, g)          # exact in fp64 and fp32
     want = R[:, ks].T.astype(np.float32)
@@ -145,40 +176,42 @@ def test_one_hot_rows_recover_weights_bit_exactly(path, g, rows):
     assert np.array_equal(Y, want), f"max diff {np.abs(Y.astype(np.float64) - R[:, ks].T).max()}"
 
 
-@pytest.mark.parametrize("path", [DECODE, TILE])
-def test_low_rank_only_and_zero_head(path):
-    inp = synth.make("tiny", seed=5, V=600, D=256, N=8, r_c=16, r_r=24, g=64)
+@pytest.mark.parametrize("path,N", [(DECODE, 8), (DECODE, 40), (TILE, 8)])
+def test_low_rank_only_and_zero_head(path, N):
+    D = 512  # a multiple of 512: the batched kernel takes the 40-token call
+    inp = synth.make("tiny", seed=5, V=600, D=D, N=N, r_c=16, r_r=24, g=64)
     inp.head.q4[:] = 0
     head = _head(inp)
     check_parity(to_f64(run(head, inp.H_bits, path)), oracle.logits(inp.H_bits, inp.head), "low-rank only")
-    z = synth.zero_head(600, 256, 16, 24, 64)
+    z = synth.zero_head(600, D, 16, 24, 64)
     Yz = to_f64(run(_head(synth.Inputs(inp.H_bits, z)), inp.H_bits, path))
     assert not Yz.any()
 
 
-@pytest.mark.parametrize("path", [DECODE, TILE])
-def test_hidden_state_edge_values(path):
+@pytest.mark.parametrize("path,N", [(DECODE, 6), (DECODE, 21), (TILE, 6)])
+def test_hidden_state_edge_values(path, N):
     """All-zero rows, a row of tiny values, a row with a single huge value,
     and bf16 subnormals: the per-token fp16 scaling keeps them in range."""
-    inp = synth.make("tiny", seed=9, V=400, D=256, N=6, r_c=8, r_r=8, g=64)
+    D = 512
+    inp = synth.make("tiny", seed=9, V=400, D=D, N=N, r_c=8, r_r=8, g=64)
     H = inp.H_bits.copy()
     H[0] = 0
-    H[1] = synth.f32_to_bf16_bits(np.full(256, 3e-30, np.float32))
+    H[1] = synth.f32_to_bf16_bits(np.full(D, 3e-30, np.float32))
     H[2] = 0
     H[2, 17] = synth.f32_to_bf16_bits(np.array([1e30], np.float32))[0]
-    H[3] = synth.f32_to_bf16_bits(np.full(256, 5e4, np.float32) * np.sign(np.arange(256) - 127.5))
+    H[3] = synth.f32_to_bf16_bits(np.full(D, 5e4, np.float32) * np.sign(np.arange(D) - 255.5))
     H[4, ::3] = 0x0001                               # bf16 subnormals
     head = _head(inp)
     Yr = oracle.logits(H, inp.head)
     Yg = to_f64(run(head, H, path))
     assert not np.isnan(Yg).any()
-    for n in range(6):
+    for n in range(N):
         scale = np.abs(Yr[n]).max()
         err = np.abs(Yg[n] - Yr[n]).max()
         assert err <= 2e-3 * scale or (scale == 0 and err == 0), (n, err, scale)
 
 
-@pytest.mark.parametrize("path,N", [(DECODE, 13), (TILE, 33)])
+@pytest.mark.parametrize("path,N", [(DECODE, 13), (DECODE, 50), (TILE, 33)])
 def test_deterministic(path, N):
     inp = synth.make("tiny", seed=3, V=2000, D=512, N=N, r_c=16, r_r=16, g=128)
     head = _head(inp)
@@ -187,26 +220,28 @@ def test_deterministic(path, N):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("path,N", [(DECODE, 12), (TILE, 20)])
+@pytest.mark.parametrize("path,N", [(DECODE, 12), (DECODE, 45), (TILE, 20)])
 def test_bf16_output_is_rounded_fp32_output(path, N):
     torch = torch_mod()
-    inp = synth.make("tiny", seed=11, V=1500, D=256, N=N, r_c=16, r_r=8, g=64)
+    inp = synth.make("tiny", seed=11, V=1500, D=512, N=N, r_c=16, r_r=8, g=64)
     head = _head(inp)
     y32 = run(head, inp.H_bits, path, "f32")
     y16 = run(head, inp.H_bits, path, "bf16")
     assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), y16.view(torch.int16))
 
 
-def test_row_strides_and_offsets():
+@pytest.mark.parametrize("N", [10, 30])
+def test_row_strides_and_offsets(N):
     """H and Y as row-strided views into larger buffers."""
     torch = torch_mod()
     ah = ah_mod()
-    inp = synth.make("tiny", seed=13, V=500, D=256, N=10, r_c=8, r_r=8, g=64)
+    D = 512
+    inp = synth.make("tiny", seed=13, V=500, D=D, N=N, r_c=8, r_r=8, g=64)
     head = _head(inp)
-    Hbig = torch.zeros((10, 256 + 64), dtype=torch.bfloat16, device="cuda")
-    Hbig[:, 8:8 + 256] = device_H(inp.H_bits)
-    H = Hbig[:, 8:8 + 256]
-    Ybig = torch.full((10, 700), float("nan"), device="cuda")
+    Hbig = torch.zeros((N, D + 64), dtype=torch.bfloat16, device="cuda")
+    Hbig[:, 8:8 + D] = device_H(inp.H_bits)
+    H = Hbig[:, 8:8 + D]
+    Ybig = torch.full((N, 700), float("nan"), device="cuda")
     Y = Ybig[:, 100:600]
     Yr = oracle.logits(inp.H_bits, inp.head)
     for path in (DECODE, TILE):
