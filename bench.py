@@ -36,6 +36,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 KERNEL_SOURCES = {
     "decode_kernel": ["decode.hip", "device_common.h", "internal.h"],
     "small_decode_kernel": ["decode_small.hip", "device_common.h", "internal.h"],
+    "batch_kernel": ["batch.hip", "device_common.h", "internal.h"],
     "tile32_kernel": ["tile.hip", "tile32.h", "rowstat.h", "device_common.h", "internal.h"],
 }
 
