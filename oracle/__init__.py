@@ -8,4 +8,6 @@ from .archead_oracle import (  # noqa: F401
     w_hat, logits, row_argmax, top2_gap, row_stats, row_topk,
     quant_int8_rows, quant_int8_groups, quant_sc4, core_residual, quantize,
     damped_covariance, metric_transform, rsvd, metric_objective, fit, logit_error,
+    ALT_FORMAT, ALT_PERM8, alt_persistent_bytes, pack_alt, unpack_alt, w_hat_alt, logits_alt,
+    quant_group_int4,
 )

@@ -80,23 +80,33 @@ def _up(x, a):
     return (x + a - 1) // a * a
 
 
-def layout(V, D, r_c, r_r, g):
-    """Offsets and sizes of every section of the packed buffer (see FORMAT)."""
+def layout(V, D, r_c, r_r, g, fmt=0):
+    """Offsets and sizes of every section of the packed buffer (see FORMAT;
+    fmt 1 and 2 are the comparison heads of ALT_FORMAT)."""
     if V < 1 or D < 128 or D % 128 or g < 2 or g % 2 or D % g or r_c < 0 or r_r < 0:
         raise ValueError("unsupported dims")
+    if fmt not in (0, 1, 2) or (fmt and (r_c or r_r)):
+        raise ValueError("unsupported format")
     V16 = _up(V, 16)
     r = r_c + r_r
     ng = D // g
     nA = int(r_c > 0) + int(r_r > 0)
-    sizes = dict(
-        r_codes=V16 * D // 2,
-        r_gcodes=V16 * ng,
-        r_rowscale=2 * V16,
-        a_codes=V16 * r,
-        a_scales=2 * V16 * nA,
-        b_codes=r * D,
-        b_scales=2 * r * ng,
-    )
+    if fmt == 0:
+        sizes = dict(
+            r_codes=V16 * D // 2,
+            r_gcodes=V16 * ng,
+            r_rowscale=2 * V16,
+            a_codes=V16 * r,
+            a_scales=2 * V16 * nA,
+            b_codes=r * D,
+            b_scales=2 * r * ng,
+        )
+    else:
+        sizes = {name: 0 for name in _SECTIONS}
+        if fmt == 1:
+            sizes.update(r_codes=V16 * D // 2, r_gcodes=2 * V16 * ng)
+        else:
+            sizes.update(r_codes=V16 * D, r_rowscale=2 * V16)
     out = dict(header=(0, HEADER_BYTES))
     off = _up(HEADER_BYTES, ALIGN)
     for name in _SECTIONS:
@@ -309,6 +319,171 @@ def _w_hat_rows(head, cols):
     if head.r_r:
         W += dequant_rows(head.A_w[cols], head.s_Aw[cols]) @ dequant_groups(head.B_w, head.s_Bw, g)
     return W
+
+
+# ------------------------------------------------------- comparison heads ---
+#
+# The storage-matched heads the pages set beside ARCHead (ARCHead, results
+# discussion of Table 7: a GPTQ-style INT4 head at 25.78% of the BF16 head's
+# storage; of Table 8: a row-INT8 head, more accurate but about twice the
+# storage).  The page gives their storage, not their bytes; ALT_FORMAT is the
+# reading taken, in the same container as FORMAT.
+
+ALT_FORMAT = """
+Comparison heads, format field f of the header's flags word (bytes 36..39),
+r_c = r_r = 0, same header and 256-byte section alignment as FORMAT; sections
+not listed are empty.
+  f = 1, group INT4 with fp16 group scales (symmetric, no zero point):
+   r_codes    the INT4 tiles of FORMAT (same byte positions);
+   r_gcodes   V16*ng fp16, row-major: v*ng + t = scale of row v, group t.
+   W_hat[v,k] = q4[v,k] * s_G[v, k//g]
+   storage: 4 bits per weight + 16 bits per group = (4 + 16/g)/16 of BF16.
+  f = 2, row INT8:
+   r_codes    nkt*nb tiles of 2048 B, k-tile major: tile (b, kt) starts at
+              (kt*nb + b)*2048.  In tile (b, kt), byte 32*l + 8*s + p
+              (l in [0,64), s in [0,4), p in [0,8)) holds the INT8 code of row
+              v = 16*b + (l mod 16) at k = 128*kt + 32*s + 8*(l div 16) + P[p],
+              P = (0, 1, 4, 5, 2, 3, 6, 7).
+   r_rowscale V16 fp16: s[v].
+   W_hat[v,k] = q8[v,k] * s[v]
+   storage: 8 bits per weight + 16 bits per row = (8 + 16/D)/16 of BF16.
+"""
+
+ALT_PERM8 = (0, 1, 4, 5, 2, 3, 6, 7)
+
+
+def alt_persistent_bytes(V, D, g, fmt):
+    """Sum of numel x element size over a comparison head's stored tensors
+    (V a multiple of 16)."""
+    if fmt == 1:
+        return V * D // 2 + 2 * V * (D // g)
+    if fmt == 2:
+        return V * D + 2 * V
+    raise ValueError(fmt)
+
+
+def _bytes_to_tiles8(q8):
+    """[V16, D] int8 codes -> row-INT8 tile bytes (ALT_FORMAT f = 2).  Writing
+    k = 128*kt + 32*s + 8*q + P[p] and v = 16*b + i, the byte order is
+    (kt, b, q, i, s, p); lane l = 16*q + i."""
+    V16, D = q8.shape
+    t = q8.reshape(V16 // 16, 16, D // 128, 4, 4, 8)             # b i kt s q j
+    t = t[..., list(ALT_PERM8)]                                    # byte p holds column P[p]
+    t = t.transpose(2, 0, 4, 1, 3, 5)                              # kt b q i s p
+    return np.ascontiguousarray(t).view(np.uint8).reshape(-1)
+
+
+def _tiles8_to_bytes(raw, V16, D):
+    """Inverse of ``_bytes_to_tiles8``."""
+    t = np.asarray(raw, np.uint8).view(np.int8).reshape(D // 128, V16 // 16, 4, 16, 4, 8)   # kt b q i s p
+    t = t.transpose(1, 3, 0, 4, 2, 5)                              # b i kt s q p
+    out = np.empty_like(t)
+    out[..., list(ALT_PERM8)] = t                                  # column P[p] from byte p
+    return out.reshape(V16, D)
+
+
+def _header(V, D, r_c, r_r, g, flags):
+    hdr = np.zeros(HEADER_BYTES, np.uint8)
+    hdr[0:4] = np.frombuffer(np.uint32(MAGIC).tobytes(), np.uint8)
+    hdr[4:8] = np.frombuffer(np.uint32(FORMAT_VERSION).tobytes(), np.uint8)
+    hdr[8:16] = np.frombuffer(np.uint64(V).tobytes(), np.uint8)
+    hdr[16:24] = np.frombuffer(np.uint64(D).tobytes(), np.uint8)
+    hdr[24:28] = np.frombuffer(np.uint32(r_c).tobytes(), np.uint8)
+    hdr[28:32] = np.frombuffer(np.uint32(r_r).tobytes(), np.uint8)
+    hdr[32:36] = np.frombuffer(np.uint32(g).tobytes(), np.uint8)
+    hdr[36:40] = np.frombuffer(np.uint32(flags).tobytes(), np.uint8)
+    return hdr
+
+
+def pack_alt(head) -> np.ndarray:
+    """Serialise a comparison head (attributes fmt, V, D, g, codes, scales) into
+    ALT_FORMAT.  fmt 1: codes [V, D] in [-8, 7], scales [V, D/g] fp16; fmt 2:
+    codes [V, D] in [-127, 127], scales [V] fp16."""
+    V, D, g, fmt = head.V, head.D, head.g, head.fmt
+    L = layout(V, D, 0, 0, g, fmt)
+    V16 = L["V16"]
+    buf = np.zeros(L["total_bytes"], np.uint8)
+    buf[0:HEADER_BYTES] = _header(V, D, 0, 0, g, fmt)
+
+    def put(name, arr):
+        off, size = L[name]
+        raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+        assert raw.size == size, (name, raw.size, size)
+        buf[off:off + size] = raw
+
+    q = np.zeros((V16, D), np.int8)
+    q[:V] = head.codes
+    if fmt == 1:
+        if q.min() < -8 or q.max() > 7:
+            raise ValueError("INT4 code out of range")
+        put("r_codes", _nibbles_to_tiles(q.view(np.uint8) & 0xF))
+        sg = np.zeros((V16, D // g), np.float16)
+        sg[:V] = head.scales
+        put("r_gcodes", sg)
+    else:
+        if q.min() < -127:
+            raise ValueError("INT8 code out of range")
+        put("r_codes", _bytes_to_tiles8(q))
+        sr = np.zeros(V16, np.float16)
+        sr[:V] = head.scales
+        put("r_rowscale", sr)
+    return buf
+
+
+def unpack_alt(buf, V, D, g, fmt) -> dict:
+    """Read a comparison head back out of its packed buffer."""
+    L = layout(V, D, 0, 0, g, fmt)
+    V16 = L["V16"]
+    buf = np.asarray(buf, np.uint8)
+
+    def get(name, dtype):
+        off, size = L[name]
+        return buf[off:off + size].view(dtype)
+
+    hdr = buf[:HEADER_BYTES]
+    out = dict(magic=int(hdr[0:4].view(np.uint32)[0]), flags=int(hdr[36:40].view(np.uint32)[0]))
+    if fmt == 1:
+        q = _tiles_to_nibbles(get("r_codes", np.uint8), V16, D).astype(np.int8)
+        q[q >= 8] -= 16
+        out.update(codes=q[:V], scales=get("r_gcodes", np.float16).reshape(V16, D // g)[:V])
+    else:
+        q = _tiles8_to_bytes(get("r_codes", np.uint8), V16, D)
+        out.update(codes=q[:V], scales=get("r_rowscale", np.float16)[:V])
+    return out
+
+
+def w_hat_alt(head, v0=0, v1=None):
+    """Rows v0..v1 of a comparison head's W_hat (fp64, exact)."""
+    v1 = head.V if v1 is None else v1
+    q = head.codes[v0:v1].astype(np.float64)
+    if head.fmt == 1:
+        return q * np.repeat(f16_to_f64(head.scales[v0:v1]), head.g, axis=1)
+    return q * f16_to_f64(head.scales[v0:v1])[:, None]
+
+
+def logits_alt(H_bits, head, rows=None, v_chunk=8192):
+    """Y_ref = H W_hat^T of a comparison head in fp64."""
+    H = bf16_bits_to_f64(H_bits if rows is None else H_bits[rows])
+    Y = np.empty((H.shape[0], head.V), np.float64)
+    for v0 in range(0, head.V, v_chunk):
+        v1 = min(head.V, v0 + v_chunk)
+        Y[:, v0:v1] = H @ w_hat_alt(head, v0, v1).T
+    return Y
+
+
+def quant_group_int4(M32, g):
+    """Group-wise (g columns) symmetric INT4 with fp16 scales, the reading of
+    the GPTQ-style head's storage with round-to-nearest codes:
+    s = fp16(amax / 7), code = clamp(rint(x / s), -8, 7), 0 where s = 0
+    (decisions in fp32).  Returns (codes int8 [n, D], scales fp16 [n, D/g])."""
+    M32 = np.asarray(M32, np.float32)
+    n, D = M32.shape
+    G = M32.reshape(n * (D // g), g)
+    s = (np.abs(G).max(axis=1) / np.float32(7)).astype(np.float16)
+    s32 = s.astype(np.float32)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s32 > 0, np.rint(G / np.where(s32 > 0, s32, np.float32(1))), 0)
+    return np.clip(q, -8, 7).astype(np.int8).reshape(n, D), s.reshape(n, D // g)
 
 
 # -------------------------------------------------------------- statistics ---

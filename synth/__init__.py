@@ -137,6 +137,41 @@ def draw_head(rng, V, D, r_c, r_r, g) -> Head:
 
 
 @dataclass
+class AltHead:
+    """A storage-matched comparison head, unpacked.  fmt 1 (group INT4 with
+    fp16 group scales): codes [V, D] int8 in [-8, 7], scales [V, D/g] float16.
+    fmt 2 (row INT8): codes [V, D] int8 in [-127, 127], scales [V] float16."""
+    fmt: int
+    V: int
+    D: int
+    g: int
+    codes: np.ndarray
+    scales: np.ndarray
+
+
+def draw_alt_head(rng, fmt, V, D, g) -> AltHead:
+    """Codes uniform over their range; fp16 scales |N(0, 1e-2)| per group
+    (fmt 1) or |N(0, 1e-3)| per row (fmt 2).  Draw order: codes, scales."""
+    if fmt == 1:
+        codes = rng.integers(-8, 8, size=(V, D), dtype=np.int8)
+        scales = _abs_normal_f16(rng, 1e-2, (V, D // g))
+    elif fmt == 2:
+        codes = rng.integers(-127, 128, size=(V, D), dtype=np.int8)
+        scales = _abs_normal_f16(rng, 1e-3, V)
+    else:
+        raise ValueError(fmt)
+    return AltHead(fmt, V, D, g, codes, scales)
+
+
+def make_alt(fmt, seed, V, D, N, g, n_outlier=4, outlier_scale=20.0):
+    """Hidden states (drawn first, as in ``make``) and a comparison head of
+    format ``fmt`` from one seeded stream.  Returns (H_bits, head)."""
+    rng = np.random.default_rng(seed)
+    H_bits, _ = draw_hidden(rng, N, D, n_outlier, outlier_scale)
+    return H_bits, draw_alt_head(rng, fmt, V, D, g)
+
+
+@dataclass
 class Dense:
     """Dense inputs of the packing step: the head W and the factor matrices."""
     W: np.ndarray      # [V, D] bf16 bit patterns (uint16) or float32

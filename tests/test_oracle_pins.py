@@ -840,3 +840,159 @@ def test_fit_pin_rejects_plausible_mistakes(monkeypatch, mutant):
     monkeypatch.setattr(oracle.archead_oracle, "metric_transform", real)
     dJ, dP = _correction_gap(case, f)
     assert dJ > 1e-2 and dP > 1e-2, (mutant, dJ, dP)
+
+
+# -------------------------------------------------------- comparison heads ---
+# The storage-matched heads set beside ARCHead (results discussion of Tables 7
+# and 8): group INT4 with fp16 group scales (format 1) and row INT8 (format 2).
+
+def _alt_header_bytes(d, flags):
+    return np.frombuffer(np.array([0x48435241, 1], np.uint32).tobytes() +
+                         np.array([d["V"], d["D"]], np.uint64).tobytes() +
+                         np.array([0, 0, d["g"], flags], np.uint32).tobytes(), np.uint8)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_alt_golden_positions(golden_dir, fmt):
+    G = json.load(open(os.path.join(golden_dir, "format_alt_cases.json")))[f"f{fmt}"]
+    d = G["dims"]
+    L = oracle.layout(d["V"], d["D"], 0, 0, d["g"], fmt)
+    for name, (off, size) in G["sections"].items():
+        assert tuple(L[name]) == (off, size), name
+    assert L["total_bytes"] == G["total_bytes"] and L["payload_bytes"] == G["payload_bytes"]
+    V, D, g = d["V"], d["D"], d["g"]
+    codes = np.zeros((V, D), np.int8)
+    scales = np.zeros((V, D // g) if fmt == 1 else V, np.float16)
+    expect = {}
+    if fmt == 1:
+        for c in G["nibbles"]:
+            codes[c["v"], c["k"]] = c["code"]
+            nib = c["code"] & 0xF
+            expect[c["byte"]] = expect.get(c["byte"], 0) | (nib if c["half"] == "lo" else nib << 4)
+        for c in G["group_scales"]:
+            scales.view(np.uint16)[c["v"], c["t"]] = c["f16_bits"]
+            expect[c["byte"]] = c["f16_bits"] & 0xFF
+            expect[c["byte"] + 1] = c["f16_bits"] >> 8
+            assert float(_f16_exact(c["f16_bits"])) == c["value"]
+    else:
+        for c in G["codes"]:
+            codes[c["v"], c["k"]] = c["code"]
+            expect[c["byte"]] = c["code"] & 0xFF
+        for c in G["row_scale"]:
+            scales.view(np.uint16)[c["v"]] = c["f16_bits"]
+            expect[c["byte"]] = c["f16_bits"] & 0xFF
+            expect[c["byte"] + 1] = c["f16_bits"] >> 8
+    for i, b in enumerate(_alt_header_bytes(d, fmt)):
+        expect[i] = int(b)
+    buf = oracle.pack_alt(synth.AltHead(fmt, V, D, g, codes, scales))
+    assert buf.size == G["total_bytes"]
+    nz = {int(i): int(buf[i]) for i in np.flatnonzero(buf)}
+    assert nz == {k: v for k, v in expect.items() if v}
+
+
+def _tile8_pack_loop(q8_padded):
+    """Element-by-element reading of the row-INT8 tile order (tiny shapes only)."""
+    V16, D = q8_padded.shape
+    out = np.zeros(V16 * D, np.uint8)
+    nb = V16 // 16
+    P = (0, 1, 4, 5, 2, 3, 6, 7)
+    for v in range(V16):
+        for k in range(D):
+            b, i = divmod(v, 16)
+            kt, kk = divmod(k, 128)
+            s, rem = divmod(kk, 32)
+            q, j = divmod(rem, 8)
+            pos = (kt * nb + b) * 2048 + 32 * (16 * q + i) + 8 * s + P.index(j)
+            out[pos] = int(q8_padded[v, k]) & 0xFF
+    return out
+
+
+@pytest.mark.parametrize("V,D", [(16, 128), (33, 256)])
+def test_alt_tile8_order_matches_loop(V, D):
+    _, h = synth.make_alt(2, V + D, V, D, 1, 64)
+    L = oracle.layout(V, D, 0, 0, 64, 2)
+    q = np.zeros((L["V16"], D), np.int8)
+    q[:V] = h.codes
+    off, size = L["r_codes"]
+    assert np.array_equal(oracle.pack_alt(h)[off:off + size], _tile8_pack_loop(q))
+
+
+@pytest.mark.parametrize("fmt,V,D,g", [(1, 100, 512, 64), (1, 37, 256, 128), (2, 100, 512, 64), (2, 9, 384, 32)])
+def test_alt_pack_unpack_roundtrip(fmt, V, D, g):
+    _, h = synth.make_alt(fmt, 7, V, D, 1, g)
+    u = oracle.unpack_alt(oracle.pack_alt(h), V, D, g, fmt)
+    assert u["magic"] == 0x48435241 and u["flags"] == fmt
+    assert np.array_equal(u["codes"], h.codes)
+    assert np.array_equal(u["scales"].view(np.uint16), h.scales.view(np.uint16))
+
+
+def test_alt_storage_matches_pages():
+    """Table 7 discussion: the GPTQ-style INT4 head takes 25.78% of the BF16
+    head (4 bits per weight + one fp16 scale per 128); Table 8 discussion: row
+    INT8 takes about twice the storage of the 25.6% ARCHead head."""
+    V, D = 151936, 4096
+    f1 = oracle.alt_persistent_bytes(V, D, 128, 1)
+    assert f1 / (2 * V * D) == (4 + 16 / 128) / 16 == 0.2578125
+    assert round(100 * f1 / (2 * V * D), 2) == 25.78
+    f2 = oracle.alt_persistent_bytes(V, D, 128, 2)
+    assert f2 / (2 * V * D) == 0.5 + 1 / D
+    ratio = f2 / oracle.persistent_bytes(V, D, 6, 6, 128)
+    assert 1.9 < ratio < 2.0
+    for fmt in (1, 2):  # the layout's payload is the persistent size, and nothing is V x D at 16 bits
+        L = oracle.layout(V, D, 0, 0, 128, fmt)
+        assert L["payload_bytes"] == oracle.alt_persistent_bytes(V, D, 128, fmt)
+        assert L["total_bytes"] < 2 * V * D
+
+
+def test_alt_group_int4_is_sc4_when_scales_factor():
+    """A group scale that is exactly c8 * s_R (s_R a power of two, so the
+    product is exact in fp16) makes the format-1 head the same matrix as the
+    format-0 head with r_c = r_r = 0: two different decode routines of the
+    oracle must agree."""
+    inp = synth.make("tiny", seed=21, V=200, D=256, N=3, r_c=0, r_r=0, g=64)
+    h = inp.head
+    h.s_R[:] = np.float16(2.0 ** -12)
+    sg = (h.c8.astype(np.float64) * 2.0 ** -12).astype(np.float16)
+    assert np.array_equal(sg.astype(np.float64), h.c8.astype(np.float64) * 2.0 ** -12)
+    alt = synth.AltHead(1, h.V, h.D, h.g, h.q4.copy(), sg)
+    Y0 = oracle.logits(inp.H_bits, h)
+    Y1 = oracle.logits_alt(inp.H_bits, alt)
+    assert np.abs(Y0 - Y1).max() <= 1e-12 * np.abs(Y0).max()
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_alt_exact_rational(fmt):
+    """Comparison-head logits against exact integer evaluation."""
+    H_bits, h = synth.make_alt(fmt, 31 + fmt, 40, 256, 3, 64)
+    SH = 133
+    Hi = np.array([[int(_bf16_exact(int(b)) * (1 << SH)) for b in row] for row in H_bits], dtype=object)
+
+    def f16i(a):
+        a = np.asarray(a)
+        return np.array([int(_f16_exact(int(b)) * (1 << 24)) for b in a.view(np.uint16).reshape(-1)],
+                        dtype=object).reshape(a.shape)
+
+    s = f16i(h.scales)
+    Wq = h.codes.astype(object) * (np.repeat(s, h.g, axis=1) if fmt == 1 else s[:, None])
+    exact = np.array([[float(Fraction(int(x), 1 << (SH + 24))) for x in row] for row in Hi.dot(Wq.T)])
+    Y = oracle.logits_alt(H_bits, h)
+    assert np.abs(Y - exact).max() <= 1e-12 * np.abs(exact).max()
+
+
+def test_quant_group_int4_worked_cases():
+    """Worked groups (g = 4): amax 0.7 -> s = fp16(0.1); codes rint(x / s);
+    a group of zeros has scale 0 and codes 0; |code| never passes 7 on the
+    largest element, and -8 is reachable only through rounding below -7.5."""
+    M = np.array([[0.7, -0.35, 0.07, -0.7, 0.0, 0.0, 0.0, 0.0]], np.float32)
+    q, s = oracle.quant_group_int4(M, 4)
+    s0 = np.float32(np.float16(np.float32(0.7) / np.float32(7)))
+    assert s.view(np.uint16)[0, 0] == np.float16(np.float32(0.7) / np.float32(7)).view(np.uint16)
+    assert q[0, :4].tolist() == [int(np.rint(np.float32(x) / s0)) for x in M[0, :4]]
+    assert q[0, 0] == 7 and q[0, 3] == -7
+    assert s[0, 1] == 0 and not q[0, 4:].any()
+    rng = np.random.default_rng(3)
+    R = rng.standard_normal((50, 256)).astype(np.float32)
+    q, s = oracle.quant_group_int4(R, 64)
+    deq = q.astype(np.float32) * np.repeat(s.astype(np.float32), 64, axis=1)
+    assert np.abs(q).max() <= 8
+    assert np.all(np.abs(R - deq) <= 0.5 * np.repeat(s.astype(np.float32), 64, axis=1) * 1.01 + 1e-7)
