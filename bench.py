@@ -36,7 +36,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 KERNEL_SOURCES = {
     "decode_kernel": ["decode.hip", "device_common.h", "internal.h"],
     "small_decode_kernel": ["decode_small.hip", "device_common.h", "internal.h"],
-    "batch_kernel": ["batch.hip", "device_common.h", "internal.h"],
+    "batch_kernel": ["batch.hip", "batch_kernel.h", "device_common.h", "internal.h"],
     "tile32_kernel": ["tile.hip", "tile32.h", "rowstat.h", "device_common.h", "internal.h"],
 }
 
@@ -261,6 +261,57 @@ def run_stats(name, steps, warmup):
 
 
 FP64_PEAK_TFLOPS = 78.6  # MI355X vector fp64
+
+ALT_NAMES = {1: "group_int4", 2: "row_int8"}
+
+
+def run_alt(name, fmt, steps, warmup, archead_ms=None):
+    """archead_logits on a storage-matched comparison head (fmt 1: group INT4
+    with fp16 group scales; fmt 2: row INT8) of one workload's shape (V, D, g,
+    N): K timed whole calls, two copies of the head rotated as in the main
+    workload, and the main kernel's time from the library's events (with more
+    than 32 tokens, the events span every launch of the call and the later
+    launches' conversions)."""
+    import torch
+    import synth
+    import compressed_output_head_amd as ah
+
+    cfg = synth.config(name)
+    V, D, g, N = cfg["V"], cfg["D"], cfg["g"], cfg["N"]
+    H_bits, h = synth.make_alt(fmt, 11 + fmt, V, D, N, g)
+    packed = ah.archead_pack(h)
+    L = ah.archead_pack_layout(V, D, 0, 0, g, fmt)
+    heads = [ah.PackedHead(V, D, 0, 0, g, packed, fmt=fmt)]
+    heads.append(ah.PackedHead(V, D, 0, 0, g, heads[0].buffer.clone(), fmt=fmt))
+    H = torch.from_numpy(H_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    Y = torch.empty((N, V), dtype=torch.bfloat16 if cfg["y_dtype"] == "bf16" else torch.float32, device="cuda")
+    for hd in heads:
+        hd.ensure_workspace(N)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        ah.archead_logits(H, heads[i % 2], Y)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        ah.archead_logits(H, heads[i % 2], Y)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    kms = []
+    for i in range(steps):
+        ah.archead_logits_events(H, heads[i % 2], Y, 0, eb, ee)
+        torch.cuda.synchronize()
+        kms.append(eb.elapsed_time(ee))
+    kernel_ms = float(np.mean(kms))
+    payload = L["payload_bytes"]
+    out = {"workload": name, "format": ALT_NAMES[fmt], "N": N, "ms_per_call": round(ms, 5),
+           "kernel_ms": round(kernel_ms, 5), "launches": (N + 31) // 32, "payload_bytes": payload,
+           "head_gbps": round(payload / (kernel_ms / 1e3) / 1e9, 1) if N <= 32 else None}
+    if archead_ms:
+        out["ms_vs_archead"] = round(ms / archead_ms, 3)
+    return out
 
 
 def run_topk(name, steps, warmup, k=10):
@@ -544,6 +595,9 @@ def main():
     ap.add_argument("--topk", default="batched", help="workload timed through archead_logits_topk, k=10 ('' to skip)")
     ap.add_argument("--fit", default="decode",
                     help="head shape timed through archead_fit, the whole construction ('' to skip)")
+    ap.add_argument("--compare", default="decode,batched",
+                    help="workloads whose shape the two storage-matched comparison heads (group INT4, row INT8) "
+                         "are timed on ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -620,6 +674,15 @@ def main():
         out["workloads"][w] = entry
         if "secondary" not in out:
             out["secondary"] = entry
+    if args.compare:
+        out["comparison_heads"] = {}
+        known = {args.config: r["ms"]} | {w: e["ms_per_step"] for w, e in out.get("workloads", {}).items()
+                                          if "chunk_rows" not in e}
+        for w in [w for w in args.compare.split(",") if w]:
+            for fmt in (1, 2):
+                c = run_alt(w, fmt, max(5, args.steps // 5), 2, known.get(w))
+                log(f"[bench] {ALT_NAMES[fmt]} head on {w}: {c['ms_per_call'] * 1e3:.1f} us/call")
+                out["comparison_heads"][f"{w}/{ALT_NAMES[fmt]}"] = c
     if args.stats:
         st = run_stats(args.stats, max(5, args.steps // 5), max(2, args.warmup // 5))
         log(f"[bench] stats on {args.stats}: {st['ms_per_call']:.3f} ms/call")

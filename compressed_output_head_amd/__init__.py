@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libarchead.so")
 ARCHEAD_OK = 0
 ARCHEAD_BF16, ARCHEAD_F32 = 1, 2
 ARCHEAD_PATH_AUTO, ARCHEAD_PATH_DECODE, ARCHEAD_PATH_TILE = 0, 1, 2
+# storage formats (archead_format): the method's head and the two comparison heads
+ARCHEAD_FMT_ARCHEAD, ARCHEAD_FMT_GROUP_INT4, ARCHEAD_FMT_ROW_INT8 = 0, 1, 2
 # main kernels (archead_main_kernel), by the names the profiler shows
 KERNEL_NAMES = {0: "tile32_kernel", 1: "small_decode_kernel", 2: "decode_kernel", 3: "batch_kernel"}
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_DIMS", 3: "E_UNSUPPORTED", 4: "E_DTYPE", 5: "E_SHAPE",
@@ -42,7 +44,8 @@ class ArcheadError(RuntimeError):
 
 class ArcheadDims(ctypes.Structure):
     _fields_ = [("V", ctypes.c_int64), ("D", ctypes.c_int64),
-                ("r_c", ctypes.c_int32), ("r_r", ctypes.c_int32), ("g", ctypes.c_int32)]
+                ("r_c", ctypes.c_int32), ("r_r", ctypes.c_int32), ("g", ctypes.c_int32),
+                ("format", ctypes.c_int32)]
 
 
 class ArcheadSpan(ctypes.Structure):
@@ -62,7 +65,7 @@ class ArcheadLayout(ctypes.Structure):
 
 class ArcheadHostComponents(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("q4", "c8", "s_R", "A_c", "A_w", "s_Ac", "s_Aw", "B_c", "B_w", "s_Bc", "s_Bw")]
+                ("q4", "c8", "s_R", "A_c", "A_w", "s_Ac", "s_Aw", "B_c", "B_w", "s_Bc", "s_Bw", "s_G", "q8")]
 
 
 class ArcheadTensor(ctypes.Structure):
@@ -146,8 +149,8 @@ def _load():
 lib = _load()
 
 
-def _dims(V, D, r_c, r_r, g) -> ArcheadDims:
-    return ArcheadDims(int(V), int(D), int(r_c), int(r_r), int(g))
+def _dims(V, D, r_c, r_r, g, fmt=ARCHEAD_FMT_ARCHEAD) -> ArcheadDims:
+    return ArcheadDims(int(V), int(D), int(r_c), int(r_r), int(g), int(fmt))
 
 
 def _check(status: int, where: str):
@@ -165,10 +168,10 @@ def archead_format_version() -> int:
     return lib.archead_format_version()
 
 
-def archead_pack_layout(V, D, r_c, r_r, g) -> dict:
+def archead_pack_layout(V, D, r_c, r_r, g, fmt=ARCHEAD_FMT_ARCHEAD) -> dict:
     """Section offsets/sizes of the packed buffer (see include/archead.h)."""
     L = ArcheadLayout()
-    _check(lib.archead_pack_layout(ctypes.byref(_dims(V, D, r_c, r_r, g)), ctypes.byref(L)),
+    _check(lib.archead_pack_layout(ctypes.byref(_dims(V, D, r_c, r_r, g, fmt)), ctypes.byref(L)),
            "archead_pack_layout")
     out = {n: (getattr(L, n).offset, getattr(L, n).bytes) for n in _SECTIONS}
     out.update(total_bytes=L.total_bytes, payload_bytes=L.payload_bytes, header_bytes=L.header_bytes,
@@ -176,38 +179,39 @@ def archead_pack_layout(V, D, r_c, r_r, g) -> dict:
     return out
 
 
-def archead_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
+def archead_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int, fmt=ARCHEAD_FMT_ARCHEAD) -> int:
     b = ctypes.c_uint64()
-    _check(lib.archead_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
+    _check(lib.archead_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g, fmt)), int(n_tokens),
                                        ctypes.byref(b)), "archead_workspace_bytes")
     return b.value
 
 
-def archead_workspace_bytes_path(V, D, r_c, r_r, g, n_tokens: int, path: int) -> int:
+def archead_workspace_bytes_path(V, D, r_c, r_r, g, n_tokens: int, path: int, fmt=ARCHEAD_FMT_ARCHEAD) -> int:
     b = ctypes.c_uint64()
-    _check(lib.archead_workspace_bytes_path(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens), int(path),
+    _check(lib.archead_workspace_bytes_path(ctypes.byref(_dims(V, D, r_c, r_r, g, fmt)), int(n_tokens), int(path),
                                             ctypes.byref(b)), "archead_workspace_bytes_path")
     return b.value
 
 
-def archead_main_kernel(V, D, r_c, r_r, g, n_tokens: int, path: int = ARCHEAD_PATH_AUTO) -> str:
+def archead_main_kernel(V, D, r_c, r_r, g, n_tokens: int, path: int = ARCHEAD_PATH_AUTO,
+                        fmt=ARCHEAD_FMT_ARCHEAD) -> str:
     """Name of the main kernel a call of n_tokens rows on `path` launches."""
     k = ctypes.c_int()
-    _check(lib.archead_main_kernel(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens), int(path),
+    _check(lib.archead_main_kernel(ctypes.byref(_dims(V, D, r_c, r_r, g, fmt)), int(n_tokens), int(path),
                                    ctypes.byref(k)), "archead_main_kernel")
     return KERNEL_NAMES[k.value]
 
 
-def archead_stats_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
+def archead_stats_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int, fmt=ARCHEAD_FMT_ARCHEAD) -> int:
     b = ctypes.c_uint64()
-    _check(lib.archead_stats_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
+    _check(lib.archead_stats_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g, fmt)), int(n_tokens),
                                              ctypes.byref(b)), "archead_stats_workspace_bytes")
     return b.value
 
 
-def archead_topk_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
+def archead_topk_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int, fmt=ARCHEAD_FMT_ARCHEAD) -> int:
     out = ctypes.c_uint64(0)
-    _check(lib.archead_topk_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
+    _check(lib.archead_topk_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g, fmt)), int(n_tokens),
                                             ctypes.byref(out)), "archead_topk_workspace_bytes")
     return out.value
 
@@ -219,19 +223,38 @@ def _ptr(a: Optional[np.ndarray], dtype):
     return a, a.ctypes.data
 
 
+def _head_dims(head):
+    """(V, D, r_c, r_r, g, fmt) of an ARCHead (attributes V, D, r_c, r_r, g) or
+    of a comparison head (attributes fmt, V, D, g; no factors)."""
+    fmt = int(getattr(head, "fmt", ARCHEAD_FMT_ARCHEAD))
+    if fmt == ARCHEAD_FMT_ARCHEAD:
+        return head.V, head.D, head.r_c, head.r_r, head.g, fmt
+    return head.V, head.D, 0, 0, head.g, fmt
+
+
 def archead_pack(head) -> np.ndarray:
-    """Serialise host components (an object with attributes V, D, r_c, r_r, g,
-    q4, c8, s_R, A_c, A_w, s_Ac, s_Aw, B_c, B_w, s_Bc, s_Bw) into a uint8 array."""
-    d = _dims(head.V, head.D, head.r_c, head.r_r, head.g)
-    L = archead_pack_layout(head.V, head.D, head.r_c, head.r_r, head.g)
+    """Serialise host components into a uint8 array: an ARCHead (attributes
+    V, D, r_c, r_r, g, q4, c8, s_R, A_c, A_w, s_Ac, s_Aw, B_c, B_w, s_Bc, s_Bw)
+    or a comparison head (attributes fmt, V, D, g, codes, scales: fmt 1 reads
+    codes as q4 and scales as s_G, fmt 2 codes as q8 and scales as s_R)."""
+    dims = _head_dims(head)
+    d = _dims(*dims)
+    L = archead_pack_layout(*dims)
     out = np.empty(L["total_bytes"], np.uint8)
     keep = []
     comp = ArcheadHostComponents()
-    spec = [("q4", np.int8), ("c8", np.uint8), ("s_R", np.float16), ("A_c", np.int8), ("A_w", np.int8),
-            ("s_Ac", np.float16), ("s_Aw", np.float16), ("B_c", np.int8), ("B_w", np.int8),
-            ("s_Bc", np.float16), ("s_Bw", np.float16)]
-    for name, dt in spec:
-        arr, p = _ptr(getattr(head, name), dt)
+    fmt = dims[5]
+    if fmt == ARCHEAD_FMT_ARCHEAD:
+        spec = [("q4", np.int8, head.q4), ("c8", np.uint8, head.c8), ("s_R", np.float16, head.s_R),
+                ("A_c", np.int8, head.A_c), ("A_w", np.int8, head.A_w), ("s_Ac", np.float16, head.s_Ac),
+                ("s_Aw", np.float16, head.s_Aw), ("B_c", np.int8, head.B_c), ("B_w", np.int8, head.B_w),
+                ("s_Bc", np.float16, head.s_Bc), ("s_Bw", np.float16, head.s_Bw)]
+    elif fmt == ARCHEAD_FMT_GROUP_INT4:
+        spec = [("q4", np.int8, head.codes), ("s_G", np.float16, head.scales)]
+    else:
+        spec = [("q8", np.int8, head.codes), ("s_R", np.float16, head.scales)]
+    for name, dt, val in spec:
+        arr, p = _ptr(val, dt)
         keep.append(arr)
         setattr(comp, name, p)
     _check(lib.archead_pack(ctypes.byref(d), ctypes.byref(comp), out.ctypes.data, out.nbytes), "archead_pack")
@@ -248,10 +271,11 @@ def _torch():
 class PackedHead:
     """A packed head resident in device memory plus a reusable workspace."""
 
-    def __init__(self, V, D, r_c, r_r, g, buffer, device=None):
+    def __init__(self, V, D, r_c, r_r, g, buffer, device=None, fmt=ARCHEAD_FMT_ARCHEAD):
         torch = _torch()
         self.V, self.D, self.r_c, self.r_r, self.g = int(V), int(D), int(r_c), int(r_r), int(g)
-        self.layout = archead_pack_layout(V, D, r_c, r_r, g)
+        self.fmt = int(fmt)
+        self.layout = archead_pack_layout(V, D, r_c, r_r, g, fmt)
         if isinstance(buffer, np.ndarray):
             buffer = torch.from_numpy(buffer).to(device or "cuda")
         if buffer.dtype != torch.uint8 or buffer.numel() < self.layout["total_bytes"]:
@@ -261,11 +285,12 @@ class PackedHead:
 
     @classmethod
     def from_components(cls, head, device="cuda") -> "PackedHead":
-        return cls(head.V, head.D, head.r_c, head.r_r, head.g, archead_pack(head), device=device)
+        V, D, r_c, r_r, g, fmt = _head_dims(head)
+        return cls(V, D, r_c, r_r, g, archead_pack(head), device=device, fmt=fmt)
 
     @property
     def dims(self):
-        return dict(V=self.V, D=self.D, r_c=self.r_c, r_r=self.r_r, g=self.g)
+        return dict(V=self.V, D=self.D, r_c=self.r_c, r_r=self.r_r, g=self.g, fmt=self.fmt)
 
     def ensure_workspace(self, n_tokens: int, stats: bool = False, topk: bool = False, logit_error: bool = False,
                          path: int = ARCHEAD_PATH_AUTO):
@@ -273,16 +298,17 @@ class PackedHead:
         if logit_error or topk or stats:
             size = archead_logit_error_workspace_bytes if logit_error else archead_topk_workspace_bytes if topk \
                 else archead_stats_workspace_bytes
-            need = size(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens)
+            need = size(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens, fmt=self.fmt)
         else:
-            need = archead_workspace_bytes_path(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens, path)
+            need = archead_workspace_bytes_path(self.V, self.D, self.r_c, self.r_r, self.g, n_tokens, path,
+                                                fmt=self.fmt)
         if self.workspace is None or self.workspace.numel() < need:
             self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.buffer.device)
         return self.workspace
 
     def struct(self) -> ArcheadPackedHead:
         ws = self.workspace
-        return ArcheadPackedHead(_dims(self.V, self.D, self.r_c, self.r_r, self.g),
+        return ArcheadPackedHead(_dims(self.V, self.D, self.r_c, self.r_r, self.g, self.fmt),
                                  self.buffer.data_ptr(), self.buffer.numel(),
                                  ws.data_ptr() if ws is not None else None,
                                  ws.numel() if ws is not None else 0)
@@ -478,9 +504,9 @@ def archead_fit(W, H, omega_c, omega_r, r_c: int, r_r: int, g: int, p: float = 0
     return PackedHead(V, D, r_c, r_r, g, buf), f
 
 
-def archead_logit_error_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int) -> int:
+def archead_logit_error_workspace_bytes(V, D, r_c, r_r, g, n_tokens: int, fmt=ARCHEAD_FMT_ARCHEAD) -> int:
     out = ctypes.c_uint64(0)
-    _check(lib.archead_logit_error_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g)), int(n_tokens),
+    _check(lib.archead_logit_error_workspace_bytes(ctypes.byref(_dims(V, D, r_c, r_r, g, fmt)), int(n_tokens),
                                                    ctypes.byref(out)), "archead_logit_error_workspace_bytes")
     return out.value
 

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libarchead.so")
-SOURCES = ["archead.hip", "prep.hip", "decode.hip", "decode_small.hip", "batch.hip", "tile.hip", "tile_stats.hip", "stats.hip",
+SOURCES = ["archead.hip", "prep.hip", "decode.hip", "decode_small.hip", "batch.hip", "batch_g4.hip", "batch_r8.hip", "tile.hip", "tile_stats.hip", "stats.hip",
            "quantize.hip", "topk.hip", "fit.hip", "logit_error.hip"]
 # dense products and factorisations of the construction step
 LINK_LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-lrocsolver"]

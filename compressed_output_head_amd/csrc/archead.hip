@@ -18,9 +18,16 @@ int check_dims(const archead_dims* d) {
   if (d->V < 1 || d->D < kKTile || d->D % kKTile != 0) return ARCHEAD_E_DIMS;
   if (d->g < 2 || d->g % 2 != 0 || d->D % d->g != 0) return ARCHEAD_E_DIMS;
   if (d->r_c < 0 || d->r_r < 0) return ARCHEAD_E_DIMS;
+  if (d->format < ARCHEAD_FMT_ARCHEAD || d->format > ARCHEAD_FMT_ROW_INT8) return ARCHEAD_E_DIMS;
+  if (d->format != ARCHEAD_FMT_ARCHEAD && (d->r_c != 0 || d->r_r != 0)) return ARCHEAD_E_DIMS;
   if (d->V > (int64_t(1) << 31) || d->D > (int64_t(1) << 20)) return ARCHEAD_E_UNSUPPORTED;
   if (d->r_c > (1 << 20) || d->r_r > (1 << 20)) return ARCHEAD_E_UNSUPPORTED;
   return ARCHEAD_OK;
+}
+
+int check_archead_format(const archead_dims* d) {
+  if (!d) return ARCHEAD_E_NULL;
+  return d->format == ARCHEAD_FMT_ARCHEAD ? ARCHEAD_OK : ARCHEAD_E_UNSUPPORTED;
 }
 
 int check_kernel_dims(const archead_dims* d) {
@@ -47,7 +54,14 @@ void compute_layout(const archead_dims* d, archead_layout* L) {
   uint64_t off = round_up(64, ARCHEAD_ALIGNMENT);
   archead_span* spans[7] = {&L->r_codes, &L->r_gcodes, &L->r_rowscale, &L->a_codes,
                             &L->a_scales, &L->b_codes, &L->b_scales};
-  const uint64_t sizes[7] = {V16 * D / 2, V16 * ng, 2 * V16, V16 * r, 2 * V16 * nA, r * D, 2 * r * ng};
+  uint64_t sizes[7] = {V16 * D / 2, V16 * ng, 2 * V16, V16 * r, 2 * V16 * nA, r * D, 2 * r * ng};
+  if (d->format == ARCHEAD_FMT_GROUP_INT4) {  // INT4 tiles and fp16 group scales
+    const uint64_t s1[7] = {V16 * D / 2, 2 * V16 * ng, 0, 0, 0, 0, 0};
+    memcpy(sizes, s1, sizeof(sizes));
+  } else if (d->format == ARCHEAD_FMT_ROW_INT8) {  // INT8 tiles and fp16 row scales
+    const uint64_t s2[7] = {V16 * D, 0, 2 * V16, 0, 0, 0, 0};
+    memcpy(sizes, s2, sizeof(sizes));
+  }
   uint64_t payload = 0;
   for (int i = 0; i < 7; ++i) {
     *spans[i] = {off, sizes[i]};
@@ -62,9 +76,12 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
                                  bool allow_decode) {
   WorkspaceLayout w{};
   const uint64_t n = (uint64_t)std::max<int64_t>(n_tokens, 0);
-  w.small = allow_decode && small_decode_fits(d, n_tokens);
-  w.batch = allow_decode && !w.small && batch_fits(d, n_tokens);
-  w.decode = w.small || w.batch || (allow_decode && decode_fits(d, n_tokens));
+  // a comparison head runs the batched kernel only, up to kAltChunk tokens a launch
+  const bool alt = d->format != ARCHEAD_FMT_ARCHEAD;
+  const int64_t chunk = alt ? std::min<int64_t>(n_tokens, kAltChunk) : n_tokens;
+  w.small = !alt && allow_decode && small_decode_fits(d, n_tokens);
+  w.batch = allow_decode && !w.small && batch_fits(d, alt ? std::max<int64_t>(chunk, 1) : chunk);
+  w.decode = w.small || w.batch || (!alt && allow_decode && decode_fits(d, n_tokens));
   w.rc32 = (int)round_up((uint64_t)d->r_c, 32);
   w.rr32 = (int)round_up((uint64_t)d->r_r, 32);
   w.zsteps = (w.rc32 + w.rr32) / 32;
@@ -83,9 +100,10 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
     w.zscale = take(n32 * 4);
     w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
   } else if (w.small || w.batch) {  // few-token and batched decode kernels: converted H, its scales, Z
-    w.hc = take(n * D * 2);
-    w.hscale = take(n * 4);
-    w.z32 = take(n * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
+    const uint64_t nc = (uint64_t)std::max<int64_t>(chunk, 0);  // rows converted per launch
+    w.hc = take(nc * D * 2);
+    w.hscale = take(nc * 4);
+    w.z32 = take(nc * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
   } else {  // the decode path: partial sums of Z
     w.z32 = take(decode_workspace_bytes(d, n_tokens));
   }
@@ -161,6 +179,7 @@ int archead_workspace_bytes_path(const archead_dims* d, int64_t n_tokens, int pa
   if (rc) return rc;
   if (n_tokens < 0) return ARCHEAD_E_SHAPE;
   if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
+  if (d->format != ARCHEAD_FMT_ARCHEAD && path == ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
   *bytes = workspace_layout(d, n_tokens, false, kSplitBytes, path != ARCHEAD_PATH_TILE).total;
   return ARCHEAD_OK;
 }
@@ -173,6 +192,7 @@ int archead_main_kernel(const archead_dims* d, int64_t n_tokens, int path, int* 
   if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
   const WorkspaceLayout w = workspace_layout(d, n_tokens, false, kSplitBytes, path != ARCHEAD_PATH_TILE);
   if (path == ARCHEAD_PATH_DECODE && !w.decode) return ARCHEAD_E_UNSUPPORTED;
+  if (d->format != ARCHEAD_FMT_ARCHEAD && !w.batch) return ARCHEAD_E_UNSUPPORTED;  // batched kernel only
   *kernel = !w.decode ? ARCHEAD_KERNEL_TILE
             : w.small ? ARCHEAD_KERNEL_DECODE_FEW
             : w.batch ? ARCHEAD_KERNEL_DECODE_BATCH
@@ -189,9 +209,16 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
   if (!d || !src || !dst) return ARCHEAD_E_NULL;
   int rc = check_dims(d);
   if (rc) return rc;
-  if (!src->q4 || !src->c8 || !src->s_R) return ARCHEAD_E_NULL;
-  if (d->r_c > 0 && (!src->A_c || !src->s_Ac || !src->B_c || !src->s_Bc)) return ARCHEAD_E_NULL;
-  if (d->r_r > 0 && (!src->A_w || !src->s_Aw || !src->B_w || !src->s_Bw)) return ARCHEAD_E_NULL;
+  const int fmt = d->format;
+  if (fmt == ARCHEAD_FMT_ARCHEAD) {
+    if (!src->q4 || !src->c8 || !src->s_R) return ARCHEAD_E_NULL;
+    if (d->r_c > 0 && (!src->A_c || !src->s_Ac || !src->B_c || !src->s_Bc)) return ARCHEAD_E_NULL;
+    if (d->r_r > 0 && (!src->A_w || !src->s_Aw || !src->B_w || !src->s_Bw)) return ARCHEAD_E_NULL;
+  } else if (fmt == ARCHEAD_FMT_GROUP_INT4) {
+    if (!src->q4 || !src->s_G) return ARCHEAD_E_NULL;
+  } else if (!src->q8 || !src->s_R) {
+    return ARCHEAD_E_NULL;
+  }
   archead_layout L;
   compute_layout(d, &L);
   if (dst_bytes < L.total_bytes) return ARCHEAD_E_SIZE;
@@ -201,35 +228,67 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
   const int nA = (r_c > 0) + (r_r > 0);
   const int64_t nkt = D / kKTile, nb = V16 / 16;
 
-  // range check of the INT4 codes first, so a failure writes nothing
+  // range check of the codes first, so a failure writes nothing
   std::atomic<bool> bad{false};
   parallel_for(V, [&](int64_t b, int64_t e) {
     for (int64_t v = b; v < e && !bad.load(std::memory_order_relaxed); ++v) {
-      const int8_t* row = src->q4 + v * D;
-      for (int64_t k = 0; k < D; ++k)
-        if (row[k] < -8 || row[k] > 7) {
-          bad = true;
-          break;
-        }
+      if (fmt == ARCHEAD_FMT_ROW_INT8) {
+        const int8_t* row = src->q8 + v * D;
+        for (int64_t k = 0; k < D; ++k)
+          if (row[k] == -128) {
+            bad = true;
+            break;
+          }
+      } else {
+        const int8_t* row = src->q4 + v * D;
+        for (int64_t k = 0; k < D; ++k)
+          if (row[k] < -8 || row[k] > 7) {
+            bad = true;
+            break;
+          }
+      }
     }
   });
   if (bad.load()) return ARCHEAD_E_VALUE;
 
   uint8_t* out = static_cast<uint8_t*>(dst);
   memset(out, 0, L.total_bytes);
-  // header
+  // header; the flags word holds the format
   {
     uint32_t u32[2] = {ARCHEAD_MAGIC, ARCHEAD_FORMAT_VERSION};
     uint64_t u64[2] = {(uint64_t)V, (uint64_t)D};
-    uint32_t u32b[4] = {(uint32_t)r_c, (uint32_t)r_r, (uint32_t)g, 0u};
+    uint32_t u32b[4] = {(uint32_t)r_c, (uint32_t)r_r, (uint32_t)g, (uint32_t)fmt};
     memcpy(out, u32, 8);
     memcpy(out + 8, u64, 16);
     memcpy(out + 24, u32b, 16);
   }
-  // residual tiles, k-tile major: tile (b, kt) at (kt*nb + b)*1024; its byte
+  uint8_t* rcodes = out + L.r_codes.offset;
+  if (fmt == ARCHEAD_FMT_ROW_INT8) {
+    // INT8 tiles, k-tile major: tile (b, kt) at (kt*nb + b)*2048; its byte
+    // 32*l + 8*s + p holds row 16b + l%16, column 128kt + 32s + 8(l/16) + P[p]
+    // with P = (0,1,4,5,2,3,6,7): the fp16 operand slot order of the kernels
+    static const int kPerm8[8] = {0, 1, 4, 5, 2, 3, 6, 7};
+    parallel_for(nb, [&](int64_t b0, int64_t b1) {
+      for (int64_t b = b0; b < b1; ++b)
+        for (int i = 0; i < 16; ++i) {
+          const int64_t v = 16 * b + i;
+          if (v >= V) break;
+          const int8_t* row = src->q8 + v * D;
+          for (int64_t kt = 0; kt < nkt; ++kt) {
+            uint8_t* tile = rcodes + (kt * nb + b) * 2 * kTileBytes;
+            for (int qq = 0; qq < 4; ++qq)
+              for (int st = 0; st < 4; ++st)
+                for (int pp = 0; pp < 8; ++pp)
+                  tile[32 * (16 * qq + i) + 8 * st + pp] = (uint8_t)row[kKTile * kt + 32 * st + 8 * qq + kPerm8[pp]];
+          }
+        }
+    });
+    memcpy(out + L.r_rowscale.offset, src->s_R, 2 * V);
+    return ARCHEAD_OK;
+  }
+  // INT4 tiles, k-tile major: tile (b, kt) at (kt*nb + b)*1024; its byte
   // 16*l + 4*s + c holds row 16b + l%16, columns k = 128kt + 32s + 8(l/16) + 2c
   // (low nibble) and k + 1 (high nibble)
-  uint8_t* rcodes = out + L.r_codes.offset;
   uint8_t* gcodes = out + L.r_gcodes.offset;
   parallel_for(nb, [&](int64_t b0, int64_t b1) {
     for (int64_t b = b0; b < b1; ++b) {
@@ -247,10 +306,14 @@ int archead_pack(const archead_dims* d, const archead_host_components* src, void
                 tile[16 * (16 * qq + i) + 4 * s + c] = (uint8_t)(lo | (hi << 4));
               }
         }
-        memcpy(gcodes + v * ng, src->c8 + v * ng, (size_t)ng);
+        if (fmt == ARCHEAD_FMT_GROUP_INT4)  // fp16 group scales, row-major
+          memcpy(gcodes + 2 * v * ng, src->s_G + v * ng, (size_t)(2 * ng));
+        else
+          memcpy(gcodes + v * ng, src->c8 + v * ng, (size_t)ng);
       }
     }
   });
+  if (fmt == ARCHEAD_FMT_GROUP_INT4) return ARCHEAD_OK;
   memcpy(out + L.r_rowscale.offset, src->s_R, 2 * V);
   int8_t* acodes = reinterpret_cast<int8_t*>(out + L.a_codes.offset);
   uint16_t* ascales = reinterpret_cast<uint16_t*>(out + L.a_scales.offset);
@@ -330,6 +393,7 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
   a.rr32 = W.rr32;
   a.zsteps = W.zsteps;
   a.nA = (d->r_c > 0) + (d->r_r > 0);
+  a.fmt = d->format;
   a.H = static_cast<const uint16_t*>(H->data);
   a.H_stride = H->row_stride;
   a.r_codes = buf + L.r_codes.offset;
@@ -361,6 +425,7 @@ int logits_impl(const archead_tensor* H, const archead_packed_head* head, archea
   if (!H || !head || !Y) return ARCHEAD_E_NULL;
   if (int rc0 = check_kernel_dims(&head->dims)) return rc0;
   if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
+  if (head->dims.format != ARCHEAD_FMT_ARCHEAD && path == ARCHEAD_PATH_TILE) return ARCHEAD_E_UNSUPPORTED;
   if (H->dtype != ARCHEAD_BF16) return ARCHEAD_E_DTYPE;
   if (Y->dtype != ARCHEAD_F32 && Y->dtype != ARCHEAD_BF16) return ARCHEAD_E_DTYPE;
   const int64_t N = H->rows;
@@ -377,6 +442,27 @@ int logits_impl(const archead_tensor* H, const archead_packed_head* head, archea
   a.y_bf16 = Y->dtype == ARCHEAD_BF16;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (head->dims.format != ARCHEAD_FMT_ARCHEAD) {
+    // a comparison head: the batched kernel, kAltChunk tokens a launch, each
+    // launch after the conversion of its own rows (the workspace holds one chunk)
+    if (!W.batch) return ARCHEAD_E_UNSUPPORTED;
+    const int64_t chunk = std::min<int64_t>(N, kAltChunk);
+    if ((uint64_t)(chunk - 1) * (uint64_t)Y->row_stride * ysz + (uint64_t)head->dims.V * ysz >= (1ull << 32))
+      return ARCHEAD_E_UNSUPPORTED;
+    (void)hipGetLastError();  // start from a clean error state
+    for (int64_t c0 = 0; c0 < N; c0 += kAltChunk) {
+      FwdArgs ac = a;
+      ac.N = std::min<int64_t>(kAltChunk, N - c0);
+      ac.H = a.H + c0 * a.H_stride;
+      ac.Y = static_cast<uint8_t*>(Y->data) + (uint64_t)c0 * (uint64_t)Y->row_stride * ysz;
+      if (launch_small_prep(ac, s) != hipSuccess) return ARCHEAD_E_HIP;
+      if (c0 == 0 && ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
+        return ARCHEAD_E_HIP;
+      if (launch_batch(ac, s) != hipSuccess) return ARCHEAD_E_HIP;
+    }
+    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
+    return ARCHEAD_OK;
+  }
   // auto: the decode kernel when it takes the call, else the tile path; the
   // caller may force either (a forced decode path it does not take is an error)
   const bool decode = W.decode;
@@ -431,6 +517,7 @@ int archead_logits_noalloc(const archead_tensor* H, const archead_packed_head* h
                            void* stream) {
   if (!H || !head || !Y) return ARCHEAD_E_NULL;
   if (int rc = check_kernel_dims(&head->dims)) return rc;
+  if (int rc = check_archead_format(&head->dims)) return rc;
   if (H->rows < 0) return ARCHEAD_E_SHAPE;
   if (H->rows == 0) return ARCHEAD_OK;
   // the call's workspace without split-tile partial sums must fit; whatever
@@ -457,8 +544,9 @@ int archead_logits(const archead_tensor* H, const archead_packed_head* head, arc
 
 int archead_stats_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint64_t* bytes) {
   if (!d || !bytes) return ARCHEAD_E_NULL;
-  const int rc = check_dims(d);
+  int rc = check_dims(d);
   if (rc) return rc;
+  if ((rc = check_archead_format(d))) return rc;
   if (n_tokens < 0) return ARCHEAD_E_SHAPE;
   *bytes = workspace_layout(d, n_tokens, true).total;
   return ARCHEAD_OK;
@@ -467,6 +555,7 @@ int archead_stats_workspace_bytes(const archead_dims* d, int64_t n_tokens, uint6
 int archead_logits_stats(const archead_tensor* H, const archead_packed_head* head, const archead_row_stats* out,
                          void* stream) {
   if (!H || !head || !out) return ARCHEAD_E_NULL;
+  if (int rc0 = check_archead_format(&head->dims)) return rc0;
   if (out->row_ce && !out->targets) return ARCHEAD_E_NULL;
   for (const void* p : {(const void*)out->row_max, (const void*)out->row_argmax, (const void*)out->row_lse,
                         (const void*)out->row_ce, (const void*)out->targets})

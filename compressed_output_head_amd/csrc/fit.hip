@@ -192,6 +192,7 @@ FitLayout fit_layout(const archead_dims* d, int oversample) {
 int check_fit(const archead_dims* d, int oversample, archead_layout* L) {
   int rc = archead_pack_layout(d, L);
   if (rc) return rc;
+  if (d->format != ARCHEAD_FMT_ARCHEAD) return ARCHEAD_E_UNSUPPORTED;  // the fit writes an ARCHead-format head
   if (d->g != 32 && d->g != 64 && d->g != 128 && d->g != 256) return ARCHEAD_E_UNSUPPORTED;
   if (d->D > archead::kQuantMaxD || d->r_c > archead::kQuantMaxCoreRank) return ARCHEAD_E_UNSUPPORTED;
   if (oversample < 0) return ARCHEAD_E_SHAPE;

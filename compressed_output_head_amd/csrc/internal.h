@@ -25,6 +25,10 @@ inline uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 int check_dims(const archead_dims* d);
 // Additional limits of the kernels (rank a multiple of 8, g in {32,64,128,256}).
 int check_kernel_dims(const archead_dims* d);
+// E_UNSUPPORTED for a comparison head (entry points that serve the ARCHead format only).
+int check_archead_format(const archead_dims* d);
+// Tokens per launch of the batched kernel for a comparison head.
+constexpr int64_t kAltChunk = 32;
 void compute_layout(const archead_dims* d, archead_layout* L);
 
 // Whether a call with n_tokens rows of H runs the decode kernel (pure host
@@ -62,6 +66,7 @@ struct FwdArgs {
   // dims
   int64_t V, D, N, n32, nb;        // nb = V16/16 row blocks
   int r_c, r_r, g, ng, nkt, nks, rc32, rr32, zsteps, nA;
+  int fmt;                         // archead_format of the packed head
   // input / output
   const uint16_t* H;          // bf16 [N][H_stride]
   int64_t H_stride;

@@ -345,6 +345,7 @@ int archead_quantize(const archead_dims* d, const archead_dense_head* src, void*
   archead_layout L;
   int rc = archead_pack_layout(d, &L);
   if (rc) return rc;
+  if (d->format != ARCHEAD_FMT_ARCHEAD) return ARCHEAD_E_UNSUPPORTED;  // writes an ARCHead-format head
   if (d->g != 32 && d->g != 64 && d->g != 128 && d->g != 256) return ARCHEAD_E_UNSUPPORTED;
   if (d->D > kQuantMaxD || d->r_c > kQuantMaxCoreRank || d->r_r > (1 << 16)) return ARCHEAD_E_UNSUPPORTED;
   if ((d->r_c > 0 && (!src->A_c || !src->B_c)) || (d->r_r > 0 && (!src->A_w || !src->B_w))) return ARCHEAD_E_NULL;

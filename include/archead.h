@@ -26,6 +26,10 @@
  *   - Device pointers must stay valid until the stream has passed the work
  *     enqueued by the call.  Calls on different streams need different
  *     workspaces; the library holds no global state and is re-entrant.
+ *   - The comparison heads (archead_format other than ARCHEAD_FMT_ARCHEAD) are
+ *     served by archead_pack_layout, archead_pack, archead_workspace_bytes(_path),
+ *     archead_main_kernel and archead_logits(_path, _events); every other
+ *     entry point gives E_UNSUPPORTED for them.
  */
 #ifndef ARCHEAD_H
 #define ARCHEAD_H
@@ -49,10 +53,12 @@ extern "C" {
 typedef enum {
   ARCHEAD_OK = 0,
   ARCHEAD_E_NULL = 1,        /* a required pointer is NULL                        */
-  ARCHEAD_E_DIMS = 2,        /* dims are invalid (V<1, D not a multiple of 128, D % g != 0, rank < 0) */
+  ARCHEAD_E_DIMS = 2,        /* dims are invalid (V<1, D not a multiple of 128, D % g != 0, rank < 0,
+                                unknown format, a comparison head with factors) */
   ARCHEAD_E_UNSUPPORTED = 3, /* valid but not implemented (g not in {32,64,128,256}, rank not a multiple of 8,
                                 rank above 1024, a forced decode path the decode kernel does not take,
-                                section offsets past 32 bits) */
+                                section offsets past 32 bits, a comparison head where only the
+                                ARCHead format is served) */
   ARCHEAD_E_DTYPE = 4,       /* H is not bf16, or Y is neither fp32 nor bf16       */
   ARCHEAD_E_SHAPE = 5,       /* H.cols != D, Y.cols != V, Y.rows != H.rows, bad strides */
   ARCHEAD_E_ALIGN = 6,       /* buffer/workspace not 256-byte aligned, H rows not 16-byte aligned,
@@ -84,11 +90,24 @@ typedef enum {
   ARCHEAD_PATH_TILE = 2    /* LDS-tiled MFMA path (any N); needs the workspace    */
 } archead_path;
 
+/* Storage format of a packed head.  ARCHEAD_FMT_ARCHEAD is the method's own
+ * head.  The other two are the storage-matched heads the pages set beside it
+ * (results discussion of Table 7: a GPTQ-style INT4 head at 25.78% of the
+ * BF16 head; of Table 8: a row-INT8 head at about twice ARCHead's storage);
+ * they have no factors (r_c = r_r = 0). */
+typedef enum {
+  ARCHEAD_FMT_ARCHEAD = 0,    /* SC4 residual + quantised core + INT8 correction        */
+  ARCHEAD_FMT_GROUP_INT4 = 1, /* W[v,k] = q4[v,k] * s_G[v, k/g], fp16 group scales       */
+  ARCHEAD_FMT_ROW_INT8 = 2    /* W[v,k] = q8[v,k] * s[v], fp16 row scales                */
+} archead_format;
+
 /* Shape of a packed head (Algorithm 1 inputs: vocabulary V, hidden size D,
- * core rank r_c, correction rank r_r, group size g along D). */
+ * core rank r_c, correction rank r_r, group size g along D) and its storage
+ * format (archead_format; 0 when the struct is zero-initialised). */
 typedef struct {
   int64_t V, D;
   int32_t r_c, r_r, g;
+  int32_t format;
 } archead_dims;
 
 typedef struct {
@@ -114,6 +133,14 @@ typedef struct {
  *   b_scales    fp16 [r_c + r_r][D/g], group scales of B_c then B_w.
  * Dequantisation: R[v,k] = q4 * c8[v,k/g] * s_R[v];  A[v,j] = code * s_A(part)[v];
  * B[j,k] = code * s_B[j,k/g].  W_hat = R + A_c B_c + A_w B_w.
+ * The header's flags word holds the format.  The comparison heads use the
+ * same container with r_c = r_r = 0 (sections not named are empty):
+ *   ARCHEAD_FMT_GROUP_INT4: r_codes as above; r_gcodes holds fp16 group
+ *     scales [V16][D/g] (byte 2*(v*(D/g) + t)).  W_hat[v,k] = q4 * s_G[v,k/g].
+ *   ARCHEAD_FMT_ROW_INT8: r_codes holds INT8 tiles of 16 rows x 128 columns
+ *     (2048 B), tile (b, kt) at (kt*nb + b)*2048; byte 32*l + 8*s + p holds
+ *     row 16*b + l%16 at column 128*kt + 32*s + 8*(l/16) + P[p],
+ *     P = {0,1,4,5,2,3,6,7}; r_rowscale holds fp16 s[v].  W_hat[v,k] = q8 * s[v].
  * payload_bytes is the sum of numel x element size over the seven stored
  * tensors (the persistent size of Sec. 3); total_bytes adds the header and
  * alignment padding. */
@@ -142,6 +169,11 @@ typedef struct {
   const int8_t* B_w;
   const uint16_t* s_Bc;
   const uint16_t* s_Bw;
+  /* comparison heads: ARCHEAD_FMT_GROUP_INT4 reads q4 and s_G [V][D/g] fp16;
+   * ARCHEAD_FMT_ROW_INT8 reads q8 [V][D] int8 in [-127, 127] and s_R as the
+   * row scales.  Unused fields may be NULL. */
+  const uint16_t* s_G;
+  const int8_t* q8;
 } archead_host_components;
 
 /* A 2-D device tensor: element (i, j) at data + (i*row_stride + j)*elem_size. */
@@ -206,8 +238,9 @@ enum archead_kernel {
 ARCHEAD_API int archead_main_kernel(const archead_dims* d, int64_t n_tokens, int path, int* kernel);
 
 /* Serialise host components into `dst` (host memory, dst_bytes >=
- * layout.total_bytes), writing every byte of the layout including padding.
- * Host only; multithreaded.  E_NULL, E_DIMS, E_SIZE, E_VALUE. */
+ * layout.total_bytes), writing every byte of the layout including padding,
+ * in the format d->format names.  Host only; multithreaded.  E_NULL, E_DIMS,
+ * E_SIZE, E_VALUE (an INT4 code outside [-8, 7], an INT8 code of -128). */
 ARCHEAD_API int archead_pack(const archead_dims* d, const archead_host_components* src, void* dst,
                  uint64_t dst_bytes);
 
@@ -333,10 +366,12 @@ ARCHEAD_API int archead_logit_error(const archead_tensor* H, const archead_packe
  *   Y: fp32 or bf16 [N][V] device tensor, written completely (every element
  *      once); bf16 output is rounded to nearest even from the fp32 result.
  *   stream: a hipStream_t (NULL = the default stream).
- * Enqueues the decode path (up to 16 tokens whose converted H and Z fit
- * LDS: a small pre-projection kernel, then one kernel that streams the head)
- * or the tile path (pre-projection kernels, then the tile kernel) on `stream`
- * and returns without synchronising.
+ * Enqueues the decode path (up to 64 tokens: a small pre-projection kernel,
+ * then one kernel that streams the head) or the tile path (pre-projection
+ * kernels, then the tile kernel) on `stream` and returns without
+ * synchronising.  A comparison head (ARCHEAD_FMT_GROUP_INT4, _ROW_INT8) runs
+ * on the batched streaming kernel only, 32 tokens per launch (the tile path
+ * gives E_UNSUPPORTED); it needs D a multiple of 512 and D/g <= 64.
  * N = 0 is a no-op that returns ARCHEAD_OK.  Faults inside kernels surface at
  * the caller's next synchronisation with the stream. */
 ARCHEAD_API int archead_logits(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y,
@@ -354,7 +389,8 @@ ARCHEAD_API int archead_logits(const archead_tensor* H, const archead_packed_hea
  * routine; the first call on a device looks the array's address up.  Every
  * call on one GPU uses the same array and nothing in it needs to start at
  * zero: calls that overlap on one GPU (other streams, other threads) race and
- * give undefined results.  Other arguments and errors as archead_logits. */
+ * give undefined results.  ARCHead-format heads only (E_UNSUPPORTED for a
+ * comparison head).  Other arguments and errors as archead_logits. */
 #define ARCHEAD_NOALLOC_SCRATCH_BYTES (16ull << 20)
 ARCHEAD_API int archead_logits_noalloc(const archead_tensor* H, const archead_packed_head* head,
                                        archead_tensor* Y, void* stream);
