@@ -299,6 +299,9 @@ def run_alt(name, fmt, steps, warmup, archead_ms=None):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb.record(stream)  # creates the underlying hipEvents
+    ee.record(stream)
+    torch.cuda.synchronize()
     kms = []
     for i in range(steps):
         ah.archead_logits_events(H, heads[i % 2], Y, 0, eb, ee)

@@ -37,6 +37,11 @@ CASES = [
     (1000, 512, 16, 8, 64, 40, 5),
     (2048, 1024, 32, 32, 128, 300, 10),
     (530, 512, 40, 72, 256, 513, 4),
+    # many 1024-logit spans per row, so the span-maximum threshold leaves
+    # most spans out: k = 1, 5, 16, one and several chunks
+    (30000, 256, 16, 8, 64, 9, 16),
+    (30011, 512, 8, 8, 32, 70, 1),
+    (65536, 256, 16, 16, 128, 300, 5),
 ]
 
 
@@ -63,15 +68,40 @@ def test_topk_matches_oracle(V, D, r_c, r_r, g, N, k):
     assert np.abs(np.take_along_axis(Yr, idx.astype(np.int64), 1) - rv).max() <= 2 * TOL * scale
 
 
-def test_topk_ties():
-    """A zero head gives Y = 0: every row's top-k is indices 0..k-1 with value 0."""
-    V, D, N, k = 600, 256, 20, 7
+@pytest.mark.parametrize("V,k", [(600, 7), (20000, 16)])
+def test_topk_ties(V, k):
+    """A zero head gives Y = 0: every row's top-k is indices 0..k-1 with value
+    0 (with V = 20000 every span's maximum equals the threshold)."""
+    D, N = 256, 20
     inp = synth.make("tiny", seed=5, V=V, D=D, N=N, r_c=16, r_r=24, g=64)
     ah = ah_mod()
     head = ah.PackedHead.from_components(synth.zero_head(V, D, 16, 24, 64))
     vals, idx = ah.archead_logits_topk(device_H(inp.H_bits), head, k)
     torch_mod().cuda.synchronize()
     assert (idx.cpu().numpy() == np.arange(k)).all() and (vals.cpu().numpy() == 0).all()
+
+
+def test_topk_planted_in_one_span():
+    """One-hot rows pick one weight column: its largest stored value sits in
+    sixteen rows of one span, and every other span's maximum is one step
+    lower, so the threshold keeps many spans and the ties inside the best
+    span decide by index."""
+    V, D, N, k = 40000, 256, 4, 16
+    inp = synth.make("tiny", seed=9, V=V, D=D, N=1, r_c=0, r_r=0, g=64)
+    h = inp.head
+    rng = np.random.default_rng(17)
+    h.c8[:] = 1
+    h.s_R[:] = np.float16(1.0)
+    h.q4[:] = rng.integers(-8, 7, size=h.q4.shape, dtype=np.int8)   # at most 6
+    cols = np.array([0, 77, 128, 255])
+    h.q4[5000:5016, cols] = 7                                        # rows 5000..5015, span 4
+    eye = np.zeros((N, D), np.float32)
+    eye[np.arange(N), cols] = 1.0
+    ah = ah_mod()
+    head = ah.PackedHead.from_components(h)
+    vals, idx = ah.archead_logits_topk(device_H(synth.f32_to_bf16_bits(eye)), head, k)
+    torch_mod().cuda.synchronize()
+    assert (idx.cpu().numpy() == np.arange(5000, 5016)).all() and (vals.cpu().numpy() == 7).all()
 
 
 @pytest.mark.slow
