@@ -117,7 +117,7 @@ typedef struct {
 /* Where every stored tensor lives inside the one contiguous packed buffer
  * (format version 1; each section starts on a 256-byte boundary):
  *   header      64 B: u32 magic 0x48435241, u32 version, u64 V, u64 D,
- *                     u32 r_c, u32 r_r, u32 g, u32 flags (0), 24 zero bytes
+ *                      u32 r_c, u32 r_r, u32 g, u32 flags (the format), 24 zero bytes
  *   r_codes     SC4 codes in tiles of 16 rows x 128 columns (1024 B).  With
  *               V16 = V rounded up to 16 and nb = V16/16 row blocks, tile
  *               (b, kt) sits at (kt*nb + b)*1024 (k-tile major, so tiles read
