@@ -20,9 +20,9 @@
  *     HIP call; on a non-zero status nothing has been enqueued.
  *   - The caller owns all memory.  The library allocates nothing on the
  *     device and keeps no pointer after a call returns, except that
- *     archead_fit and archead_logit_error create a rocBLAS handle for the call
- *     (rocBLAS and rocSOLVER allocate their own scratch) and wait for the
- *     stream before returning.
+ *     archead_fit and archead_logit_error create rocBLAS handles for the call
+ *     (rocBLAS and rocSOLVER allocate their own scratch; archead_fit also a
+ *     second stream) and wait for the stream before returning.
  *   - Device pointers must stay valid until the stream has passed the work
  *     enqueued by the call.  Calls on different streams need different
  *     workspaces; the library holds no global state and is re-entrant.
@@ -316,28 +316,35 @@ typedef struct {
 } archead_fit_outputs;
 
 /* Device workspace archead_fit needs (two fp32 V x D arrays, four D x D, the
- * randomized SVDs' panels and the factors).  Pure host arithmetic.  E_NULL,
- * E_DIMS, E_UNSUPPORTED, E_SHAPE (a rank plus oversample above V or D). */
+ * randomized SVDs' panels, 65 chunk products of D x k, small fp64 matrices and
+ * the factors; k = max(r_c, r_r) + oversample).  Pure host arithmetic.
+ * E_NULL, E_DIMS, E_SHAPE (k above V or D), E_UNSUPPORTED (k above 128, or
+ * what archead_quantize does not take). */
 ARCHEAD_API int archead_fit_workspace_bytes(const archead_dims* d, int32_t oversample, uint64_t* bytes);
 
 /* Build a packed head from a dense one (Algorithm 1; Sec. 3 metric transform,
  * quantized-core equation and packed-variant paragraph):
  *   1. A_c B_c = rank-r_c randomized SVD of W (Y = W omega_c, power_iters
- *      rounds of QR-orthonormalised power iteration, Q = qr(Y), Q^T W = U S V^T,
- *      A_c = Q U_r S_r, B_c = V_r^T);
+ *      rounds of power iteration with an orthonormal basis between them,
+ *      Q = orth(Y), Q^T W = U S V^T, A_c = Q U_r S_r, B_c = V_r^T);
  *   2. the packing step of archead_quantize for the core: INT8 A_c, B_c, SC4 of
  *      R = W - Q(A_c) Q(B_c), and E = W - W_d;
  *   3. C_lam = H^T H / H_rows + lambda c_bar I (c_bar = mean diagonal of
  *      H^T H / H_rows), C_lam = Q Lam Q^T, T_p = Q Lam^p Q^T, T_p^{-1};
  *   4. A_w Bt = rank-r_r randomized SVD of E T_p (omega_r), B_w = Bt T_p^{-1};
  *   5. INT8 A_w (rows) and B_w (groups) into the same buffer.
- * Dense products run on rocBLAS and QR / SVD / the eigendecomposition on
- * rocSOLVER, in fp32; a rocBLAS handle is created for the call (rocBLAS may
- * allocate its own scratch).  The call waits for the stream at the end to read
- * the solvers' status: ARCHEAD_E_VALUE if one failed (or for a lambda that is
- * not positive, or a non-finite p).  packed: as for archead_quantize.
- * E_NULL, E_DIMS, E_UNSUPPORTED, E_DTYPE, E_SHAPE, E_ALIGN, E_SIZE,
- * E_WORKSPACE, E_VALUE, E_HIP. */
+ * Dense products run on rocBLAS in fp32 (E T_p is never formed: the
+ * randomized SVD applies E and T_p in turn), orthonormal bases by Cholesky QR
+ * twice with fp64 Gram matrices, the SVD of the k x D sketch from the fp64
+ * eigenpairs of its Gram matrix, the eigendecomposition of C_lam on rocSOLVER
+ * (fp32).  Step 3 runs on a second stream (default priority) created for the
+ * call, beside steps 1-2; two rocBLAS handles are created for the call
+ * (rocBLAS may allocate its own scratch).  k = max(r_c, r_r) + oversample
+ * must be at most 128.  The call waits for both streams at the end to read
+ * the solvers' status: ARCHEAD_E_VALUE if one failed or a Cholesky pivot was
+ * not finite (or for a lambda that is not positive, or a non-finite p).
+ * packed: as for archead_quantize.  E_NULL, E_DIMS, E_UNSUPPORTED, E_DTYPE,
+ * E_SHAPE, E_ALIGN, E_SIZE, E_WORKSPACE, E_VALUE, E_HIP. */
 ARCHEAD_API int archead_fit(const archead_dims* d, const archead_fit_inputs* in, void* packed,
                             uint64_t packed_bytes, void* workspace, uint64_t workspace_bytes,
                             const archead_fit_outputs* out, void* stream);

@@ -346,12 +346,19 @@ def test_fit_workspace_bytes(ah):
     up = lambda x: (x + 255) // 256 * 256
     for (V, D, r_c, r_r, g, o) in [(1000, 256, 16, 8, 64, 8), (151936, 4096, 32, 32, 128, 8), (500, 384, 0, 24, 128, 4)]:
         k = max(r_c, r_r) + o
-        parts = [V * D * 4, V * D * 4, V * k * 4, D * k * 4, k * 4, k * D * 4, k * 4, k * k * 4, k * D * 4,
-                 max(k, D) * 4, 64, D * D * 4, D * 4, D * D * 4, D * D * 4, D * D * 4,
+        # W and E in fp32; V x k, D x k and k x D panels (two, three, two); 65 chunk products of D x k;
+        # 64 fp64 Gram partials, the Gram matrix, eigenvalues and scratch; R^{-1}, U S, U S^{-1};
+        # status ints; covariance, eigenvalues, eigensolver scratch, three more D x D; the factors
+        parts = [V * D * 4, V * D * 4, V * k * 4, V * k * 4, D * k * 4, D * k * 4, D * k * 4, k * D * 4,
+                 k * D * 4, 65 * D * k * 4, 64 * k * k * 8, k * k * 8, k * 8, k * 8, k * k * 4, k * k * 4,
+                 k * k * 4, 64, D * D * 4, D * 4, D * 4, D * D * 4, D * D * 4, D * D * 4,
                  V * r_c * 4, r_c * D * 4, V * r_r * 4, r_r * D * 4, r_r * D * 4]
         assert ah.archead_fit_workspace_bytes(V, D, r_c, r_r, g, o) == sum(up(x) for x in parts)
     with pytest.raises(ah.ArcheadError):
         ah.archead_fit_workspace_bytes(20, 128, 16, 8, 64, 8)     # rank + oversample above V
+    with pytest.raises(ah.ArcheadError):
+        ah.archead_fit_workspace_bytes(4096, 1024, 128, 8, 64, 1)  # rank + oversample above 128
+    assert ah.archead_fit_workspace_bytes(4096, 1024, 120, 8, 64, 8) > 0
 
 
 def test_fit_error_paths(ah):
@@ -378,6 +385,7 @@ def test_fit_error_paths(ah):
     assert call(W_stride=D - 1) == 5 and call(H_stride=D - 2) == 5 and call(H_rows=0) == 5
     assert call(oversample=-1) == 5 and call(power_iters=17) == 5
     assert call(dims=(20, D, r_c, r_r, g)) == 5                                   # rank + oversample above V
+    assert call(dims=(V, D, r_c, 128, g)) == 3                                    # rank + oversample above 128
     assert call(lam=0.0) == 9 and call(p=float("nan")) == 9
     assert call(buf=FAKE + 128) == 6 and call(w=FAKE + 64) == 6 and call(H=FAKE + 1) == 6
     assert call(nbytes=total - 1) == 10
