@@ -1,6 +1,8 @@
-// Decode path for a few tokens (N <= 4 at D = 4096): a per-token
-// pre-projection kernel, then a streaming kernel with four small workgroups
-// per CU, each with its own copy of H and Z in LDS.
+// Decode path for a few tokens (N <= 16 at D = 4096): a per-token
+// pre-projection kernel, then a streaming kernel whose workgroups each hold a
+// copy of H and Z in LDS: four workgroups of 4 waves per CU when a copy fits
+// 48 KiB (N <= 4 at D = 4096), else one workgroup of 16 waves per CU with one
+// copy of up to 152 KiB.
 //
 // Y = H W_d^T + (H B_w^T) A_w^T (Algorithm 1, inference step) with
 // W_d = Q(A_c)Q(B_c) + SC4(R) (Sec. 3, quantized-core equation); the core is
@@ -28,6 +30,7 @@ namespace {
 
 constexpr int kSmallMaxTokens = 16;       // token rows of the per-WG arrays
 constexpr uint64_t kSmallLdsBytes = 48 * 1024;  // H and Z per workgroup: four fit a CU
+constexpr uint64_t kWideLdsBytes = 152 * 1024;  // one 16-wave workgroup per CU (160 KiB of LDS)
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -141,7 +144,8 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
 // ---------------------------------------------------------------------------
 // Streaming kernel, persistent.
 //
-// The grid holds only co-resident workgroups (at most kLdsWgPerCu per CU).
+// The grid holds only co-resident workgroups (at most kLdsWgPerCu per CU for
+// NW = 4 waves a workgroup, one for NW = 16).
 // Every wave walks a grid-strided list of 16-row blocks (b, b + W, b + 2W, ...
 // with W the number of waves), so at any moment neighbouring waves read
 // neighbouring 1 KB tiles of the same k-tile plane.  Each wave keeps a ring of
@@ -151,8 +155,6 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
 // (already scaled fp16 from the pre-projection kernel) and Z (fp32) sit in
 // LDS; LDS reads use the separate lgkm counter and never wait behind the ring.
 // MFMA rows past the tokens read a zero row of H in LDS.
-constexpr int kLdsWaves = 4;
-constexpr int kLdsThreads = 64 * kLdsWaves;
 #ifndef ARCHEAD_DECODE_WG_PER_CU
 #define ARCHEAD_DECODE_WG_PER_CU 4
 #endif
@@ -183,8 +185,10 @@ __host__ __device__ inline size_t lds_bytes(int64_t N, int64_t D, int r) {
   return lds_h_bytes(N, D) + (size_t)N * r * 4;
 }
 
-template <int P, int G>
-__global__ __launch_bounds__(kLdsThreads) void small_decode_kernel(const FwdArgs a) {
+template <int P, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void small_decode_kernel(const FwdArgs a) {
+  constexpr int kLdsWaves = NW;
+  constexpr int kLdsThreads = 64 * NW;
   static_assert(P % 4 == 0, "the ring holds whole 4-tile code chunks");
   using CV = typename CodeVec<G>::T;
   constexpr int NC = P / 4;
@@ -413,24 +417,32 @@ int device_cu_count() {
   return n;
 }
 
-template <int P, int G>
+template <int P, int G, int NW>
 hipError_t launch_lds_p(const FwdArgs& a, hipStream_t s) {
   const size_t lds = lds_bytes(a.N, a.D, a.r_c + a.r_r);
+  constexpr int kThreads = 64 * NW;
+  if (lds > 64 * 1024) {  // dynamic LDS beyond 64 KiB is opted into per kernel
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&small_decode_kernel<P, G, NW>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   // persistent grid: never more workgroups than can be resident at once
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, small_decode_kernel<P, G>, kLdsThreads, lds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, small_decode_kernel<P, G, NW>, kThreads, lds) !=
           hipSuccess || per_cu < 1)
     per_cu = 1;
-  per_cu = std::min(per_cu, kLdsWgPerCu);
-  const int64_t need = (a.nb + kLdsWaves - 1) / kLdsWaves;
+  per_cu = std::min(per_cu, NW == 4 ? kLdsWgPerCu : 1);
+  const int64_t need = (a.nb + NW - 1) / NW;
   const int64_t grid = std::min<int64_t>(need, (int64_t)device_cu_count() * per_cu);
-  hipLaunchKernelGGL((small_decode_kernel<P, G>), dim3((unsigned)grid), dim3(kLdsThreads), lds, s, a);
+  hipLaunchKernelGGL((small_decode_kernel<P, G, NW>), dim3((unsigned)grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_lds(const FwdArgs& a, hipStream_t s) {
-  return launch_lds_p<kRingDepth, G>(a, s);
+  // four workgroups of 4 waves per CU when their copies of H and Z fit, else one of 16
+  if (lds_bytes(a.N, a.D, a.r_c + a.r_r) <= kSmallLdsBytes) return launch_lds_p<kRingDepth, G, 4>(a, s);
+  return launch_lds_p<kRingDepth, G, 16>(a, s);
 }
 
 }  // namespace
@@ -438,7 +450,7 @@ hipError_t launch_lds(const FwdArgs& a, hipStream_t s) {
 bool small_decode_fits(const archead_dims* d, int64_t n_tokens) {
   if (n_tokens < 1 || n_tokens > kSmallMaxTokens || (d->D / kKTile) % 4 != 0) return false;
   if (d->g != 32 && d->g != 64 && d->g != 128 && d->g != 256) return false;
-  if (lds_bytes(n_tokens, d->D, d->r_c + d->r_r) > kSmallLdsBytes) return false;
+  if (lds_bytes(n_tokens, d->D, d->r_c + d->r_r) > kWideLdsBytes) return false;
   // 32-bit offsets into the residual tiles, the group codes and the A codes
   const uint64_t V16 = round_up((uint64_t)d->V, 16);
   return V16 * (uint64_t)d->D / 2 < (1ull << 32) && V16 * (uint64_t)(d->D / d->g) < (1ull << 32) &&

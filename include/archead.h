@@ -217,9 +217,9 @@ ARCHEAD_API int archead_workspace_bytes_path(const archead_dims* d, int64_t n_to
 /* The main kernel a successful archead_logits_path call of n_tokens rows
  * launches (after its pre-projection kernel):
  *   ARCHEAD_KERNEL_TILE           tile32_kernel, the LDS-tiled MFMA path
- *   ARCHEAD_KERNEL_DECODE_FEW     small_decode_kernel: few tokens whose bf16
- *                                 rows and Z fit in 48 KB of LDS (N <= 4 at
- *                                 D = 4096, r = 64)
+ *   ARCHEAD_KERNEL_DECODE_FEW     small_decode_kernel: up to 16 tokens whose
+ *                                 fp16 rows and Z fit in 152 KiB of LDS (N <= 16
+ *                                 at D = 4096, r <= 128; D a multiple of 512)
  *   ARCHEAD_KERNEL_DECODE_STREAM  decode_kernel: the k-tile-major streaming
  *                                 kernel for the other calls of up to 16 tokens
  *   ARCHEAD_KERNEL_DECODE_BATCH   batch_kernel: the batched streaming kernel

@@ -114,9 +114,10 @@ def _tile_workspace(V, D, r_c, r_r, g, N):
 
 
 def _few_tokens(V, D, r_c, r_r, g, N):
-    """The few-token decode kernels take the call: H (N + 1 rows of D + 8
-    halves) and Z (N r fp32) within 48 KiB of LDS, k-tiles a multiple of 4."""
-    return 1 <= N <= 16 and (D // 128) % 4 == 0 and (N + 1) * (D + 8) * 2 + N * (r_c + r_r) * 4 <= 48 * 1024
+    """The few-token decode kernel takes the call: H (N + 1 rows of D + 8
+    halves) and Z (N r fp32) within 152 KiB of LDS (four workgroups per CU up
+    to 48 KiB, else one of 16 waves), k-tiles a multiple of 4."""
+    return 1 <= N <= 16 and (D // 128) % 4 == 0 and (N + 1) * (D + 8) * 2 + N * (r_c + r_r) * 4 <= 152 * 1024
 
 
 def _batched(V, D, r_c, r_r, g, N):

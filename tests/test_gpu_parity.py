@@ -100,6 +100,56 @@ def test_many_groups_per_row_decode(shape, N):
             run(head, np.repeat(inp.H_bits[:1], n, axis=0), 0)
 
 
+# Few-token calls whose copy of H and Z needs more than 48 KiB of LDS: the
+# few-token kernel runs one workgroup of 16 waves per CU that shares one copy
+# (up to 152 KiB: 16 tokens at D = 4096, 8 at D = 8192); past that the
+# k-tile-major streaming kernel takes the call.
+WIDE = [(1000, 4096, 32, 32, 128), (700, 8192, 16, 16, 128), (900, 4096, 8, 24, 32)]
+
+
+@pytest.mark.parametrize("shape", WIDE)
+@pytest.mark.parametrize("N", [5, 8, 12, 16])
+def test_few_token_wide_workgroup(shape, N):
+    V, D, r_c, r_r, g = shape
+    lds = (N + 1) * (D + 8) * 2 + N * (r_c + r_r) * 4
+    kern = ah_mod().archead_main_kernel(V, D, r_c, r_r, g, N)
+    log(f"few-token wide V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N} lds={lds} -> {kern}")
+    assert (kern == "small_decode_kernel") == (lds <= 152 * 1024)
+    inp = synth.make("tiny", seed=V + D + N, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=8)
+    head = _head(inp)
+    Yr = oracle.logits(inp.H_bits, inp.head)
+    Yd = to_f64(run(head, inp.H_bits, 0))
+    check_parity(Yd, Yr, f"auto {kern}")
+    if kern != "tile32_kernel":
+        assert np.array_equal(to_f64(run(head, inp.H_bits, DECODE)), Yd)
+    torch = torch_mod()
+    y16 = run(head, inp.H_bits, 0, "bf16")
+    assert torch.equal(torch.from_numpy(Yd.astype(np.float32)).to(torch.bfloat16).view(torch.int16),
+                       y16.cpu().view(torch.int16))
+
+
+@pytest.mark.parametrize("g", [32, 128])
+def test_one_hot_wide_workgroup_bit_exact(g):
+    """One-hot hidden states, 16 per call at D = 4096 (the 16-wave few-token
+    workgroup): every stored weight comes back exactly."""
+    V, D = 400, 4096
+    inp = synth.make("tiny", seed=g + 1, V=V, D=D, N=1, r_c=0, r_r=0, g=g)
+    h = inp.head
+    h.q4[0, :] = -8
+    h.c8[1, :] = 255
+    h.s_R.view(np.uint16)[2] = 0x0001
+    ks = np.array(sorted(set([0, 1, 31, 32, 127, 128, 511, 512, 2047, 2048, 4095] + list(range(3, D, 97)))))
+    assert ah_mod().archead_main_kernel(V, D, 0, 0, g, 16) == "small_decode_kernel"
+    eye = np.zeros((ks.size, D), np.float32)
+    eye[np.arange(ks.size), ks] = 1.0
+    Hb = synth.f32_to_bf16_bits(eye)
+    head = _head(inp)
+    Y = np.concatenate([run(head, Hb[i:i + 16], DECODE).cpu().numpy() for i in range(0, ks.size, 16)])
+    want = oracle.dequant_R(h.q4, h.c8, h.s_R, g)[:, ks].T.astype(np.float32)
+    assert not np.isnan(Y).any()
+    assert np.array_equal(Y, want)
+
+
 # 64 groups per row (D/g = 64) and D = 8192 on the batched kernel
 @pytest.mark.parametrize("N", [17, 40, 64])
 def test_batched_deep_rows(N):
