@@ -1,7 +1,7 @@
 // Decode path for a few tokens (N <= 16 at D = 4096): a per-token
 // pre-projection kernel, then a streaming kernel whose workgroups each hold a
-// copy of H and Z in LDS: four workgroups of 4 waves per CU when a copy fits
-// 48 KiB (N <= 4 at D = 4096), else one workgroup of 16 waves per CU with one
+// copy of H and Z in LDS: two workgroups of 8 waves per CU when a copy fits
+// 76 KiB (N <= 8 at D = 4096), else one workgroup of 16 waves per CU with one
 // copy of up to 152 KiB.
 //
 // Y = H W_d^T + (H B_w^T) A_w^T (Algorithm 1, inference step) with
@@ -29,7 +29,7 @@ namespace archead {
 namespace {
 
 constexpr int kSmallMaxTokens = 16;       // token rows of the per-WG arrays
-constexpr uint64_t kSmallLdsBytes = 48 * 1024;  // H and Z per workgroup: four fit a CU
+constexpr uint64_t kSmallLdsBytes = 76 * 1024;  // H and Z per workgroup: two fit a CU
 constexpr uint64_t kWideLdsBytes = 152 * 1024;  // one 16-wave workgroup per CU (160 KiB of LDS)
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -144,8 +144,11 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
 // ---------------------------------------------------------------------------
 // Streaming kernel, persistent.
 //
-// The grid holds only co-resident workgroups (at most kLdsWgPerCu per CU for
-// NW = 4 waves a workgroup, one for NW = 16).
+// The grid holds only co-resident workgroups: 16 waves per CU, two workgroups
+// of NW = 8 waves or one of NW = 16 (at most 128 VGPRs a wave).  Measured on
+// the decode workload, two 8-wave workgroups per CU are as fast as four of 4
+// waves for one token and faster for 4 to 8; one of 16 is slower (about 15%
+// at one token) and serves only the copies of H that two would not fit.
 // Every wave walks a grid-strided list of 16-row blocks (b, b + W, b + 2W, ...
 // with W the number of waves), so at any moment neighbouring waves read
 // neighbouring 1 KB tiles of the same k-tile plane.  Each wave keeps a ring of
@@ -155,10 +158,6 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
 // (already scaled fp16 from the pre-projection kernel) and Z (fp32) sit in
 // LDS; LDS reads use the separate lgkm counter and never wait behind the ring.
 // MFMA rows past the tokens read a zero row of H in LDS.
-#ifndef ARCHEAD_DECODE_WG_PER_CU
-#define ARCHEAD_DECODE_WG_PER_CU 4
-#endif
-constexpr int kLdsWgPerCu = ARCHEAD_DECODE_WG_PER_CU;
 constexpr int kEpiSteps = 2;  // low-rank 32-column steps whose A codes are prefetched
 
 // The lane's group codes for one chunk of 4 tiles (512 columns): 512/g bytes.
@@ -186,7 +185,7 @@ __host__ __device__ inline size_t lds_bytes(int64_t N, int64_t D, int r) {
 }
 
 template <int P, int G, int NW>
-__global__ __launch_bounds__(64 * NW) void small_decode_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(64 * NW, 16 / NW) void small_decode_kernel(const FwdArgs a) {
   constexpr int kLdsWaves = NW;
   constexpr int kLdsThreads = 64 * NW;
   static_assert(P % 4 == 0, "the ring holds whole 4-tile code chunks");
@@ -431,7 +430,7 @@ hipError_t launch_lds_p(const FwdArgs& a, hipStream_t s) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, small_decode_kernel<P, G, NW>, kThreads, lds) !=
           hipSuccess || per_cu < 1)
     per_cu = 1;
-  per_cu = std::min(per_cu, NW == 4 ? kLdsWgPerCu : 1);
+  per_cu = std::min(per_cu, 16 / NW);
   const int64_t need = (a.nb + NW - 1) / NW;
   const int64_t grid = std::min<int64_t>(need, (int64_t)device_cu_count() * per_cu);
   hipLaunchKernelGGL((small_decode_kernel<P, G, NW>), dim3((unsigned)grid), dim3(kThreads), lds, s, a);
@@ -440,8 +439,8 @@ hipError_t launch_lds_p(const FwdArgs& a, hipStream_t s) {
 
 template <int G>
 hipError_t launch_lds(const FwdArgs& a, hipStream_t s) {
-  // four workgroups of 4 waves per CU when their copies of H and Z fit, else one of 16
-  if (lds_bytes(a.N, a.D, a.r_c + a.r_r) <= kSmallLdsBytes) return launch_lds_p<kRingDepth, G, 4>(a, s);
+  // two workgroups of 8 waves per CU when their copies of H and Z fit, else one of 16
+  if (lds_bytes(a.N, a.D, a.r_c + a.r_r) <= kSmallLdsBytes) return launch_lds_p<kRingDepth, G, 8>(a, s);
   return launch_lds_p<kRingDepth, G, 16>(a, s);
 }
 

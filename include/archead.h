@@ -75,9 +75,9 @@ typedef enum {
   ARCHEAD_PATH_AUTO = 0,   /* the decode path when it takes the call, else the tile path */
   ARCHEAD_PATH_DECODE = 1, /* one kernel that streams the head once for up to 64 tokens.
                               Up to 16 tokens: the few-token kernel when H (N + 1 rows of D + 8
-                              halves) and Z (N (r_c + r_r) fp32) fit 48 KiB of
-                              LDS and D/128 is a multiple of 4 (N <= 4 at
-                              D = 4096, r = 64), else the k-tile-major kernel
+                              halves) and Z (N (r_c + r_r) fp32) fit 152 KiB of
+                              LDS and D/128 is a multiple of 4 (N <= 16 at
+                              D = 4096, r <= 128; N <= 8 at D = 8192), else the k-tile-major kernel
                               when the converted H fits the 160 KiB of LDS of a
                               workgroup (N <= 16 at D = 4096, N <= 8 at D = 8192),
                               with N (r_c + r_r) <= 2048, round_up(r_c, 32) +

@@ -115,8 +115,8 @@ def _tile_workspace(V, D, r_c, r_r, g, N):
 
 def _few_tokens(V, D, r_c, r_r, g, N):
     """The few-token decode kernel takes the call: H (N + 1 rows of D + 8
-    halves) and Z (N r fp32) within 152 KiB of LDS (four workgroups per CU up
-    to 48 KiB, else one of 16 waves), k-tiles a multiple of 4."""
+    halves) and Z (N r fp32) within 152 KiB of LDS (two workgroups of 8 waves
+    per CU up to 76 KiB, else one of 16 waves), k-tiles a multiple of 4."""
     return 1 <= N <= 16 and (D // 128) % 4 == 0 and (N + 1) * (D + 8) * 2 + N * (r_c + r_r) * 4 <= 152 * 1024
 
 

@@ -100,15 +100,15 @@ def test_many_groups_per_row_decode(shape, N):
             run(head, np.repeat(inp.H_bits[:1], n, axis=0), 0)
 
 
-# Few-token calls whose copy of H and Z needs more than 48 KiB of LDS: the
+# Few-token calls whose copy of H and Z needs more than 76 KiB of LDS: the
 # few-token kernel runs one workgroup of 16 waves per CU that shares one copy
-# (up to 152 KiB: 16 tokens at D = 4096, 8 at D = 8192); past that the
-# k-tile-major streaming kernel takes the call.
-WIDE = [(1000, 4096, 32, 32, 128), (700, 8192, 16, 16, 128), (900, 4096, 8, 24, 32)]
+# (up to 152 KiB: 16 tokens at D = 4096, 8 at D = 8192) instead of two of 8
+# waves; past that another kernel takes the call.
+WIDE = [(1000, 4096, 32, 32, 128), (700, 8192, 16, 16, 128), (900, 4096, 8, 24, 32), (800, 2048, 16, 16, 64)]
 
 
 @pytest.mark.parametrize("shape", WIDE)
-@pytest.mark.parametrize("N", [5, 8, 12, 16])
+@pytest.mark.parametrize("N", [3, 5, 8, 9, 12, 16])
 def test_few_token_wide_workgroup(shape, N):
     V, D, r_c, r_r, g = shape
     lds = (N + 1) * (D + 8) * 2 + N * (r_c + r_r) * 4
