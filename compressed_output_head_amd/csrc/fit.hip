@@ -48,7 +48,7 @@ using archead::QuantArgs;
 constexpr int kFThreads = 256;
 constexpr int kFitMaxK = 128;      // rank + oversample of either randomized SVD
 constexpr int kSplit = 64;         // row chunks of a reduction over V rows
-constexpr int kGramChunks = 64;    // row chunks of a Gram matrix
+constexpr int kGramChunks = 256;   // row chunks of a Gram matrix
 constexpr int kGramRows = 32;      // rows per LDS tile of the Gram kernel
 constexpr int kTri = kFitMaxK * (kFitMaxK + 1) / 2;
 constexpr uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
@@ -79,13 +79,13 @@ __global__ __launch_bounds__(kFThreads) void damp_kernel(float* C, int n, float 
   for (int i = threadIdx.x; i < n; i += kFThreads) C[(int64_t)i * n + i] += add;
 }
 
-// dst[:, j] = src[:, j] * max(s[j], tiny)^p for column-major n_rows x n_cols (ld = n_rows)
+// dst[:, j] = src[:, j] * max(s[j], tiny)^p for column-major n_rows x n_cols
+// (ld = n_rows); one workgroup per column at a time, the power once per thread
 __global__ __launch_bounds__(kFThreads) void scale_cols_kernel(const float* src, float* dst, int64_t n_rows,
                                                                int64_t n_cols, int64_t ld, const float* s, float p) {
-  const int64_t n = n_rows * n_cols, stride = (int64_t)gridDim.x * kFThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kFThreads + threadIdx.x; i < n; i += stride) {
-    const int64_t j = i / n_rows, r = i - j * n_rows;
-    dst[j * ld + r] = src[j * ld + r] * powf(fmaxf(s[j], 1e-30f), p);
+  for (int64_t j = blockIdx.x; j < n_cols; j += gridDim.x) {
+    const float f = powf(fmaxf(s[j], 1e-30f), p);
+    for (int64_t r = threadIdx.x; r < n_rows; r += kFThreads) dst[j * ld + r] = src[j * ld + r] * f;
   }
 }
 
@@ -525,7 +525,7 @@ int archead_fit(const archead_dims* d, const archead_fit_inputs* in, void* packe
         const float pw[2] = {in->p, -in->p};
         const uint64_t dst[2] = {FL.Tp, FL.Ti};
         for (int t = 0; t < 2 && !st.rc; ++t) {
-          hipLaunchKernelGGL(scale_cols_kernel, dim3(grid_for((int64_t)D * D)), dim3(kFThreads), 0, s2, F(FL.C),
+          hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)(D < 8192 ? D : 8192)), dim3(kFThreads), 0, s2, F(FL.C),
                              F(FL.M1), (int64_t)D, (int64_t)D, (int64_t)D, F(FL.Lam), pw[t]);
           if (!st.ok(hipGetLastError())) break;
           st.ok(rocblas_sgemm(h2, rocblas_operation_none, rocblas_operation_transpose, D, D, D, &kOne, F(FL.M1), D,

@@ -348,10 +348,10 @@ def test_fit_workspace_bytes(ah):
     for (V, D, r_c, r_r, g, o) in [(1000, 256, 16, 8, 64, 8), (151936, 4096, 32, 32, 128, 8), (500, 384, 0, 24, 128, 4)]:
         k = max(r_c, r_r) + o
         # W and E in fp32; V x k, D x k and k x D panels (two, three, two); 65 chunk products of D x k;
-        # 64 fp64 Gram partials, the Gram matrix, eigenvalues and scratch; R^{-1}, U S, U S^{-1};
+        # 256 fp64 Gram partials, the Gram matrix, eigenvalues and scratch; R^{-1}, U S, U S^{-1};
         # status ints; covariance, eigenvalues, eigensolver scratch, three more D x D; the factors
         parts = [V * D * 4, V * D * 4, V * k * 4, V * k * 4, D * k * 4, D * k * 4, D * k * 4, k * D * 4,
-                 k * D * 4, 65 * D * k * 4, 64 * k * k * 8, k * k * 8, k * 8, k * 8, k * k * 4, k * k * 4,
+                 k * D * 4, 65 * D * k * 4, 256 * k * k * 8, k * k * 8, k * 8, k * 8, k * k * 4, k * k * 4,
                  k * k * 4, 64, D * D * 4, D * 4, D * 4, D * D * 4, D * D * 4, D * D * 4,
                  V * r_c * 4, r_c * D * 4, V * r_r * 4, r_r * D * 4, r_r * D * 4]
         assert ah.archead_fit_workspace_bytes(V, D, r_c, r_r, g, o) == sum(up(x) for x in parts)
