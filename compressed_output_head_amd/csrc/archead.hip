@@ -101,9 +101,10 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
     w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
   } else if (w.small || w.batch) {  // few-token and batched decode kernels: converted H, its scales, Z
     const uint64_t nc = (uint64_t)std::max<int64_t>(chunk, 0);  // rows converted per launch
+    w.zsl = w.small ? small_z_slices(d->D, n_tokens) : 1;       // Z as partial sums over slices of D
     w.hc = take(nc * D * 2);
     w.hscale = take(nc * 4);
-    w.z32 = take(nc * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
+    w.z32 = take((uint64_t)w.zsl * nc * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
   } else {  // the decode path: partial sums of Z
     w.z32 = take(decode_workspace_bytes(d, n_tokens));
   }
@@ -392,6 +393,7 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
   a.rc32 = W.rc32;
   a.rr32 = W.rr32;
   a.zsteps = W.zsteps;
+  a.zsl = W.zsl > 0 ? W.zsl : 1;
   a.nA = (d->r_c > 0) + (d->r_r > 0);
   a.fmt = d->format;
   a.H = static_cast<const uint16_t*>(H->data);

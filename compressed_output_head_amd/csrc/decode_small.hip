@@ -8,8 +8,10 @@
 // W_d = Q(A_c)Q(B_c) + SC4(R) (Sec. 3, quantized-core equation); the core is
 // evaluated through the same association, (H B_c^T) A_c^T.
 //
-// Pre-projection, grid (N, ceil(r/4) + 1): z32[n][j] = sum_k H[n,k] B_hat[j,k]
-// in fp32, one wave per (token, rank), and for each token hscale[n] = 2^-S_n
+// Pre-projection, grid (N, S ceil(r/4) + 1): z32[s][n][j] = sum over the
+// columns k of slice s of H[n,k] B_hat[j,k] in fp32, one wave per (slice,
+// token, rank) (S = 1 for the batched kernel; the few-token kernel adds the S
+// slices in order), and for each token hscale[n] = 2^-S_n
 // and hc[n][:] = fp16(H[n,:] 2^S_n) in kernel k-order, S_n putting the row
 // maximum in [2^14, 2^15) (exact for every bf16 value within 2^31 of it).
 //
@@ -41,10 +43,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Small-N pre-projection, grid (N, ceil(r/4) + 1):
-//   blockIdx.y < ceil(r/4): z32[n][j] = sum_k H[n,k] B_hat[j,k] in fp32, one
-//     wave per (token, j); every lane issues all its loads before the arithmetic.
-//   blockIdx.y == ceil(r/4): hscale[n] = 2^-S_n and hc[n][:] = fp16(H[n,:] 2^S_n)
+// Small-N pre-projection, grid (N, S ceil(r/4) + 1) with S = a.zsl slices of D:
+//   blockIdx.y < S ceil(r/4): z32[s][n][j] = sum over slice s of H[n,k] B_hat[j,k]
+//     in fp32, one wave per (slice, token, j); every lane issues all its loads
+//     before the arithmetic.
+//   blockIdx.y == S ceil(r/4): hscale[n] = 2^-S_n and hc[n][:] = fp16(H[n,:] 2^S_n)
 //     in kernel k-order (S_n as in prep_kernel).
 constexpr int kSmallPrepThreads = 256;
 constexpr int kSmallPrepChunks = 16;  // D <= 64*8*16 = 8192 columns per lane loop
@@ -56,7 +59,8 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
   const int nJ = (r + 3) / 4;
   const uint16_t* hrow = a.H + n * a.H_stride;
   const int nchunk = (int)(a.D / 8);
-  if ((int)blockIdx.y == nJ) {
+  const int nsl = a.zsl;
+  if ((int)blockIdx.y == nJ * nsl) {
     // the row's first kSmallPrepKeep * 256 chunks stay in registers between the
     // maximum and the conversion (one read of H for D <= 8192)
     constexpr int kSmallPrepKeep = 4;
@@ -103,19 +107,22 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
     });
     return;
   }
-  const int j = blockIdx.y * (kSmallPrepThreads / 64) + wave;
+  const int sl = (int)blockIdx.y / nJ;
+  const int j = ((int)blockIdx.y - sl * nJ) * (kSmallPrepThreads / 64) + wave;
   if (j >= r) return;
   const int8_t* brow = a.b_codes + (int64_t)j * a.D;
   const uint16_t* srow = a.b_scales + (int64_t)j * a.ng;
+  // this wave's 8-column chunks: [c_lo, c_hi) of the row
+  const int c_lo = (int)((int64_t)sl * nchunk / nsl), c_hi = (int)((int64_t)(sl + 1) * nchunk / nsl);
   float acc = 0.0f;
-  for (int c0 = 0; c0 < nchunk; c0 += 64 * kSmallPrepChunks) {
+  for (int c0 = c_lo; c0 < c_hi; c0 += 64 * kSmallPrepChunks) {
     u4 hr[kSmallPrepChunks];
     u2 br[kSmallPrepChunks];
     uint16_t sr[kSmallPrepChunks];
 #pragma unroll
     for (int u = 0; u < kSmallPrepChunks; ++u) {
       const int c = c0 + lane + 64 * u;
-      if (c < nchunk) {
+      if (c < c_hi) {
         hr[u] = *reinterpret_cast<const u4*>(hrow + 8 * (int64_t)c);
         br[u] = *reinterpret_cast<const u2*>(brow + 8 * (int64_t)c);
         sr[u] = srow[(8 * c) / a.g];
@@ -124,7 +131,7 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
 #pragma unroll
     for (int u = 0; u < kSmallPrepChunks; ++u) {
       const int c = c0 + lane + 64 * u;
-      if (c < nchunk) {
+      if (c < c_hi) {
         float part = 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
     }
   }
   acc = wave_sum(acc);
-  if (lane == 0) a.z32[n * r + j] = acc;
+  if (lane == 0) a.z32[((int64_t)sl * a.N + n) * r + j] = acc;
 }
 
 
@@ -243,7 +250,14 @@ __global__ __launch_bounds__(64 * NW, 16 / NW) void small_decode_kernel(const Fw
     hpre[i] = c < N * per_row ? *reinterpret_cast<const u4*>(a.hc + (int64_t)(c / per_row) * D + 8 * (c % per_row))
                               : u4{0u, 0u, 0u, 0u};
   }
-  const float zpre = tid < N * r ? a.z32[tid] : 0.0f;
+  // Z = the sum of its slices' partial sums, added in slice order
+  const int zs = a.zsl;
+  auto zsum = [&](int c) {
+    float z = 0.0f;
+    for (int sl = 0; sl < zs; ++sl) z += a.z32[(int64_t)sl * N * r + c];
+    return z;
+  };
+  const float zpre = tid < N * r ? zsum(tid) : 0.0f;
   const float hspre = tid < N ? a.hscale[tid] : 0.0f;
   u4 wr[P];
   CV cv[NC];
@@ -265,7 +279,7 @@ __global__ __launch_bounds__(64 * NW, 16 / NW) void small_decode_kernel(const Fw
     *reinterpret_cast<u4*>(sH + n * ldh + 8 * k8) =
         *reinterpret_cast<const u4*>(a.hc + (int64_t)n * D + 8 * k8);
   }
-  for (int c = tid + kLdsThreads; c < N * r; c += kLdsThreads) sZ[c] = a.z32[c];
+  for (int c = tid + kLdsThreads; c < N * r; c += kLdsThreads) sZ[c] = zsum(c);
   __syncthreads();
   if (b >= nb) return;
 
@@ -466,9 +480,18 @@ hipError_t launch_small_decode(const FwdArgs& a, hipStream_t s) {
 }
 
 
+// One to four 8-column chunks of a row per lane of a Z wave (more tokens,
+// fewer slices: the few-token kernel reads S N r partial sums per workgroup).
+int small_z_slices(int64_t D, int64_t n_tokens) {
+  const int64_t cpl = n_tokens <= 2 ? 1 : n_tokens <= 8 ? 2 : 4;
+  const int64_t sl = D / (512 * cpl);
+  return sl < 1 ? 1 : (int)sl;
+}
+
 hipError_t launch_small_prep(const FwdArgs& a, hipStream_t s) {
   const int r = a.r_c + a.r_r;
-  hipLaunchKernelGGL(small_prep_kernel, dim3((unsigned)a.N, (unsigned)((r + 3) / 4 + 1)), dim3(kSmallPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(small_prep_kernel, dim3((unsigned)a.N, (unsigned)(a.zsl * ((r + 3) / 4) + 1)),
+                     dim3(kSmallPrepThreads), 0, s, a);
   return hipGetLastError();
 }
 

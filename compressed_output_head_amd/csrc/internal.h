@@ -51,6 +51,7 @@ struct WorkspaceLayout {
   int64_t n32;          // tokens rounded up to 32 (rows of every per-token workspace section)
   int rc32, rr32;       // ranks rounded up to 32
   int zsteps;           // (rc32 + rr32) / 32
+  int zsl;              // few-token kernel: slices of D in the partial sums of Z (else 1)
   uint64_t hf, hscale, zf, zscale, z32, hc, split, split_bytes;
   uint64_t st_part, st_y;  // row statistics only: pieces [N][st_nparts], Y [N][V] fp32 (decode kernel)
   int64_t st_nparts;
@@ -67,6 +68,7 @@ struct FwdArgs {
   int64_t V, D, N, n32, nb;        // nb = V16/16 row blocks
   int r_c, r_r, g, ng, nkt, nks, rc32, rr32, zsteps, nA;
   int fmt;                         // archead_format of the packed head
+  int zsl;                         // few-token path: slices of D whose partial sums of Z the prep writes (else 1)
   // input / output
   const uint16_t* H;          // bf16 [N][H_stride]
   int64_t H_stride;
@@ -104,6 +106,8 @@ hipError_t launch_tile(const FwdArgs& a, hipStream_t s);
 // decode path: the partial sums of Z into the workspace, then the streaming kernel
 hipError_t launch_decode_prep(const FwdArgs& a, hipStream_t s);
 hipError_t launch_small_prep(const FwdArgs& a, hipStream_t s);
+// slices of D over which the few-token pre-projection splits each element of Z
+int small_z_slices(int64_t D, int64_t n_tokens);
 hipError_t launch_small_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_batch(const FwdArgs& a, hipStream_t s);

@@ -149,8 +149,12 @@ def test_workspace_bytes(ah):
         if not decode:
             want = _tile_workspace(V, D, r_c, r_r, g, N)
         elif _few_tokens(V, D, r_c, r_r, g, N) or _batched(V, D, r_c, r_r, g, N):
-            # converted H [N][D] fp16, its scales, Z [N][r] fp32
-            want = up(N * D * 2) + up(N * 4) + up(N * (r_c + r_r) * 4)
+            # converted H [N][D] fp16, its scales, Z [S][N][r] fp32: partial sums over S
+            # slices of D for the few-token kernel (one to four 8-column chunks per
+            # lane as N grows), S = 1 for the batched kernel
+            cpl = 1 if N <= 2 else 2 if N <= 8 else 4
+            S = max(1, D // (512 * cpl)) if _few_tokens(V, D, r_c, r_r, g, N) else 1
+            want = up(N * D * 2) + up(N * 4) + up(S * N * (r_c + r_r) * 4)
         else:  # Z partial sums per element: slices of 8 k-tiles, padded to 4
             zst = (-(-(D // 128) // 8) + 3) // 4 * 4
             want = up(N * (r_c + r_r) * zst * 4)
