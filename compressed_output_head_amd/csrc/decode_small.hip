@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
 // waves for one token and faster for 4 to 8; one of 16 is slower (about 15%
 // at one token) and serves only the copies of H that two would not fit.
 // Every wave walks a grid-strided list of 16-row blocks (b, b + W, b + 2W, ...
-// with W the number of waves), so at any moment neighbouring waves read
-// neighbouring 1 KB tiles of the same k-tile plane.  Each wave keeps a ring of
+// with W the number of waves), so at any moment the waves read neighbouring
+// 1 KB tiles of the same k-tile plane.  Each wave keeps a ring of
 // P packed tiles in flight in registers, plus one vector of group codes per
 // chunk of 4 tiles (the lane's row codes for 512 columns, one small load).  The
 // ring runs across block boundaries, so a wave never drains its pipeline.  H
@@ -236,7 +236,11 @@ __global__ __launch_bounds__(64 * NW, 16 / NW) void small_decode_kernel(const Fw
   const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(a.a_scales, 2u * v16 * (uint32_t)a.nA);
   const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a.a_codes, v16 * (uint32_t)r);
 
-  int64_t b = (int64_t)blockIdx.x * kLdsWaves + wave;
+  // first block of this wave: the 16-wave workgroup spreads its waves a grid
+  // apart (measured about 10% faster than 16 neighbouring blocks per CU for
+  // 9 to 16 tokens); the 8-wave workgroups keep neighbouring blocks (the
+  // spread measured no faster there)
+  int64_t b = NW == 16 ? (int64_t)blockIdx.x + (int64_t)gridDim.x * wave : (int64_t)blockIdx.x * kLdsWaves + wave;
   const int64_t b0 = b < nb ? b : nb - 1;  // waves without work load a valid block, store nothing
   const int per_row = D / 8;
 
