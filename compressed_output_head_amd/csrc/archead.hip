@@ -98,7 +98,9 @@ WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool s
     w.hscale = take(n32 * 4);
     w.zf = take(n32 * (uint64_t)w.zsteps * 2 * 32 * 2);
     w.zscale = take(n32 * 4);
-    w.z32 = take(n32 * ((uint64_t)d->r_c + (uint64_t)d->r_r) * 4);
+    const int r = d->r_c + d->r_r;
+    const uint64_t zp = r > 0 ? (uint64_t)zmm_parts((int64_t)n32, r, d->D, d->g) : 1;
+    w.z32 = take(zp * n32 * (uint64_t)r * 4);  // parts of the k range, added by zsplit_kernel
   } else if (w.small || w.batch) {  // few-token and batched decode kernels: converted H, its scales, Z
     const uint64_t nc = (uint64_t)std::max<int64_t>(chunk, 0);  // rows converted per launch
     w.zsl = w.small ? small_z_slices(d->D, n_tokens) : 1;       // Z as partial sums over slices of D

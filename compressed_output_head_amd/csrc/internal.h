@@ -101,6 +101,8 @@ struct FwdArgs {
 
 // tile path: H and Z into the workspace, then the tile kernel
 hipError_t launch_prep(const FwdArgs& a, hipStream_t s);
+// parts of the hidden dimension in the tile path's fp32 Z ([parts][n32][r])
+int zmm_parts(int64_t n32, int r, int64_t D, int g);
 bool tile32_eligible(const FwdArgs& a);
 hipError_t launch_tile(const FwdArgs& a, hipStream_t s);
 // decode path: the partial sums of Z into the workspace, then the streaming kernel

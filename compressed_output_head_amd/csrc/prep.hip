@@ -18,6 +18,8 @@
 // H; zmm_kernel forms Z on the 32 x 32 x 16 MFMA from that fp16 H and the
 // exact INT8 B codes (so B is read once per 32-token tile, not once per
 // token); zsplit_kernel picks F_n and writes the hi/lo fragments.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -106,17 +108,19 @@ __device__ __forceinline__ h8 unpack_i8x8_h(uint32_t lo, uint32_t hi) {
   return unpack_i8x8(__builtin_amdgcn_perm(hi, lo, 0x05040100u), __builtin_amdgcn_perm(hi, lo, 0x07060302u));
 }
 
-// Z on the MFMA, grid (n32/32 token tiles, ceil(r/32) rank blocks), 16
-// waves: wave w takes slice w of the k range (whole groups) for the
-// workgroup's 32 tokens and 32 ranks.  MFMA A operand = hf fragments
-// (tokens), B operand = the exact INT8 codes of the same 16 columns (ranks);
-// each group of g columns is accumulated on its own and added times its fp16
-// scale.  The slices are summed through LDS and z32[n][j] = hscale[n] * sum
-// is written.
+// Z on the MFMA, grid (n32/32 token tiles, ceil(r/32) rank blocks, S parts of
+// the k range), 16 waves: wave w takes slice w of its part's k range (whole
+// groups) for the workgroup's 32 tokens and 32 ranks.  MFMA A operand = hf
+// fragments (tokens), B operand = the exact INT8 codes of the same 16 columns
+// (ranks); each group of g columns is accumulated on its own and added times
+// its fp16 scale.  The slices are summed through LDS and
+// z32[part][n][j] = hscale[n] * sum is written; zsplit_kernel adds the parts
+// in order (S > 1 only when the token and rank tiles alone would leave most
+// CUs idle).
 // GC: group size 0 -> g >= 128, 1 -> 64, 2 -> 32 (steps of a k-tile per group).
 constexpr int kZmmWaves = 16;
 template <int GC>
-__global__ __launch_bounds__(64 * kZmmWaves) void zmm_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(64 * kZmmWaves) void zmm_kernel(const FwdArgs a, int parts) {
   __shared__ float red[kZmmWaves][32][33];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -129,7 +133,8 @@ __global__ __launch_bounds__(64 * kZmmWaves) void zmm_kernel(const FwdArgs a) {
   const h8* hf = reinterpret_cast<const h8*>(a.hf) + tile * a.nkt * 8 * 64 + lane;
   const int kpu = a.g > kKTile ? a.g / kKTile : 1;  // k-tiles per unit (a unit holds whole groups)
   const int units = (int)(a.nkt / kpu);
-  const int u0 = wave * units / kZmmWaves, u1 = (wave + 1) * units / kZmmWaves;
+  const int p0 = (int)blockIdx.z * units / parts, pn = ((int)blockIdx.z + 1) * units / parts - p0;
+  const int u0 = p0 + wave * pn / kZmmWaves, u1 = p0 + (wave + 1) * pn / kZmmWaves;
   const int half = lane >> 5;
   f16x tot = {}, part = {};
   for (int kt = u0 * kpu; kt < u1 * kpu; ++kt) {
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(64 * kZmmWaves) void zmm_kernel(const FwdArgs a) {
 #pragma unroll
     for (int w = 0; w < kZmmWaves; ++w) z += red[w][tok][jr];
     const int64_t n = 32 * tile + tok;
-    if (jj < r) a.z32[n * r + jj] = z * a.hscale[n];
+    if (jj < r) a.z32[((int64_t)blockIdx.z * a.n32 + n) * r + jj] = z * a.hscale[n];
   }
 }
 
@@ -189,16 +194,21 @@ __global__ __launch_bounds__(64 * kZmmWaves) void zmm_kernel(const FwdArgs a) {
 // half q holds ranks 32 i + 16 q + 8 (s & 1) .. (one 16-byte load of A codes
 // feeds both steps of a pair), slot order k_order_z.
 constexpr int kZsplitThreads = 256;
-__global__ __launch_bounds__(kZsplitThreads) void zsplit_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(kZsplitThreads) void zsplit_kernel(const FwdArgs a, int parts) {
   const int lane = threadIdx.x & 63;
   const int64_t n = 4 * (int64_t)blockIdx.x + (threadIdx.x >> 6);
   if (n >= a.n32) return;
   const bool real = n < a.N;
   const int r = a.r_c + a.r_r;
-  const float* zrow = a.z32 + n * r;
+  // z[j]: the parts of the k range added in order
+  auto zrow = [&](int j) {
+    float z = 0.0f;
+    for (int p = 0; p < parts; ++p) z += a.z32[((int64_t)p * a.n32 + n) * r + j];
+    return z;
+  };
   float m = 0.0f;
   if (real)
-    for (int j = lane; j < r; j += 64) m = fmaxf(m, fabsf(zrow[j]));
+    for (int j = lane; j < r; j += 64) m = fmaxf(m, fabsf(zrow(j)));
   m = wave_max(m);
   const int F = row_exponent(m);
   if (lane == 0) a.zscale[n] = real ? ldexpf(1.0f, -F) : 0.0f;
@@ -216,7 +226,7 @@ __global__ __launch_bounds__(kZsplitThreads) void zsplit_kernel(const FwdArgs a)
     for (int jj = 0; jj < 8; ++jj) {
       const int col = 32 * (sl >> 1) + 16 * q + 8 * (sl & 1) + k_order_z(jj);
       float z = 0.0f;
-      if (real && col < rank) z = ldexpf(zrow[base + col], F);
+      if (real && col < rank) z = ldexpf(zrow(base + col), F);
       const _Float16 zh = (_Float16)z;
       hi[jj] = zh;
       lo[jj] = (_Float16)(z - (float)zh);
@@ -229,19 +239,32 @@ __global__ __launch_bounds__(kZsplitThreads) void zsplit_kernel(const FwdArgs a)
 
 }  // namespace
 
+// Parts of the k range zmm_kernel splits Z into: at least about 128
+// workgroups (half the CUs), at least one unit of whole groups per wave of a
+// part; one part once the token and rank tiles alone reach that.
+int zmm_parts(int64_t n32, int r, int64_t D, int g) {
+  const int64_t base = (n32 / 32) * ((r + 31) / 32);
+  const int64_t kpu = g > kKTile ? g / kKTile : 1;
+  const int64_t units = D / kKTile / kpu;
+  int64_t p = base > 0 ? (128 + base - 1) / base : 1;
+  p = std::min<int64_t>(p, units / kZmmWaves);
+  return p < 1 ? 1 : (int)p;
+}
+
 hipError_t launch_prep(const FwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prep_h32_kernel, dim3((unsigned)((a.n32 + 3) / 4)), dim3(kPrepHThreads), 0, s, a);
   const int r = a.r_c + a.r_r;
+  const int parts = r > 0 ? zmm_parts(a.n32, r, a.D, a.g) : 1;
   if (r > 0) {
-    const dim3 grid((unsigned)(a.n32 / 32), (unsigned)((r + 31) / 32));
+    const dim3 grid((unsigned)(a.n32 / 32), (unsigned)((r + 31) / 32), (unsigned)parts);
     if (a.g == 32)
-      hipLaunchKernelGGL(zmm_kernel<2>, grid, dim3(64 * kZmmWaves), 0, s, a);
+      hipLaunchKernelGGL(zmm_kernel<2>, grid, dim3(64 * kZmmWaves), 0, s, a, parts);
     else if (a.g == 64)
-      hipLaunchKernelGGL(zmm_kernel<1>, grid, dim3(64 * kZmmWaves), 0, s, a);
+      hipLaunchKernelGGL(zmm_kernel<1>, grid, dim3(64 * kZmmWaves), 0, s, a, parts);
     else
-      hipLaunchKernelGGL(zmm_kernel<0>, grid, dim3(64 * kZmmWaves), 0, s, a);
+      hipLaunchKernelGGL(zmm_kernel<0>, grid, dim3(64 * kZmmWaves), 0, s, a, parts);
   }
-  hipLaunchKernelGGL(zsplit_kernel, dim3((unsigned)((a.n32 + 3) / 4)), dim3(kZsplitThreads), 0, s, a);
+  hipLaunchKernelGGL(zsplit_kernel, dim3((unsigned)((a.n32 + 3) / 4)), dim3(kZsplitThreads), 0, s, a, parts);
   return hipGetLastError();
 }
 

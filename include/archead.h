@@ -392,7 +392,7 @@ ARCHEAD_API int archead_logits(const archead_tensor* H, const archead_packed_hea
  * and head->workspace_bytes are ignored.  Calls whose workspace (without the
  * optional split-tile partial sums, which get whatever is left) exceeds it
  * give E_WORKSPACE before anything is enqueued: at D = 4096, r_c = r_r = 64
- * that is past about 1790 tokens (960 at D = 8192).  Allocates nothing and calls no allocating
+ * that is past about 1790 tokens (930 at D = 8192).  Allocates nothing and calls no allocating
  * routine; the first call on a device looks the array's address up.  Every
  * call on one GPU uses the same array and nothing in it needs to start at
  * zero: calls that overlap on one GPU (other streams, other threads) race and

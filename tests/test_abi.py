@@ -103,14 +103,27 @@ def test_layout_dims_errors(ah):
     assert ah.lib.archead_pack_layout(ctypes.byref(ah.ArcheadDims(16, 256, 0, 0, 64)), None) == 1
 
 
+def _zmm_parts(N, D, r, g):
+    """Parts of the k range of the tile path's fp32 Z: workgroups (32-token by
+    32-rank tiles) times parts reach about 128, each of the 16 waves of a part
+    keeps at least one unit of whole groups."""
+    n32 = (N + 31) // 32 * 32
+    base = (n32 // 32) * ((r + 31) // 32)
+    units = D // 128 // (g // 128 if g > 128 else 1)
+    p = min(-(-128 // base) if base else 1, units // 16)
+    return max(p, 1)
+
+
 def _tile_workspace(V, D, r_c, r_r, g, N):
     """hf (N32*D*2) | hscale (N32*4) | zf (N32*2*(rc32+rr32)*2) | zscale (N32*4) |
-    z32 (N32*r*4) | split-tile partial sums (64 MiB); each 256-aligned."""
+    z32 (parts*N32*r*4) | split-tile partial sums (64 MiB); each 256-aligned."""
     up = lambda x: (x + 255) // 256 * 256
     n32 = (N + 31) // 32 * 32
     rc32, rr32 = (r_c + 31) // 32 * 32, (r_r + 31) // 32 * 32
+    r = r_c + r_r
+    parts = _zmm_parts(N, D, r, g) if r else 1
     return (up(n32 * D * 2) + up(n32 * 4) + up(n32 * 2 * (rc32 + rr32) * 2) + up(n32 * 4) +
-            up(n32 * (r_c + r_r) * 4) + (64 << 20))
+            up(parts * n32 * r * 4) + (64 << 20))
 
 
 def _few_tokens(V, D, r_c, r_r, g, N):
