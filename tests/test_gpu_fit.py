@@ -44,6 +44,8 @@ CASES = [
     (2048, 512, 32, 32, 128, 1024, 0.5, 0.05, 8, 2),
     (777, 384, 8, 0, 128, 300, 0.75, 0.01, 4, 1),
     (600, 256, 0, 16, 32, 400, 1.0, 0.1, 8, 3),
+    # larger than the V row chunks of the thin products (64) and the Gram chunks (256) by far
+    (8192, 1024, 32, 32, 128, 2048, 0.75, 0.01, 8, 2),
 ]
 
 
@@ -155,3 +157,19 @@ def test_fit_fp32_strided_w():
                                power_iters=1)
     torch.cuda.synchronize()
     assert torch.equal(head_a.buffer, head_b.buffer)
+
+
+def test_fit_zero_head_drops_every_direction():
+    """W = 0: every Cholesky pivot of the randomized SVDs' panels vanishes, so
+    every direction is dropped and the factors come out zero (the same
+    function as any orthonormal basis of a zero sketch would give); the packed
+    head is all zero codes and E = 0, with no error."""
+    V, D, r_c, r_r, g = 300, 256, 8, 8, 64
+    fi = synth.draw_fit(np.random.default_rng(3), V, D, r_c, r_r, 200, oversample=4)
+    fi.W[:] = 0
+    buf, f = _run(fi, r_c, r_r, g, 0.75, 0.01, 4, 2)
+    for k in ("A_c", "B_c", "A_w", "B_w", "E"):
+        assert not f[k].any(), k
+    zeros = (np.zeros((V, r_c), np.float32), np.zeros((r_c, D), np.float32))
+    head_ref, _ = oracle.quantize(fi.W, *zeros, np.zeros((V, r_r), np.float32), np.zeros((r_r, D), np.float32), g)
+    assert np.array_equal(buf, oracle.pack(head_ref))
