@@ -150,6 +150,33 @@ def test_one_hot_wide_workgroup_bit_exact(g):
     assert np.array_equal(Y, want)
 
 
+# The few-token pre-projection splits each element of Z over slices of D
+# (D/512 slices for up to 2 tokens, D/1024 up to 8, D/2048 beyond, at least
+# one), which need not divide the row's 8-column chunks evenly.
+@pytest.mark.parametrize("D", [1536, 2560])
+@pytest.mark.parametrize("N", [1, 2, 3, 9])
+def test_few_token_uneven_z_slices(D, N):
+    V, r_c, r_r, g = 900, 16, 24, 128
+    log(f"few-token Z slices V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N}")
+    assert ah_mod().archead_main_kernel(V, D, r_c, r_r, g, N) == "small_decode_kernel"
+    inp = synth.make("tiny", seed=D + N, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=4)
+    head = _head(inp)
+    check_parity(to_f64(run(head, inp.H_bits, 0)), oracle.logits(inp.H_bits, inp.head), f"D={D} N={N}")
+
+
+# The tile path's fp32 Z over parts of the hidden dimension: up to D/2048
+# parts (D/4096 for g = 256) when the 32-token x 32-rank tiles alone give
+# fewer than about 128 workgroups.
+@pytest.mark.parametrize("shape,N", [((700, 8192, 32, 32, 128), 70), ((700, 8192, 32, 32, 256), 100),
+                                     ((700, 4096, 32, 32, 64), 130), ((500, 8192, 64, 64, 128), 300)])
+def test_tile_z_parts(shape, N):
+    V, D, r_c, r_r, g = shape
+    log(f"tile Z parts V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N}")
+    inp = synth.make("tiny", seed=V + D + N, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=4)
+    head = _head(inp)
+    check_parity(to_f64(run(head, inp.H_bits, TILE)), oracle.logits(inp.H_bits, inp.head), "tile")
+
+
 # 64 groups per row (D/g = 64) and D = 8192 on the batched kernel
 @pytest.mark.parametrize("N", [17, 40, 64])
 def test_batched_deep_rows(N):
