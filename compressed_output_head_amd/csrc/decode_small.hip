@@ -152,10 +152,13 @@ __global__ __launch_bounds__(kSmallPrepThreads) void small_prep_kernel(const Fwd
 // Streaming kernel, persistent.
 //
 // The grid holds only co-resident workgroups: 16 waves per CU, two workgroups
-// of NW = 8 waves or one of NW = 16 (at most 128 VGPRs a wave).  Measured on
-// the decode workload, two 8-wave workgroups per CU are as fast as four of 4
-// waves for one token and faster for 4 to 8; one of 16 is slower (about 15%
-// at one token) and serves only the copies of H that two would not fit.
+// of NW = 8 waves or one of NW = 16 (launch bounds of four waves per SIMD, so
+// at most 128 VGPRs a wave).  Measured on the decode workload, two 8-wave
+// workgroups per CU are as fast as four of 4 waves for one token and faster
+// for 4 to 8; three per CU (six waves per SIMD, 80 VGPRs and spills) are
+// about 15% slower; one of 16 waves serves the copies of H that two would not
+// fit, its waves a grid apart (with neighbouring blocks it was about 15%
+// slower).
 // Every wave walks a grid-strided list of 16-row blocks (b, b + W, b + 2W, ...
 // with W the number of waves), so at any moment the waves read neighbouring
 // 1 KB tiles of the same k-tile plane.  Each wave keeps a ring of
@@ -192,7 +195,7 @@ __host__ __device__ inline size_t lds_bytes(int64_t N, int64_t D, int r) {
 }
 
 template <int P, int G, int NW>
-__global__ __launch_bounds__(64 * NW, 16 / NW) void small_decode_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(64 * NW, 4) void small_decode_kernel(const FwdArgs a) {
   constexpr int kLdsWaves = NW;
   constexpr int kLdsThreads = 64 * NW;
   static_assert(P % 4 == 0, "the ring holds whole 4-tile code chunks");
