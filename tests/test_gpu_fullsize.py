@@ -47,3 +47,22 @@ def test_full_size_workload(name):
         Ys = to_f64(y16[torch.as_tensor(rows, device="cuda")])
         bound = 2e-3 * np.abs(Yr).max() + 2.0 ** -8 * np.abs(Yr)
         assert (np.abs(Ys - Yr) <= bound).all()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("N", [3, 9, 17, 63])
+def test_full_size_decode_head_token_counts(N):
+    """The decode head (V=151936, D=4096, r_c=r_r=32, g=128) at token counts
+    that run the other decode-path kernels and workgroup shapes: 3 (two 8-wave
+    few-token workgroups per CU), 9 (one 16-wave workgroup), 17 and 63 (the
+    batched kernel with two and four token tiles); every row against the
+    oracle."""
+    ah = ah_mod()
+    cfg = synth.config("decode")
+    log(f"full-size decode head, N={N}")
+    inp = synth.make("decode", N=N)
+    head = ah.PackedHead.from_components(inp.head)
+    want = "small_decode_kernel" if N <= 16 else "batch_kernel"
+    assert ah.archead_main_kernel(cfg["V"], cfg["D"], cfg["r_c"], cfg["r_r"], cfg["g"], N) == want
+    Yr = oracle.logits(inp.H_bits, inp.head)
+    check_parity(to_f64(run(head, inp.H_bits, 0)), Yr, f"decode head N={N}")
