@@ -189,6 +189,21 @@ def run_workload(name, steps, warmup, path=0, n_tokens=None, chunk=None):
         for Hp in parts:
             ah.archead_logits_path(Hp, heads[i % 2], Y[:Hp.shape[0]], path)
 
+    # main-kernel events of every timed call: the library's launch of the main
+    # kernel records the first at the kernel's start and the second at the end
+    # of the forward's last kernel (the dispatches' own timestamps: nothing
+    # else goes on the stream)
+    nev = steps * len(parts)
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    eve = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    for e in evb + eve:
+        e.record(stream)  # creates the underlying hipEvent
+
+    def step_ev(i):
+        for j, Hp in enumerate(parts):
+            k = i * len(parts) + j
+            ah.archead_logits_events(Hp, heads[i % 2], Y[:Hp.shape[0]], path, evb[k], eve[k])
+
     for i in range(warmup):
         step(i)
     # timed region: K whole forward steps, nothing else on the stream
@@ -200,26 +215,15 @@ def run_workload(name, steps, warmup, path=0, n_tokens=None, chunk=None):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    # dominant-kernel duration: the library records these events on the launch
-    # stream right before and after the main kernel.  Each instrumented call
-    # runs on an idle queue (synchronized before the next one): with calls
-    # queued back to back the start marker waits behind the previous call and
-    # the pre-projection, and the span then includes dispatch gaps that are
-    # not the kernel's
-    # (a chunked step's kernel time is the sum over its chunks)
-    evb = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts))]
-    eve = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts))]
-    for e in evb + eve:
-        e.record(stream)  # creates the underlying hipEvent
-    torch.cuda.synchronize()
-    kms = []
+    # dominant-kernel duration: the same K steps again, back to back, with the
+    # launches recording their events (a launch that records events costs a
+    # few microseconds of dispatch, so the timed loop above runs without them);
+    # a chunked step's kernel time is the sum over its chunks
     for i in range(steps):
-        t = 0.0
-        for j, Hp in enumerate(parts):
-            ah.archead_logits_events(Hp, heads[i % 2], Y[:Hp.shape[0]], path, evb[j], eve[j])
-            torch.cuda.synchronize()
-            t += evb[j].elapsed_time(eve[j])
-        kms.append(t)
+        step_ev(i)
+    torch.cuda.synchronize()
+    kms = [sum(evb[i * len(parts) + j].elapsed_time(eve[i * len(parts) + j]) for j in range(len(parts)))
+           for i in range(steps)]
     A = algorithmic(cfg, L, N)
     return dict(cfg=cfg, L=L, A=A, ms=ms, kernel=dominant_kernel(cfg, rows, path), kernel_ms=float(np.mean(kms)),
                 chunk_rows=rows if rows < N else None, calls_per_step=len(parts),
@@ -298,16 +302,16 @@ def run_alt(name, fmt, steps, warmup, archead_ms=None):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    eb.record(stream)  # creates the underlying hipEvents
-    ee.record(stream)
+    # main-kernel spans of back-to-back calls (recorded by the launches themselves)
+    ebs = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ees = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in ebs + ees:
+        e.record(stream)  # creates the underlying hipEvents
     torch.cuda.synchronize()
-    kms = []
     for i in range(steps):
-        ah.archead_logits_events(H, heads[i % 2], Y, 0, eb, ee)
-        torch.cuda.synchronize()
-        kms.append(eb.elapsed_time(ee))
-    kernel_ms = float(np.mean(kms))
+        ah.archead_logits_events(H, heads[i % 2], Y, 0, ebs[i], ees[i])
+    torch.cuda.synchronize()
+    kernel_ms = float(np.mean([ebs[i].elapsed_time(ees[i]) for i in range(steps)]))
     payload = L["payload_bytes"]
     out = {"workload": name, "format": ALT_NAMES[fmt], "N": N, "ms_per_call": round(ms, 5),
            "kernel_ms": round(kernel_ms, 5), "launches": (N + 31) // 32, "payload_bytes": payload,

@@ -72,6 +72,13 @@ void compute_layout(const archead_dims* d, archead_layout* L) {
   L->payload_bytes = payload;
 }
 
+// Events of the archead_logits_events call running on this thread (none
+// outside such a call).
+MainEvents& main_events() {
+  static thread_local MainEvents e;
+  return e;
+}
+
 WorkspaceLayout workspace_layout(const archead_dims* d, int64_t n_tokens, bool stats, uint64_t split_cap,
                                  bool allow_decode) {
   WorkspaceLayout w{};
@@ -424,6 +431,16 @@ int setup_args(const archead_tensor* H, const archead_packed_head* head, bool st
 
 // Y = H W_hat^T on the path `path`, with the split-tile partial sums capped
 // at split_cap bytes of the workspace.
+// Sets the pending kernel events for one call and clears them at its end
+// (whatever path the call takes), so no later launch records them.
+struct EventScope {
+  explicit EventScope(void* start, void* stop) {
+    main_events().start = static_cast<hipEvent_t>(start);
+    main_events().stop = static_cast<hipEvent_t>(stop);
+  }
+  ~EventScope() { main_events() = MainEvents{}; }
+};
+
 int logits_impl(const archead_tensor* H, const archead_packed_head* head, archead_tensor* Y, int path,
                 void* stream, void* ev_begin, void* ev_end, uint64_t split_cap) {
   if (!H || !head || !Y) return ARCHEAD_E_NULL;
@@ -454,17 +471,17 @@ int logits_impl(const archead_tensor* H, const archead_packed_head* head, archea
     if ((uint64_t)(chunk - 1) * (uint64_t)Y->row_stride * ysz + (uint64_t)head->dims.V * ysz >= (1ull << 32))
       return ARCHEAD_E_UNSUPPORTED;
     (void)hipGetLastError();  // start from a clean error state
+    // the first batched launch records ev_begin at its start, the last one ev_end at its end
+    EventScope evs(ev_begin, nullptr);
     for (int64_t c0 = 0; c0 < N; c0 += kAltChunk) {
       FwdArgs ac = a;
       ac.N = std::min<int64_t>(kAltChunk, N - c0);
       ac.H = a.H + c0 * a.H_stride;
       ac.Y = static_cast<uint8_t*>(Y->data) + (uint64_t)c0 * (uint64_t)Y->row_stride * ysz;
       if (launch_small_prep(ac, s) != hipSuccess) return ARCHEAD_E_HIP;
-      if (c0 == 0 && ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
-        return ARCHEAD_E_HIP;
+      if (c0 + kAltChunk >= N) main_events().stop = static_cast<hipEvent_t>(ev_end);
       if (launch_batch(ac, s) != hipSuccess) return ARCHEAD_E_HIP;
     }
-    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
     return ARCHEAD_OK;
   }
   // auto: the decode kernel when it takes the call, else the tile path; the
@@ -478,13 +495,14 @@ int logits_impl(const archead_tensor* H, const archead_packed_head* head, archea
   (void)hipGetLastError();  // start from a clean error state
   const hipError_t ep = !decode ? launch_prep(a, s) : (W.small || W.batch) ? launch_small_prep(a, s) : launch_decode_prep(a, s);
   if (ep != hipSuccess) return ARCHEAD_E_HIP;
-  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return ARCHEAD_E_HIP;
+  // the main kernel's launch records ev_begin at its start and ev_end at the
+  // end of the forward's last kernel
+  EventScope evs(ev_begin, ev_end);
   const hipError_t e = !decode ? launch_tile(a, s)
                        : W.small ? launch_small_decode(a, s)
                        : W.batch ? launch_batch(a, s)
                                  : launch_decode(a, s);
   if (e != hipSuccess) return ARCHEAD_E_HIP;
-  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return ARCHEAD_E_HIP;
   return ARCHEAD_OK;
 }
 

@@ -553,16 +553,15 @@ constexpr int batch_k(int fmt, int hk) { return fmt == ARCHEAD_FMT_ROW_INT8 ? hk
 
 template <int FMT, int T, int MM, int CPT>
 hipError_t launch_tmc(const FwdArgs& a, const BLds& L, unsigned grid, hipStream_t s) {
+  // the batched kernel ends every launch of a forward that gives it events
+  constexpr bool last = true;
   if constexpr (T <= 3) {
-    if (batch_hk(T, a.nkt) == 4) {
-      hipLaunchKernelGGL((batch_kernel<FMT, T, MM, CPT, 4, batch_k(FMT, 4), 1>), dim3(grid), dim3(kBThreads),
-                         L.total, s, a, L);
-      return hipGetLastError();
-    }
+    if (batch_hk(T, a.nkt) == 4)
+      return launch_main(batch_kernel<FMT, T, MM, CPT, 4, batch_k(FMT, 4), 1>, dim3(grid), dim3(kBThreads), L.total,
+                         s, last, a, L);
   }
-  hipLaunchKernelGGL((batch_kernel<FMT, T, MM, CPT, 2, batch_k(FMT, 2), 1>), dim3(grid), dim3(kBThreads), L.total,
-                     s, a, L);
-  return hipGetLastError();
+  return launch_main(batch_kernel<FMT, T, MM, CPT, 2, batch_k(FMT, 2), 1>, dim3(grid), dim3(kBThreads), L.total, s,
+                     last, a, L);
 }
 
 template <int FMT, int T, int CPT>

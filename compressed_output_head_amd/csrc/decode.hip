@@ -586,8 +586,7 @@ hipError_t launch_mw(const FwdArgs& a, unsigned grid, int zst, hipStream_t s) {
   bool ok = false;
   const DecLds L = dec_layout(a.N, a.D, a.r_c, a.r_r, MM, WD, ok);
   if (!ok) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_kernel<MM, WD>), dim3(grid), dim3(kDecThreads), L.total, s, a, L, zst);
-  return hipGetLastError();
+  return launch_main(decode_kernel<MM, WD>, dim3(grid), dim3(kDecThreads), L.total, s, true, a, L, zst);
 }
 
 template <int WD>

@@ -454,8 +454,7 @@ hipError_t launch_lds_p(const FwdArgs& a, hipStream_t s) {
   per_cu = std::min(per_cu, 16 / NW);
   const int64_t need = (a.nb + NW - 1) / NW;
   const int64_t grid = std::min<int64_t>(need, (int64_t)device_cu_count() * per_cu);
-  hipLaunchKernelGGL((small_decode_kernel<P, G, NW>), dim3((unsigned)grid), dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  return launch_main(small_decode_kernel<P, G, NW>, dim3((unsigned)grid), dim3(kThreads), (uint32_t)lds, s, true, a);
 }
 
 template <int G>

@@ -1,6 +1,7 @@
 // Internal declarations shared by the host library and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,6 +21,33 @@ constexpr uint32_t kMaxLdsBytes = 160 * 1024;
 constexpr uint64_t kSplitBytes = 64ull << 20;
 
 inline uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// Events a caller of archead_logits_events asked for: the start of the main
+// kernel and the end of the last kernel of the forward (the main kernel, or
+// the tile path's reduce kernel of split tiles).  Set for the duration of one
+// call on the calling thread and consumed by launch_main.
+struct MainEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+MainEvents& main_events();
+
+// Launch a kernel of the forward; with events pending on this thread, the
+// launch itself records them (AMD's launch with start and stop events: the
+// dispatch's own timestamps, no separate markers on the stream).  last: no
+// kernel of the forward follows this one.
+template <typename F, typename... Args>
+hipError_t launch_main(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, bool last, Args... args) {
+  MainEvents& e = main_events();
+  hipEvent_t start = e.start, stop = last ? e.stop : nullptr;
+  if (start || stop) {
+    e.start = nullptr;
+    if (last) e.stop = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, start, stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
+  return hipGetLastError();
+}
 
 // Checks shared by every entry point.  Returns ARCHEAD_OK or an error.
 int check_dims(const archead_dims* d);

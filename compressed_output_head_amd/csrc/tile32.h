@@ -864,10 +864,10 @@ static hipError_t launch_t32_g(const FwdArgs& a, hipStream_t s) {
   const T32Split sp = t32_split<TT>(a, tiles, t32_slots((const void*)&tile32_kernel<GC, TT, ST>, codes));
   const int nsplit = tiles - sp.full;
   const dim3 grid((unsigned)(sp.full + nsplit * sp.s)), block(kT32Threads);
-  hipLaunchKernelGGL((tile32_kernel<GC, TT, ST>), grid, block, codes, s, a, sp);
-  if (nsplit > 0 && sp.s > 1)
-    hipLaunchKernelGGL((t32_reduce_kernel<TT, ST>), dim3(nsplit * 8 * TT), dim3(256), 0, s, a, sp);
-  return hipGetLastError();
+  const bool reduce = nsplit > 0 && sp.s > 1;
+  const hipError_t e = launch_main(tile32_kernel<GC, TT, ST>, grid, block, (uint32_t)codes, s, !reduce, a, sp);
+  if (e != hipSuccess || !reduce) return e;
+  return launch_main(t32_reduce_kernel<TT, ST>, dim3(nsplit * 8 * TT), dim3(256), 0u, s, true, a, sp);
 }
 
 template <int TT, bool ST>

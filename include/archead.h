@@ -411,11 +411,15 @@ ARCHEAD_API int archead_logits_noalloc(const archead_tensor* H, const archead_pa
 ARCHEAD_API int archead_logits_path(const archead_tensor* H, const archead_packed_head* head,
                         archead_tensor* Y, int path, void* stream);
 
-/* Same as archead_logits_path, and records the caller's events ev_begin and
- * ev_end (hipEvent_t handles, either may be NULL) on `stream` immediately
- * before and after the main kernel (decode or tile), after either path's
- * pre-projection kernels.  For timing the dominant kernel on the stream it
- * runs on. */
+/* Same as archead_logits_path, and has the caller's events ev_begin and
+ * ev_end (hipEvent_t handles, either may be NULL) record the start of the
+ * main kernel (decode or tile, after either path's pre-projection kernels)
+ * and the end of the forward's last kernel (the main kernel, or the tile
+ * path's reduce kernel of split tiles; for a comparison head, from the first
+ * to the last of its launches).  The launches themselves record them (AMD's
+ * launch with start and stop events), so no marker is added to `stream` and
+ * the span is the kernels' own.  For timing the dominant kernel on the stream
+ * it runs on. */
 ARCHEAD_API int archead_logits_events(const archead_tensor* H, const archead_packed_head* head,
                                       archead_tensor* Y, int path, void* stream, void* ev_begin,
                                       void* ev_end);
