@@ -353,3 +353,44 @@ def test_split_tiles_with_unaligned_outputs(N):
             y32 = Y.clone()
         else:
             assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), Y.contiguous().view(torch.int16))
+
+
+# archead_logits_events: the launches record the caller's events (main
+# kernel start, last kernel end); the logits are those of archead_logits_path,
+# and a later call without events leaves the events as they were.
+EVENT_CASES = [
+    # label, V, D, r_c, r_r, g, N, path, comparison format (0: ARCHead)
+    ("few-token", 1000, 512, 16, 8, 64, 4, 0, 0),
+    ("few-token 16 waves", 900, 4096, 16, 16, 128, 12, 0, 0),
+    ("k-tile-major", 777, 384, 0, 24, 128, 5, 0, 0),
+    ("batched", 1000, 512, 16, 8, 64, 40, 0, 0),
+    ("tile", 2048, 1024, 32, 32, 128, 300, 2, 0),
+    ("tile, split tail", 2048, 1024, 32, 32, 128, 1100, 2, 0),
+    ("group INT4, three launches", 777, 512, 0, 0, 64, 70, 0, 1),
+]
+
+
+@pytest.mark.parametrize("label,V,D,r_c,r_r,g,N,path,fmt", EVENT_CASES)
+def test_logits_events_from_the_launches(label, V, D, r_c, r_r, g, N, path, fmt):
+    torch = torch_mod()
+    ah = ah_mod()
+    log(f"events {label}: V={V} D={D} r_c={r_c} r_r={r_r} g={g} N={N} path={path} fmt={fmt}")
+    if fmt:
+        H_bits, h = synth.make_alt(fmt, V + N, V, D, N, g)
+    else:
+        h = synth.make("tiny", seed=V + N, V=V, D=D, N=N, r_c=r_c, r_r=r_r, g=g, n_outlier=4)
+        H_bits, h = h.H_bits, h.head
+    head = ah.PackedHead.from_components(h)
+    H = device_H(H_bits)
+    y_plain = run(head, H_bits, path, H_dev=H)
+    eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb.record()
+    ee.record()
+    Y = torch.full((N, V), float("nan"), device="cuda")
+    ah.archead_logits_events(H, head, Y, path, eb, ee)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int32), y_plain.view(torch.int32))
+    span = eb.elapsed_time(ee)
+    assert span > 0.0
+    run(head, H_bits, path, H_dev=H)  # no events: the pair keeps its times
+    assert eb.elapsed_time(ee) == span
