@@ -307,7 +307,11 @@ __global__ __launch_bounds__(64 * NW, 4) void small_decode_kernel(const FwdArgs 
 
   int64_t bn = b + nwaves;
   while (b < nb) {
-    const int64_t bnx = bn < nb ? bn : b;  // the ring's next block (or a harmless re-read)
+    // the ring's next block; after the wave's last block the ring's loads go to
+    // the head's last block, the same few lines for every wave (cache hits after
+    // the first, never used; re-reading this block's first tiles, streamed long
+    // before, would fetch them from memory again)
+    const int64_t bnx = bn < nb ? bn : nb - 1;
     const int64_t v = 16 * b + i16;
     // epilogue operands of this block, loaded now so they arrive long before
     // use: buffer loads with no branches (past a section's end they read zero),
