@@ -248,8 +248,11 @@ __global__ __launch_bounds__(64 * NW, 4) void small_decode_kernel(const FwdArgs 
   const int per_row = D / 8;
 
   // prologue, one round trip: this thread's first pieces of H, Z and the
-  // token scales, then the weight ring, then those pieces into LDS
-  constexpr int kPre = 2;
+  // token scales, then the weight ring, then those pieces into LDS.  Eight
+  // 16-byte pieces a thread hold all of H at D = 4096 (up to 8 tokens in an
+  // 8-wave workgroup, 16 in a 16-wave one); the loop after them serves
+  // larger D, one round trip per pass.
+  constexpr int kPre = 8;
   u4 hpre[kPre];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) {
