@@ -234,8 +234,14 @@ __global__ __launch_bounds__(kBThreads, OCC) void batch_kernel(const FwdArgs a, 
   for (int m = 0; m < MM; ++m)
     wblk[m] = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bw0 + (m < Mw ? m : 0)) * TB);
   u4 wr[K][MM][WV];
+  // Stages past the end of the walk (never used) all read the last k-tile of
+  // the head's last block: the same lines for every wave, cache hits after the
+  // first.  The wave's own last k-tile, streamed a stage earlier without
+  // staying in the cache, would come from memory again.
+  const uint32_t wpast = (uint32_t)(nkt - 1) * tstride + (uint32_t)(a.nb - 1) * TB;
   auto issue_w = [&](auto J_, int ks) {
     constexpr int J = decltype(J_)::value;
+    const bool past = ks >= nkt;  // wave-uniform
     const uint32_t kc = (uint32_t)__builtin_amdgcn_readfirstlane(ktile(ks));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -243,7 +249,8 @@ __global__ __launch_bounds__(kBThreads, OCC) void batch_kernel(const FwdArgs a, 
 #pragma unroll
       for (int v = 0; v < WV; ++v)
         wr[J][m][v] = __builtin_bit_cast(
-            u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, kc * tstride + wblk[m] + 16u * v, kNonTemporal));
+            u4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, (past ? wpast : kc * tstride + wblk[m]) + 16u * v,
+                                                      kNonTemporal));
     __builtin_amdgcn_sched_barrier(0);
   };
 
